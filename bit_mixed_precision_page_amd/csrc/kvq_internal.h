@@ -1,0 +1,88 @@
+// kvq_internal.h -- layout constants, device helpers and kernel launchers of
+// the 2-bit mixed-precision KV cache library (gfx950).  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace kvq {
+
+constexpr int D = 128;   // head dimension
+constexpr int P = 128;   // tokens per page
+constexpr int GK = 32;   // tokens per Key group (one channel)
+constexpr int GV = 32;   // channels per Value group (one token)
+constexpr int R = 128;   // window tokens
+constexpr int F16 = 0, BF16 = 1;
+
+// Page segments (Kitty abstract: page-centric layout, Key page as two
+// uniform 2-bit planes).  Every segment is 16-byte aligned because k is a
+// multiple of 16.
+struct PageLayout {
+    uint32_t klo, khi, ks, kz, kidx, vc, vs, vz, bytes;
+};
+
+__host__ __device__ constexpr PageLayout page_layout(int k) {
+    PageLayout L{};
+    uint32_t o = 0;
+    L.klo = o;  o += P * D / 4;
+    L.khi = o;  o += P * k / 4;
+    L.ks = o;   o += (P / GK) * D * 2;
+    L.kz = o;   o += (P / GK) * D * 2;
+    L.kidx = o; o += (uint32_t)((k + 15) / 16 * 16);
+    L.vc = o;   o += P * D / 4;
+    L.vs = o;   o += (D / GV) * P * 2;
+    L.vz = o;   o += (D / GV) * P * 2;
+    L.bytes = o;
+    return L;
+}
+
+// Geometry of one cache, shared by the launchers.
+struct Geometry {
+    int B, Hq, Hkv, g, k, max_pages, dtype;
+    uint32_t page_bytes;
+    size_t res_base;  // byte offset of the window region
+    float scale;      // softmax scale
+};
+
+__host__ __device__ inline size_t page_off(const Geometry &G, int unit, int page) {
+    return ((size_t)unit * G.max_pages + page) * G.page_bytes;
+}
+__host__ __device__ inline size_t res_k_off(const Geometry &G, int unit) {
+    return G.res_base + (size_t)unit * 2 * R * D * 2;
+}
+__host__ __device__ inline size_t res_v_off(const Geometry &G, int unit) {
+    return res_k_off(G, unit) + (size_t)R * D * 2;
+}
+
+// Launchers (defined in the .hip files).  All asynchronous on `stream`.
+// Quantize `n_new` pages per unit: the source of page p of unit u starts at
+// element src + u * src_unit_stride + p * P * D of k_src / v_src ([P][D] rows
+// of D contiguous elements); destinations are pages first_page + p.
+hipError_t launch_quantize_pages(const Geometry &G, uint8_t *cache, const uint16_t *k_src,
+                                 const uint16_t *v_src, size_t src_unit_stride,
+                                 int first_page, int n_new, hipStream_t stream);
+// Same, with each unit's window as the source (one page per unit).
+hipError_t launch_flush_window(const Geometry &G, uint8_t *cache, int page, hipStream_t stream);
+// Copy one token per unit into window slot `slot`.
+hipError_t launch_append(const Geometry &G, uint8_t *cache, const uint16_t *k,
+                         const uint16_t *v, int slot, hipStream_t stream);
+// Quantize arbitrary groups (inspection entry point).
+hipError_t launch_quantize_groups(int dtype, int L, const uint16_t *x, int n_groups,
+                                  int group_len, uint16_t *s, uint16_t *z, uint8_t *codes,
+                                  hipStream_t stream);
+
+struct DecodePlan {
+    int n_pages, n_res;
+    int page_splits;      // splits over pages (0 when n_pages == 0)
+    int pages_per_split;
+    int total_splits;     // page_splits + (n_res > 0)
+    int max_splits;       // workspace stride (splits per (b, hq))
+};
+size_t decode_workspace_bytes(const Geometry &G, int max_splits);
+hipError_t launch_decode(const Geometry &G, const uint8_t *cache, const uint16_t *q,
+                         float *out, void *workspace, const DecodePlan &plan,
+                         hipEvent_t ev_before, hipEvent_t ev_after, hipStream_t stream);
+
+}  // namespace kvq

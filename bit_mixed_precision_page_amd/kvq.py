@@ -1,0 +1,246 @@
+"""ctypes binding of libkvq.so (include/kvq.h), same entry-point names.
+
+Argument marshalling only: tensors become device pointers, the torch stream
+becomes a hipStream_t, negative return codes become `KvqError`.  Every step of
+the path runs in the library's HIP kernels.  Importing this module raises if
+the library has not been built.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+_L = ctypes.CDLL(LIB_PATH)
+
+KVQ_F16, KVQ_BF16 = 0, 1
+ERRORS = {-1: "KVQ_EINVAL", -2: "KVQ_ECAPACITY", -3: "KVQ_ESTATE", -4: "KVQ_EEMPTY",
+          -5: "KVQ_EWORKSPACE", -6: "KVQ_EALIGN", -7: "KVQ_EHIP"}
+EXPORTS = ["kvq_cache_bytes", "kvq_page_bytes", "kvq_cache_create", "kvq_cache_destroy",
+           "kvq_quantize_page", "kvq_append_token", "kvq_decode_workspace_bytes",
+           "kvq_decode_attention", "kvq_set_decode_splits", "kvq_get_decode_splits",
+           "kvq_get_state", "kvq_set_state", "kvq_page_offset", "kvq_residual_offset",
+           "kvq_quantize_groups", "kvq_set_kernel_events", "kvq_strerror"]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        self.name = ERRORS.get(code, str(code))
+        msg = _L.kvq_strerror(code).decode()
+        super().__init__(f"{where}: {self.name} ({msg})")
+
+
+class KvqConfig(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_tokens", ctypes.c_int32), ("key_group_tokens", ctypes.c_int32),
+                ("value_group_channels", ctypes.c_int32), ("residual_tokens", ctypes.c_int32),
+                ("boost_channels", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+def config(batch, num_q_heads, num_kv_heads, boost_channels, max_pages, dtype,
+           softmax_scale=0.0, head_dim=128, page_tokens=128, key_group_tokens=32,
+           value_group_channels=32, residual_tokens=128):
+    return KvqConfig(batch, num_q_heads, num_kv_heads, head_dim, page_tokens,
+                     key_group_tokens, value_group_channels, residual_tokens,
+                     boost_channels, max_pages, dtype, softmax_scale)
+
+
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_i32 = ctypes.c_int32
+_cfgp = ctypes.POINTER(KvqConfig)
+_SIG = {
+    "kvq_cache_bytes": [_cfgp, ctypes.POINTER(_sz)],
+    "kvq_page_bytes": [_cfgp, ctypes.POINTER(_sz)],
+    "kvq_cache_create": [_cfgp, _vp, _sz, ctypes.POINTER(_vp)],
+    "kvq_cache_destroy": [_vp],
+    "kvq_quantize_page": [_vp, _vp, _vp, _i32, _vp],
+    "kvq_append_token": [_vp, _vp, _vp, _vp, ctypes.POINTER(_i32)],
+    "kvq_decode_workspace_bytes": [_vp, ctypes.POINTER(_sz)],
+    "kvq_decode_attention": [_vp, _vp, _vp, _vp, _sz, _vp],
+    "kvq_set_decode_splits": [_vp, _i32],
+    "kvq_get_decode_splits": [_vp, ctypes.POINTER(_i32)],
+    "kvq_get_state": [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
+    "kvq_set_state": [_vp, _i32, _i32],
+    "kvq_page_offset": [_vp, _i32, _i32, _i32, ctypes.POINTER(_sz)],
+    "kvq_residual_offset": [_vp, _i32, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)],
+    "kvq_quantize_groups": [_i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp],
+    "kvq_set_kernel_events": [_vp, _vp, _vp],
+}
+for _name, _args in _SIG.items():
+    _f = getattr(_L, _name)
+    _f.argtypes = _args
+    _f.restype = ctypes.c_int
+_L.kvq_strerror.argtypes = [ctypes.c_int]
+_L.kvq_strerror.restype = ctypes.c_char_p
+
+
+def _check(rc, where):
+    if rc != 0:
+        raise KvqError(rc, where)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+# -- entry points (same names as the C ABI) ----------------------------------
+def kvq_cache_bytes(cfg):
+    n = _sz()
+    _check(_L.kvq_cache_bytes(ctypes.byref(cfg), ctypes.byref(n)), "kvq_cache_bytes")
+    return n.value
+
+
+def kvq_page_bytes(cfg):
+    n = _sz()
+    _check(_L.kvq_page_bytes(ctypes.byref(cfg), ctypes.byref(n)), "kvq_page_bytes")
+    return n.value
+
+
+def kvq_cache_create(cfg, dev_mem, nbytes):
+    h = _vp()
+    _check(_L.kvq_cache_create(ctypes.byref(cfg), _ptr(dev_mem), nbytes, ctypes.byref(h)),
+           "kvq_cache_create")
+    return h.value
+
+
+def kvq_cache_destroy(handle):
+    _check(_L.kvq_cache_destroy(handle), "kvq_cache_destroy")
+
+
+def kvq_quantize_page(handle, k, v, n_pages, stream=None):
+    _check(_L.kvq_quantize_page(handle, _ptr(k), _ptr(v), n_pages, _stream(stream)),
+           "kvq_quantize_page")
+
+
+def kvq_append_token(handle, k, v, stream=None):
+    f = _i32()
+    _check(_L.kvq_append_token(handle, _ptr(k), _ptr(v), _stream(stream), ctypes.byref(f)),
+           "kvq_append_token")
+    return bool(f.value)
+
+
+def kvq_decode_workspace_bytes(handle):
+    n = _sz()
+    _check(_L.kvq_decode_workspace_bytes(handle, ctypes.byref(n)), "kvq_decode_workspace_bytes")
+    return n.value
+
+
+def kvq_decode_attention(handle, q, out, workspace, ws_bytes, stream=None):
+    _check(_L.kvq_decode_attention(handle, _ptr(q), _ptr(out), _ptr(workspace), ws_bytes,
+                                   _stream(stream)), "kvq_decode_attention")
+
+
+def kvq_set_decode_splits(handle, splits):
+    _check(_L.kvq_set_decode_splits(handle, splits), "kvq_set_decode_splits")
+
+
+def kvq_get_decode_splits(handle):
+    s = _i32()
+    _check(_L.kvq_get_decode_splits(handle, ctypes.byref(s)), "kvq_get_decode_splits")
+    return s.value
+
+
+def kvq_get_state(handle):
+    a, b = _i32(), _i32()
+    _check(_L.kvq_get_state(handle, ctypes.byref(a), ctypes.byref(b)), "kvq_get_state")
+    return a.value, b.value
+
+
+def kvq_set_state(handle, n_pages, n_res):
+    _check(_L.kvq_set_state(handle, n_pages, n_res), "kvq_set_state")
+
+
+def kvq_page_offset(handle, b, h, page):
+    o = _sz()
+    _check(_L.kvq_page_offset(handle, b, h, page, ctypes.byref(o)), "kvq_page_offset")
+    return o.value
+
+
+def kvq_residual_offset(handle, b, h):
+    ko, vo = _sz(), _sz()
+    _check(_L.kvq_residual_offset(handle, b, h, ctypes.byref(ko), ctypes.byref(vo)),
+           "kvq_residual_offset")
+    return ko.value, vo.value
+
+
+def kvq_quantize_groups(dtype, L, x, n_groups, group_len, s, z, codes, stream=None):
+    _check(_L.kvq_quantize_groups(dtype, L, _ptr(x), n_groups, group_len, _ptr(s), _ptr(z),
+                                  _ptr(codes), _stream(stream)), "kvq_quantize_groups")
+
+
+def kvq_set_kernel_events(handle, before, after):
+    _check(_L.kvq_set_kernel_events(handle, _ptr(before), _ptr(after)), "kvq_set_kernel_events")
+
+
+def kvq_strerror(code):
+    return _L.kvq_strerror(code).decode()
+
+
+# -- convenience owner of the device buffers -----------------------------------
+class Cache:
+    """Owns a cache's device memory and workspace (torch tensors) and its handle."""
+
+    def __init__(self, cfg, device="cuda"):
+        self.cfg = cfg
+        self.nbytes = kvq_cache_bytes(cfg)
+        self.mem = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        self.handle = kvq_cache_create(cfg, self.mem, self.nbytes)
+        self.ws_bytes = kvq_decode_workspace_bytes(self.handle)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.page_bytes = kvq_page_bytes(cfg)
+
+    def quantize_page(self, k, v, n_pages, stream=None):
+        kvq_quantize_page(self.handle, k, v, n_pages, stream)
+
+    def append_token(self, k, v, stream=None):
+        return kvq_append_token(self.handle, k, v, stream)
+
+    def decode_attention(self, q, out, stream=None):
+        kvq_decode_attention(self.handle, q, out, self.ws, self.ws_bytes, stream)
+
+    @property
+    def state(self):
+        return kvq_get_state(self.handle)
+
+    def pages_view(self):
+        """[B][Hkv][max_pages][page_bytes] uint8 view of the page region."""
+        c = self.cfg
+        n = c.batch * c.num_kv_heads * c.max_pages * self.page_bytes
+        return self.mem[:n].view(c.batch, c.num_kv_heads, c.max_pages, self.page_bytes)
+
+    def window_view(self):
+        """K and V windows, each [B][Hkv][128][128] as int16 bit patterns."""
+        c = self.cfg
+        base = c.batch * c.num_kv_heads * c.max_pages * self.page_bytes
+        w = self.mem[base:].view(torch.int16).view(c.batch, c.num_kv_heads, 2, 128, 128)
+        return w[:, :, 0], w[:, :, 1]
+
+    def close(self):
+        if self.handle:
+            kvq_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,180 @@
+/*
+ * kvq.h -- 2-bit mixed-precision paged KV cache with fused
+ * dequantize-in-attention decode, for AMD Instinct MI355X (gfx950).
+ *
+ * Plain C ABI: no HIP or torch types.  Device pointers are passed as void* /
+ * float*, a HIP stream as void* (hipStream_t; NULL = the default stream).
+ *
+ * What the library computes (sources are web pages on KV-cache quantization):
+ *  - KIVI explainer (aibr.jp), section 3: Keys quantized per channel, Values
+ *    per token, asymmetric (min/max, zero-point) quantization, a residual kept
+ *    in full precision, streaming append into the quantized cache.
+ *  - Kitty abstract (fugumt, arXiv 2511.18643): per page, a small fraction of
+ *    Key channels ranked by sensitivity is kept at 4 bits; a mixed-precision
+ *    Key page is stored as two uniform 2-bit tensors; page-centric layout.
+ *  - notes.yuuk.io "KV cache quantization", open questions: magnitude-based
+ *    channel selection; boost ratios 12.5 % and 25 %; GQA key sharing.
+ *  - MiniKV summary (f-binder), problem setting and method: keep the
+ *    attention output close to the unquantized one; fuse the 2-bit unpack
+ *    into the decode matmul.
+ *
+ * Numerics (fixed readings of what the pages leave open):
+ *  - page = 128 tokens of one (sequence, KV head); Key groups = 32 tokens of
+ *    one channel; Value groups = 32 channels of one token; window = 128;
+ *  - quantizer: z = min, s = dtype_rne(fp32((max - min) / L)), code =
+ *    clamp(rint_even(fp32(fp32(x - z) * fp32(1 / s))), 0, L), all IEEE fp32;
+ *    s == 0 gives code 0; a zero minimum is stored as +0;
+ *  - the k Key channels with the largest max|K| over the page (ties: lower
+ *    channel) use L = 15, stored as lo = code & 3 (all channels) and hi =
+ *    code >> 2 (boosted channels, ascending), others L = 3;
+ *  - attention: o = softmax(scale q . k) v over every page token
+ *    (dequantized) and every window token (exact), no mask; query head hq
+ *    reads KV head hq / (Hq / Hkv); output fp32.
+ *
+ * Page layout (k boosted channels, dtype of 2 bytes; every segment 16-byte
+ * aligned, little-endian 2-bit fields):
+ *   K_lo    [128 tok][128 ch] 2-bit, element (t, c) at bit 2 (128 t + c)
+ *   K_hi    [128 tok][k] 2-bit, (t, j) at bit 2 (k t + j)
+ *   K_scale [4][128] dtype, K_zero [4][128] dtype      (group-major)
+ *   K_idx   k bytes (ascending), padded to 16
+ *   V_codes 4096 B: token t, channel c at bit 8 byte + 16 half + 2 (c / 16),
+ *           byte = 1024 (t / 32) + 16 (16 G + c % 16) + 4 w, with
+ *           u = t % 32, r = u % 16, G = r / 4, w = 2 (u / 16) + (r % 4) / 2,
+ *           half = r % 2
+ *   V_scale [4][128] dtype, V_zero [4][128] dtype      (group-major)
+ * = 12816 bytes at k = 16, 13344 at k = 32.
+ * Cache memory: page (b, h, p) at ((b Hkv + h) max_pages + p) page_bytes,
+ * then per (b, h) a window K_res[128][128] followed by V_res[128][128].
+ *
+ * Ownership: the caller owns every device buffer (cache memory, inputs,
+ * outputs, workspace); the library owns only the host handle, never
+ * allocates or frees device memory and never synchronizes.  Every launch is
+ * asynchronous on the given stream; inputs must stay valid until the stream
+ * passes the call.  A handle is not thread-safe.
+ *
+ * Errors: 0 on success, a negative KVQ_E* code otherwise.  Every argument
+ * check happens before any launch, so a failed call changes no state.
+ * Preconditions the library does not check: inputs are finite, and a group's
+ * range (max - min) is finite in fp32.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_OK 0
+#define KVQ_EINVAL (-1)     /* bad configuration or argument */
+#define KVQ_ECAPACITY (-2)  /* more pages than max_pages */
+#define KVQ_ESTATE (-3)     /* call not allowed in the current cache state */
+#define KVQ_EEMPTY (-4)     /* attention over an empty cache */
+#define KVQ_EWORKSPACE (-5) /* workspace too small */
+#define KVQ_EALIGN (-6)     /* a device pointer is not 16-byte aligned */
+#define KVQ_EHIP (-7)       /* a kernel launch failed */
+
+typedef enum { KVQ_F16 = 0, KVQ_BF16 = 1 } kvq_dtype;
+
+typedef struct {
+    int32_t batch;                /* B >= 1 */
+    int32_t num_q_heads;          /* Hq, a multiple of Hkv, Hq / Hkv <= 16 */
+    int32_t num_kv_heads;         /* Hkv >= 1 */
+    int32_t head_dim;             /* must be 128 */
+    int32_t page_tokens;          /* must be 128 */
+    int32_t key_group_tokens;     /* must be 32 */
+    int32_t value_group_channels; /* must be 32 */
+    int32_t residual_tokens;      /* must be 128 (= page_tokens) */
+    int32_t boost_channels;       /* k: multiple of 16 in [0, 128] (16 = 12.5 %, 32 = 25 %) */
+    int32_t max_pages;            /* page capacity per (sequence, KV head), >= 1 */
+    int32_t dtype;                /* kvq_dtype of Q, K, V, window and metadata */
+    float softmax_scale;          /* <= 0 selects 1 / sqrt(head_dim) */
+} kvq_config;
+
+typedef struct kvq_cache kvq_cache; /* opaque host handle */
+
+/* Device bytes the caller must allocate for a cache with this config
+   (pages + window).  Errors: KVQ_EINVAL. */
+int kvq_cache_bytes(const kvq_config *cfg, size_t *bytes);
+
+/* Bytes of one packed page for this config (12816 at k = 16). */
+int kvq_page_bytes(const kvq_config *cfg, size_t *bytes);
+
+/* Wrap caller-owned device memory (>= kvq_cache_bytes, 16-byte aligned) in a
+   new handle with n_pages = n_res = 0.  The memory's prior contents are not
+   read.  Errors: KVQ_EINVAL, KVQ_EALIGN. */
+int kvq_cache_create(const kvq_config *cfg, void *dev_mem, size_t bytes, kvq_cache **out);
+
+/* Free the host handle (not the device memory). */
+int kvq_cache_destroy(kvq_cache *cache);
+
+/* Bulk prefill (Kitty abstract: per-page ranking and boost; KIVI section 3:
+   per-channel Keys, per-token Values).  k, v: device [B][Hkv][n_pages*128][128]
+   in the cache dtype, contiguous, 16-byte aligned.  Quantizes n_pages new
+   pages per (sequence, KV head) after the existing ones.  Requires an empty
+   window (n_res == 0; else KVQ_ESTATE) and n_pages + new <= max_pages (else
+   KVQ_ECAPACITY).  n_pages == 0 is a no-op. */
+int kvq_quantize_page(kvq_cache *cache, const void *k, const void *v, int32_t n_pages,
+                      void *stream);
+
+/* Streaming append of one token per (sequence, KV head) (KIVI section 3).
+   k, v: device [B][Hkv][128] in the cache dtype.  If the window already holds
+   128 tokens it is first quantized into page n_pages (flush-before-insert;
+   KVQ_ECAPACITY if no page is free); then the token is written to window slot
+   n_res.  *flushed (may be NULL) is set to 1 when a flush happened, else 0. */
+int kvq_append_token(kvq_cache *cache, const void *k, const void *v, void *stream,
+                     int32_t *flushed);
+
+/* Workspace bytes kvq_decode_attention needs for any state of this cache. */
+int kvq_decode_workspace_bytes(const kvq_cache *cache, size_t *bytes);
+
+/* Decode attention of one query token per sequence (MiniKV summary: fused
+   2-bit unpack + matmul).  q: device [B][Hq][128] in the cache dtype; out:
+   device [B][Hq][128] float32; workspace: device, >= the bytes above (else
+   KVQ_EWORKSPACE).  Attends to every page token and window token; KVQ_EEMPTY
+   when the cache holds no token.  Split-K over pages, then a merge. */
+int kvq_decode_attention(kvq_cache *cache, const void *q, float *out, void *workspace,
+                         size_t ws_bytes, void *stream);
+
+/* Number of page splits per (sequence, KV head) decode attention uses:
+   splits = 0 restores the automatic choice; otherwise it is clamped to
+   [1, n_pages] at each call.  Results do not depend on it beyond rounding. */
+int kvq_set_decode_splits(kvq_cache *cache, int32_t splits);
+
+/* The page split count the next kvq_decode_attention call will use. */
+int kvq_get_decode_splits(const kvq_cache *cache, int32_t *splits);
+
+/* Host-side counters: pages per sequence and window tokens. */
+int kvq_get_state(const kvq_cache *cache, int32_t *n_pages, int32_t *n_res);
+
+/* Restore counters after the device bytes were restored (snapshot/restore).
+   Errors: KVQ_EINVAL for out-of-range values. */
+int kvq_set_state(kvq_cache *cache, int32_t n_pages, int32_t n_res);
+
+/* Byte offset of page (b, h, page) and of the window of (b, h) inside the
+   cache memory (for inspection and snapshots). */
+int kvq_page_offset(const kvq_cache *cache, int32_t b, int32_t h, int32_t page, size_t *off);
+int kvq_residual_offset(const kvq_cache *cache, int32_t b, int32_t h, size_t *k_off,
+                        size_t *v_off);
+
+/* Quantize arbitrary groups with the device quantizer (inspection and
+   exhaustive checks).  x: device [n_groups][group_len] dtype; s, z: device
+   [n_groups] dtype bits (uint16); codes: device [n_groups][group_len] uint8.
+   L in {3, 15}; 1 <= group_len <= 256. */
+int kvq_quantize_groups(int32_t dtype, int32_t L, const void *x, int32_t n_groups,
+                        int32_t group_len, void *s, void *z, void *codes, void *stream);
+
+/* Optional timing hooks: when set (non-NULL hipEvent_t values), decode
+   attention records `before` on its stream just before its split kernel and
+   `after` just after it.  NULL, NULL clears them. */
+int kvq_set_kernel_events(kvq_cache *cache, void *before, void *after);
+
+/* Static description of an error code. */
+const char *kvq_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -1,0 +1,181 @@
+"""C-ABI tests that need no GPU: the library loads, exports every declared
+symbol, and rejects bad calls with the documented codes before any launch.
+
+Handles below wrap a fake, never-dereferenced device address: every call
+checked here returns before launching a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+FAKE = 0x7f0000000000  # 16-byte aligned, never touched by host-side checks
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    from bit_mixed_precision_page_amd import kvq
+    return kvq
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(kvq_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    syms = declared_symbols()
+    for name in ("kvq_quantize_page", "kvq_append_token", "kvq_decode_attention"):
+        assert name in syms
+    assert len(syms) >= 17
+
+
+def test_library_exports_every_declared_symbol(kvq):
+    lib = ctypes.CDLL(kvq.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(lib, name), f"{name} not exported"
+    assert set(declared_symbols()) == set(kvq.EXPORTS)
+
+
+def _cfg(kvq, **kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, boost_channels=16, max_pages=4,
+                dtype=kvq.KVQ_BF16)
+    base.update(kw)
+    return kvq.config(**base)
+
+
+def test_sizes_match_the_layout(kvq, ora):
+    for k in (0, 16, 32, 128):
+        c = _cfg(kvq, boost_channels=k)
+        pb = kvq.kvq_page_bytes(c)
+        assert pb == ora.page_bytes(k)
+        assert kvq.kvq_cache_bytes(c) == 2 * 2 * 4 * pb + 2 * 2 * 2 * 128 * 128 * 2
+    assert kvq.kvq_page_bytes(_cfg(kvq, boost_channels=16)) == 12816
+    assert kvq.kvq_page_bytes(_cfg(kvq, boost_channels=32)) == 13344
+
+
+@pytest.mark.parametrize("bad", [
+    dict(head_dim=64), dict(page_tokens=64), dict(key_group_tokens=16),
+    dict(value_group_channels=64), dict(residual_tokens=64), dict(boost_channels=8),
+    dict(boost_channels=144), dict(boost_channels=-16), dict(num_q_heads=6),
+    dict(num_q_heads=12, num_kv_heads=4), dict(num_q_heads=64, num_kv_heads=2),
+    dict(batch=0), dict(max_pages=0), dict(dtype=2), dict(softmax_scale=float("inf")),
+])
+def test_bad_configs_are_rejected(kvq, bad):
+    c = _cfg(kvq, **bad)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_cache_bytes(c)
+    assert e.value.name == "KVQ_EINVAL"
+
+
+def _handle(kvq, **kw):
+    c = _cfg(kvq, **kw)
+    return kvq.kvq_cache_create(c, FAKE, kvq.kvq_cache_bytes(c)), c
+
+
+def test_create_checks(kvq):
+    c = _cfg(kvq)
+    n = kvq.kvq_cache_bytes(c)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_cache_create(c, FAKE + 8, n)
+    assert e.value.name == "KVQ_EALIGN"
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_cache_create(c, FAKE, n - 1)
+    assert e.value.name == "KVQ_EINVAL"
+    h = kvq.kvq_cache_create(c, FAKE, n)
+    assert kvq.kvq_get_state(h) == (0, 0)
+    kvq.kvq_cache_destroy(h)
+
+
+def test_call_errors_leave_state_unchanged(kvq):
+    h, c = _handle(kvq)
+    ws = kvq.kvq_decode_workspace_bytes(h)
+    assert ws > 0
+    # empty cache
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_attention(h, FAKE, FAKE, FAKE, ws, 0)
+    assert e.value.name == "KVQ_EEMPTY"
+    # capacity
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_quantize_page(h, FAKE, FAKE, 5, 0)
+    assert e.value.name == "KVQ_ECAPACITY"
+    # alignment
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_quantize_page(h, FAKE + 2, FAKE, 1, 0)
+    assert e.value.name == "KVQ_EALIGN"
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_append_token(h, FAKE, FAKE + 4, 0)
+    assert e.value.name == "KVQ_EALIGN"
+    # bulk quantization needs an empty window
+    kvq.kvq_set_state(h, 1, 5)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_quantize_page(h, FAKE, FAKE, 1, 0)
+    assert e.value.name == "KVQ_ESTATE"
+    assert kvq.kvq_get_state(h) == (1, 5)
+    # workspace
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_attention(h, FAKE, FAKE, FAKE, ws - 1, 0)
+    assert e.value.name == "KVQ_EWORKSPACE"
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_attention(h, FAKE + 2, FAKE, FAKE, ws, 0)
+    assert e.value.name == "KVQ_EALIGN"
+    # a full window with no free page cannot flush
+    kvq.kvq_set_state(h, 4, 128)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_append_token(h, FAKE, FAKE, 0)
+    assert e.value.name == "KVQ_ECAPACITY"
+    assert kvq.kvq_get_state(h) == (4, 128)
+    # counters
+    for bad in [(-1, 0), (5, 0), (0, 129), (0, -1)]:
+        with pytest.raises(kvq.KvqError):
+            kvq.kvq_set_state(h, *bad)
+    assert kvq.kvq_get_state(h) == (4, 128)
+    kvq.kvq_quantize_page(h, FAKE, FAKE, 0, 0)  # zero pages: a no-op
+    kvq.kvq_cache_destroy(h)
+
+
+def test_offsets_follow_the_layout(kvq):
+    h, c = _handle(kvq)
+    pb = kvq.kvq_page_bytes(c)
+    assert kvq.kvq_page_offset(h, 1, 1, 2) == ((1 * 2 + 1) * 4 + 2) * pb
+    base = 2 * 2 * 4 * pb
+    ko, vo = kvq.kvq_residual_offset(h, 1, 0)
+    assert ko == base + 2 * 2 * 128 * 128 * 2 and vo == ko + 128 * 128 * 2
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_page_offset(h, 2, 0, 0)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_page_offset(h, 0, 0, 4)
+    kvq.kvq_cache_destroy(h)
+
+
+def test_decode_split_choice(kvq):
+    h, c = _handle(kvq, max_pages=64)
+    kvq.kvq_set_state(h, 63, 128)
+    auto = kvq.kvq_get_decode_splits(h)
+    assert 1 <= auto <= 63
+    for s, want in [(1, 1), (7, 7), (63, 63), (1000, 63)]:
+        kvq.kvq_set_decode_splits(h, s)
+        got = kvq.kvq_get_decode_splits(h)
+        # pages per split = ceil(63 / s); splits = ceil(63 / pages per split)
+        pps = -(-63 // want)
+        assert got == -(-63 // pps)
+    kvq.kvq_set_decode_splits(h, 0)
+    assert kvq.kvq_get_decode_splits(h) == auto
+    kvq.kvq_cache_destroy(h)
+
+
+def test_quantize_groups_argument_checks(kvq):
+    for args in [(2, 3), (0, 7)]:
+        with pytest.raises(kvq.KvqError):
+            kvq.kvq_quantize_groups(args[0], args[1], FAKE, 1, 4, FAKE, FAKE, FAKE, 0)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_quantize_groups(0, 3, FAKE, 1, 257, FAKE, FAKE, FAKE, 0)
+    kvq.kvq_quantize_groups(0, 3, FAKE, 0, 4, FAKE, FAKE, FAKE, 0)  # no groups: no-op
+
+
+def test_strerror(kvq):
+    for code in range(-7, 1):
+        assert kvq.kvq_strerror(code)

@@ -1,0 +1,159 @@
+"""GPU path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bars: page bytes, window bytes, quantizer outputs and channel selections are
+bit-exact; attention is within max-abs 1e-3 of the oracle's fp64 attention
+over the same dequantized cache.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from bit_mixed_precision_page_amd import inputs as gen
+from gpu_util import Pair, dev, first_page_mismatch, host
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+W = gen.WORKLOADS
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def check_pages(pair):
+    g = pair.pages()
+    o = pair.ora.pages
+    msg = first_page_mismatch(g[:, :, :pair.ora.n_pages], o[:, :, :pair.ora.n_pages])
+    assert msg is None, msg
+    kw, vw = pair.windows()
+    n = pair.ora.n_res
+    assert (kw[:, :, :n] == pair.ora.kres[:, :, :n]).all()
+    assert (vw[:, :, :n] == pair.ora.vres[:, :, :n]).all()
+
+
+def check_attention(pair, q, splits=0, tol=TOL):
+    got = pair.attention(q, splits)
+    ref = pair.ora.attention(q)
+    err = np.abs(got - ref).max()
+    say(f"    max |gpu - oracle| = {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= tol, f"max abs error {err}"
+    return got
+
+
+def test_quantize_groups_every_range(ora):
+    """Device quantizer vs the oracle on groups whose maximum runs over every
+    positive finite pattern of each dtype (so every reachable scale and its
+    IEEE reciprocal is exercised), for L = 3 and 15."""
+    from bit_mixed_precision_page_amd import kvq
+    r = np.random.default_rng(99)
+    for dt in (gen.F16, gen.BF16):
+        bits = np.arange(1, 0x7C00 if dt == gen.F16 else 0x7F80, dtype=np.uint16)
+        M = gen.from_bits(bits, dt).astype(np.float64)
+        n, glen = len(bits), 8
+        frac = r.random((n, glen - 2))
+        x = np.concatenate([np.zeros((n, 1)), M[:, None], M[:, None] * frac], axis=1)
+        sign = np.where(r.random(n) < 0.3, -1.0, 1.0)[:, None]
+        xb = gen.to_bits((x * sign).astype(np.float32), dt)
+        for L in (3, 15):
+            s = torch.empty(n, dtype=torch.int16, device="cuda")
+            z = torch.empty(n, dtype=torch.int16, device="cuda")
+            c = torch.empty(n * glen, dtype=torch.uint8, device="cuda")
+            kvq.kvq_quantize_groups(dt, L, dev(xb), n, glen, s, z, c)
+            torch.cuda.synchronize()
+            s, z = host(s).view(np.uint16), host(z).view(np.uint16)
+            c = host(c).reshape(n, glen)
+            picks = np.concatenate([np.arange(0, n, 7), np.arange(n - 300, n)])
+            for i in picks:
+                so, zo, co = ora.quantize_group(dt, xb[i], L)
+                assert s[i] == so and z[i] == zo and (c[i] == co).all(), (dt, L, i, xb[i])
+        say(f"  dtype {dt}: {n} groups checked")
+
+
+def test_pages_tiny():
+    w = W["tiny"]
+    pair = Pair(w)
+    check_pages(pair)
+    check_attention(pair, pair.query())
+
+
+@pytest.mark.parametrize("name", list(W))
+def test_pages_and_attention_reduced(name):
+    """Every workload's distribution and dtype at a reduced batch and length."""
+    w = W[name]
+    pair = Pair(w, B=2, bulk_pages=5, window=37)
+    say(f"  {name}: k={pair.k} g={w.g} dtype={w.dtype}")
+    check_pages(pair)
+    check_attention(pair, pair.query())
+
+
+def test_append_flush_stream():
+    """300 streamed tokens from an empty cache: flushes at tokens 129 and 257."""
+    w = dataclasses.replace(W["qwen3_8b_long"], B=2)
+    pair = Pair(w, B=2, bulk_pages=0, window=300, max_pages=4)
+    assert [i for i, f in enumerate(pair.flushes) if f] == [128, 256]
+    assert pair.ora.n_pages == 2 and pair.ora.n_res == 44
+    check_pages(pair)
+    check_attention(pair, pair.query())
+
+
+@pytest.mark.parametrize("nres", [1, 77, 128])
+def test_window_only(nres):
+    pair = Pair(W["llama3_8b_decode"], B=2, bulk_pages=0, window=nres)
+    check_attention(pair, pair.query())
+
+
+def test_pages_only_no_window():
+    pair = Pair(W["llama3_8b_decode"], B=2, bulk_pages=3, window=0)
+    check_pages(pair)
+    check_attention(pair, pair.query())
+
+
+@pytest.mark.parametrize("boost", [0, 48, 128])
+def test_boost_extremes(boost):
+    pair = Pair(W["llama3_8b_decode"], B=1, bulk_pages=3, window=5, boost=boost)
+    check_pages(pair)
+    check_attention(pair, pair.query())
+
+
+@pytest.mark.parametrize("g", [1, 2, 8, 16])
+def test_query_group_sizes(g):
+    pair = Pair(W["llama3_8b_decode"], B=1, bulk_pages=2, window=9, Hq=8 * g)
+    check_attention(pair, pair.query())
+
+
+def test_softmax_scale_argument():
+    pair = Pair(W["tiny"], bulk_pages=2, window=3, scale=0.3)
+    check_attention(pair, pair.query())
+
+
+def test_split_invariance_and_determinism():
+    pair = Pair(W["llama3_8b_decode"], B=2, bulk_pages=20, window=100)
+    q = pair.query()
+    outs = {s: pair.attention(q, s) for s in (1, 3, 7, 20, 0)}
+    for s, o in outs.items():
+        assert np.abs(o - outs[1]).max() <= 1e-5, s
+    again = pair.attention(q, 0)
+    assert (again == outs[0]).all(), "decode attention must be deterministic"
+    ref = pair.ora.attention(q)
+    assert np.abs(outs[0] - ref).max() <= TOL
+
+
+def test_snapshot_restore():
+    """Pages are position-independent bytes: copy the cache memory into a fresh
+    buffer, restore the counters, and the output is bitwise identical."""
+    from bit_mixed_precision_page_amd import kvq
+    pair = Pair(W["tiny"], bulk_pages=3, window=40, with_oracle=False)
+    q = pair.query()
+    a = pair.attention(q)
+    c2 = kvq.Cache(pair.cfg)
+    c2.mem.copy_(pair.gpu.mem)
+    kvq.kvq_set_state(c2.handle, *pair.gpu.state)
+    out = torch.empty(pair.B, pair.Hq, 128, dtype=torch.float32, device="cuda")
+    c2.decode_attention(dev(q), out)
+    torch.cuda.synchronize()
+    assert (host(out) == a).all()
