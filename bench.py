@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the 2-bit mixed-precision KV cache on one MI355X.
+
+One step = one decode step of one attention layer: append the new token's K
+and V into the window (flushing a full window into a page when needed) and
+run split-K decode attention of the new query over the whole cache.  Layers
+rotate over enough independent cache replicas (>= 1 GiB) that every step
+reads its cache from HBM, not from the 256 MB Infinity Cache.  Inputs are
+seeded synthetic tensors of the workload's shape, resident in HBM before the
+timed region.
+
+Prints one JSON line: value = algorithmic bytes moved by the timed steps /
+elapsed time (GB/s); roofline = the split decode kernel's algorithmic bytes
+per launch / its average launch time (HIP events around each launch); and
+cpu_baseline = the CPU oracle timed on one full decode-attention call.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn effective HBM GB/s (packed KV) + tokens/s at 8K ctx, % of HBM peak"
+HBM_PEAK_GBS = 8000.0
+PAGE = 128
+DECODE_SRC = os.path.join(ROOT, "bit_mixed_precision_page_amd", "csrc", "kvq_decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b_decode")
+    ap.add_argument("--rotate-bytes", type=float, default=1.1e9,
+                    help="bytes of cache replicas the steps rotate over")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splits", type=int, default=0, help="page splits (0 = automatic)")
+    return ap.parse_args()
+
+
+def attention_bytes(w, k_page_bytes, n_pages, n_res):
+    """Algorithmic bytes of one decode-attention call: every packed page, every
+    window token (K and V), the query and the fp32 output."""
+    units = w.B * w.Hkv
+    return (units * (n_pages * k_page_bytes + n_res * 2 * 128 * 2) + w.B * w.Hq * 128 * 2 +
+            w.B * w.Hq * 128 * 4)
+
+
+def append_bytes(w, k_page_bytes, flushed):
+    """Append: read the token's K and V, write them into the window; a flush
+    also reads the 128-token window and writes one page."""
+    units = w.B * w.Hkv
+    b = units * 2 * 128 * 2 * 2
+    if flushed:
+        b += units * (128 * 128 * 2 * 2 + k_page_bytes)
+    return b
+
+
+def pmc_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__pmc.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the path shards by (sequence, KV head) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from bit_mixed_precision_page_amd import inputs as gen
+    from bit_mixed_precision_page_amd import kvq
+
+    w = gen.WORKLOADS[a.workload]
+    if w.decode_steps:
+        raise SystemExit("the long streaming workload is a parity case, not a bench line")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+
+    t0 = time.time()
+    print(f"[bench] workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} ctx={w.ctx} k={w.boost}",
+          file=sys.stderr, flush=True)
+    # Cache state: (ctx/128 - 1) bulk pages + 127 window tokens, so that the
+    # first timed append brings every layer to exactly ctx tokens.
+    bulk = w.ctx // PAGE - 1
+    n_win = PAGE - 1
+    K, V = gen.prefill_kv(w, ntok=bulk * PAGE + n_win)
+    steps_total = a.warmup + a.steps
+    max_pages = w.ctx // PAGE + 1 + (steps_total // PAGE + 2)
+    cfg = kvq.config(w.B, w.Hq, w.Hkv, w.boost, max_pages, w.dtype)
+    base = kvq.Cache(cfg, device=dev)
+    Kd = to_dev(K[:, :, :bulk * PAGE])
+    Vd = to_dev(V[:, :, :bulk * PAGE])
+    base.quantize_page(Kd, Vd, bulk)
+    for t in range(n_win):
+        base.append_token(to_dev(K[:, :, bulk * PAGE + t]), to_dev(V[:, :, bulk * PAGE + t]))
+    torch.cuda.synchronize()
+    del Kd, Vd
+    n_pages0, n_res0 = base.state
+    layers = max(2, math.ceil(a.rotate_bytes / base.nbytes))
+    caches = [base]
+    for _ in range(layers - 1):
+        c = kvq.Cache(cfg, device=dev)
+        c.mem.copy_(base.mem)
+        kvq.kvq_set_state(c.handle, n_pages0, n_res0)
+        caches.append(c)
+    if a.splits:
+        for c in caches:
+            kvq.kvq_set_decode_splits(c.handle, a.splits)
+    # Per-step inputs, resident before timing.
+    qs, kts, vts = [], [], []
+    for s in range(steps_total):
+        qs.append(to_dev(gen.query(w, step=s)))
+        kt, vt = gen.step_kv(w, s)
+        kts.append(to_dev(kt))
+        vts.append(to_dev(vt))
+    out = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    for e0, e1 in evs:  # materialize the events so their handles exist
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    print(f"[bench] setup {time.time() - t0:.1f}s; {layers} layer replicas of "
+          f"{base.nbytes / 1e6:.1f} MB; state {n_pages0} pages + {n_res0} window",
+          file=sys.stderr, flush=True)
+
+    pb = base.page_bytes
+    state = [list(c.state) for c in caches]
+
+    def step(s, ev=None):
+        li = s % layers
+        c = caches[li]
+        if ev is not None:
+            kvq.kvq_set_kernel_events(c.handle, ev[0]._as_parameter_.value,
+                                      ev[1]._as_parameter_.value)
+        flushed = c.append_token(kts[s], vts[s])
+        c.decode_attention(qs[s], out)
+        if ev is not None:
+            kvq.kvq_set_kernel_events(c.handle, None, None)
+        n_pages, n_res = c.state
+        return flushed, n_pages, n_res
+
+    for s in range(a.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    total_bytes = 0
+    attn_bytes_sum = 0
+    split_bytes = []
+    n_flush = 0
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(a.steps):
+        s = a.warmup + i
+        flushed, n_pages, n_res = step(s, evs[i])
+        ab = attention_bytes(w, pb, n_pages, n_res)
+        attn_bytes_sum += ab
+        total_bytes += ab + append_bytes(w, pb, flushed)
+        split_bytes.append(ab - w.B * w.Hq * 128 * 4)  # pages + window + query
+        n_flush += int(flushed)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ms_step = ms / a.steps
+    kern_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    kern_avg_s = float(kern_ms.mean()) / 1e3
+    achieved = float(np.mean(split_bytes)) / kern_avg_s / 1e9
+    value = total_bytes / (ms / 1e3) / 1e9
+    attn_gbs = attn_bytes_sum / (ms / 1e3) / 1e9
+    splits = kvq.kvq_get_decode_splits(caches[0].handle)
+    print(f"[bench] {a.steps} steps in {ms:.3f} ms ({ms_step * 1e3:.1f} us/step, "
+          f"split kernel avg {kern_avg_s * 1e6:.1f} us, {n_flush} flushes)", file=sys.stderr,
+          flush=True)
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        import oracle
+        ora = oracle.lib()
+        oc = oracle.OracleCache(w.dtype, w.B, w.Hq, w.Hkv, w.boost, n_pages0 + 1)
+        oc.quantize_pages(K[:, :, :bulk * PAGE], V[:, :, :bulk * PAGE])
+        for t in range(n_win):
+            oc.append(K[:, :, bulk * PAGE + t], V[:, :, bulk * PAGE + t])
+        kt, vt = gen.step_kv(w, 0)
+        oc.append(kt, vt)
+        q0 = gen.query(w, step=0)
+        tc = time.time()
+        oc.attention(q0)
+        dt = time.time() - tc
+        b = attention_bytes(w, pb, oc.n_pages, oc.n_res)
+        cpu = {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": ora.num_threads(),
+               "kind": "oracle",
+               "sample": (f"one full decode-attention call ({w.B * w.Hkv} (sequence, KV head) "
+                          f"units, {oc.n_pages} pages + {oc.n_res} window tokens, fp64) "
+                          f"in {dt:.2f} s")}
+
+    traffic = pmc_traffic("decode_split_kernel", w.name)
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": 128, "ctx": w.ctx, "boost_channels": w.boost,
+                   "key_group": 32, "value_group": 32, "window": 128,
+                   "storage": "2-bit K/V pages + bf16 window",
+                   "layers_rotated": layers, "page_splits": splits},
+        "tokens_per_s": round(w.B / (ms_step / 1e3), 1),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "attention_gbs": round(attn_gbs, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
