@@ -65,7 +65,8 @@ size_t cache_bytes_of(const kvq::Geometry &G) {
 }
 
 int max_splits_of(const kvq::Geometry &G) {
-    return std::min(G.max_pages, kMaxSplits) + 1;  // page splits + the window split
+    // page splits + window splits (32 window tokens per split)
+    return std::min(G.max_pages, kMaxSplits) + kvq::R / 32;
 }
 
 kvq::DecodePlan plan_of(const kvq_cache *c) {
@@ -86,7 +87,7 @@ kvq::DecodePlan plan_of(const kvq_cache *c) {
         pl.pages_per_split = (c->n_pages + S - 1) / S;
         pl.page_splits = (c->n_pages + pl.pages_per_split - 1) / pl.pages_per_split;
     }
-    pl.total_splits = pl.page_splits + (c->n_res > 0 ? 1 : 0);
+    pl.total_splits = pl.page_splits + (c->n_res + 31) / 32;
     return pl;
 }
 

@@ -77,7 +77,7 @@ struct DecodePlan {
     int n_pages, n_res;
     int page_splits;      // splits over pages (0 when n_pages == 0)
     int pages_per_split;
-    int total_splits;     // page_splits + (n_res > 0)
+    int total_splits;     // page_splits + ceil(n_res / 32) window splits
     int max_splits;       // workspace stride (splits per (b, hq))
 };
 size_t decode_workspace_bytes(const Geometry &G, int max_splits);
