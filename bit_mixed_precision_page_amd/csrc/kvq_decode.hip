@@ -102,10 +102,18 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
 }
 
 __device__ __forceinline__ float dpp_quad_swap1(float v) {  // lane ^ 1 within a quad
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float dpp_quad_swap2(float v) {  // lane ^ 2 within a quad
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+// The workgroup is a single wave and LDS operations of a wave complete in
+// order, so ordering LDS writes before other lanes' reads needs only a
+// wave-scope fence; a workgroup barrier would also wait for the next page's
+// global loads that are in flight and defeat the prefetch.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 }
 __device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src, 64); }
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
@@ -133,38 +141,42 @@ struct PageRegs {
     uint4 meta[5];      // metadata copy, 16-byte chunks lane + 64 i
 };
 
+__device__ __forceinline__ void load_meta(PageRegs &R, const uint8_t *pg, const PageLayout &Ly,
+                                          int lane, int meta_chunks, uint32_t meta_a_bytes) {
+    // metadata: [K_scale K_zero K_idx] then [V_scale V_zero]
+#pragma unroll
+    for (int i = 0; i < 5; i++) {
+        int ch = min(lane + 64 * i, meta_chunks - 1);
+        uint32_t off = 16u * ch;
+        off = off < meta_a_bytes ? Ly.ks + off : Ly.vs + (off - meta_a_bytes);
+        R.meta[i] = *reinterpret_cast<const uint4 *>(pg + off);
+    }
+}
+
 template <int KH>
-__device__ __forceinline__ void load_page(PageRegs &R, const uint8_t *pg, const PageLayout &Ly,
-                                          int k, int lane, int meta_chunks, uint32_t meta_a_bytes) {
+__device__ __forceinline__ void load_codes(PageRegs &R, const uint8_t *pg, const PageLayout &Ly,
+                                           int k, int lane) {
     const int r = lane & 15, G4 = lane >> 4;
 #pragma unroll
     for (int mt = 0; mt < 8; mt++)
         R.klo[mt] = *reinterpret_cast<const uint2 *>(pg + Ly.klo + (16 * mt + r) * 32 + 8 * G4);
+    // Every load is issued unconditionally (indices clamped into the page) so
+    // the number of loads in flight is static and the compiler can wait for
+    // the current page's data without draining the prefetch of the next.
 #pragma unroll
     for (int mt = 0; mt < 8; mt++) {
 #pragma unroll
         for (int ms = 0; ms < KH; ms++) {
             int dw = 2 * ms + (G4 >> 1);
-            R.khi[mt][ms] = dw < k / 16
-                ? *reinterpret_cast<const uint32_t *>(pg + Ly.khi + (16 * mt + r) * (k / 4) + 4 * dw)
-                : 0u;
+            int dwc = dw < k / 16 ? dw : k / 16 - 1;
+            uint32_t v = *reinterpret_cast<const uint32_t *>(pg + Ly.khi + (16 * mt + r) * (k / 4) +
+                                                             4 * dwc);
+            R.khi[mt][ms] = dw < k / 16 ? v : 0u;
         }
     }
 #pragma unroll
     for (int s = 0; s < 4; s++)
         R.vc[s] = *reinterpret_cast<const uint4 *>(pg + Ly.vc + 1024 * s + 16 * lane);
-    // metadata: [K_scale K_zero K_idx] then [V_scale V_zero]
-#pragma unroll
-    for (int i = 0; i < 5; i++) {
-        int ch = lane + 64 * i;
-        if (ch < meta_chunks) {
-            uint32_t off = 16u * ch;
-            off = off < meta_a_bytes ? Ly.ks + off : Ly.vs + (off - meta_a_bytes);
-            R.meta[i] = *reinterpret_cast<const uint4 *>(pg + off);
-        } else {
-            R.meta[i] = make_uint4(0, 0, 0, 0);
-        }
-    }
 }
 
 template <int DT, int G, int KH>
@@ -176,8 +188,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     constexpr int HQ = (G + 3) / 4;       // quads of query heads
     constexpr int NHW = (G + 1) / 2;      // heads per lane in the window path
     __shared__ float qf[G][D];            // q * scale * log2(e)
-    __shared__ __align__(16) uint8_t meta[(P / GK) * D * 4 + 128 + (D / GV) * P * 4];
-    __shared__ __align__(16) uint32_t wB[HQ][4 + (KH > 0 ? KH : 1)][4][4][2][4];
+    __shared__ __align__(16) uint8_t meta[5 * 64 * 16];  // page metadata copy (16-byte chunks)
+    __shared__ __align__(16) u4_t wB[HQ][2][64];                     // lo-plane weights [hi/lo][lane]
+    __shared__ __align__(16) u4_t wBh[HQ][4][KH > 0 ? KH : 1][2][16];  // hi-plane weights [group]
+    __shared__ __align__(16) float vsf[D / GV][144];                   // V scale x 2^Eu, padded rows
+    __shared__ __align__(16) u4_t tq3[HQ][4][64];   // q pieces: B operand of the zero-point MFMA
+    __shared__ __align__(16) float tqs[HQ][64][8];  // q / 4^sig of each producer lane's slots
+    __shared__ __align__(16) float vzf[D / GV][144];                   // V zero, padded rows
     __shared__ float sw[G][32];
 
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -185,11 +202,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const int Hq = Hkv * G;
     const int lane = threadIdx.x, r = lane & 15, G4 = lane >> 4;
 
-    for (int i = lane; i < G * D; i += 64) {
-        int hh = i / D, c = i % D;
-        qf[hh][c] = dec<DT>(q[((size_t)b * Hq + h * G + hh) * D + c]) * qscale;
+    // q of the G query heads: one 16-byte load per lane per 64 chunks of 8 channels
+    for (int ch = lane; ch < G * (D / 8); ch += 64) {
+        int hh = ch / (D / 8), c0 = 8 * (ch % (D / 8));
+        uint4 v = *reinterpret_cast<const uint4 *>(q + ((size_t)b * Hq + h * G + hh) * D + c0);
+        uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            qf[hh][c0 + e] = dec<DT>((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * qscale;
     }
-    __syncthreads();
+    wave_sync();
 
     if (split >= page_splits) {
         // ---------------- window split: 32 exact tokens on the VALU ----------------
@@ -234,7 +256,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
             int hh = hs + 2 * j;
             if (hh < G) sw[hh][tl] = p;
         }
-        __syncthreads();
+        wave_sync();
         float acc[G][2];
 #pragma unroll
         for (int hh = 0; hh < G; hh++) acc[hh][0] = acc[hh][1] = 0.0f;
@@ -277,10 +299,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const uint16_t *mvz = mvs + (D / GV) * P;                                  // [4][128]
 
     // Fixed per call: q pieces as the B operand of the zero-point MFMA
-    // (column 4 h' + piece, pieces 0..2; k slot 8 G4 + e <-> channel 32 m + 8 G4 + e),
-    // and q of the two channels this lane produces weights for.
-    u4_t bq3[HQ][4];
-    float qmax = 0.0f;
+    // (column 4 h' + piece, pieces 0..2; k slot 8 G4 + e <-> channel 32 m + 8 G4 + e).
 #pragma unroll
     for (int qd = 0; qd < HQ; qd++) {
         int hh = 4 * qd + (r >> 2), pc = r & 3;
@@ -302,70 +321,65 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
                 }
                 dw[e2] = (uint32_t)pv[0] | ((uint32_t)pv[1] << 16);
             }
-            bq3[qd][m] = u4_t{dw[0], dw[1], dw[2], dw[3]};
+            tq3[qd][m][lane] = u4_t{dw[0], dw[1], dw[2], dw[3]};
         }
     }
-    // producer channels of this lane: c0 = 16 (lane / 8) + lane % 8 and c0 + 8
-    const int pc0 = 16 * (lane >> 3) + (lane & 7);
-    const int prem = lane & 7;  // extraction index j of (c0, c0 + 8) within its MFMA
-    const int pG4 = pc0 >> 5, pm = 2 * ((pc0 & 31) >> 4) + (prem >> 2), pi = prem & 3;
-    const float psig = 1.0f / (float)(1 << (2 * code_sig(prem)));
-    float qp0[G], qp1[G];
+    // Weight producer role of this lane (lo plane): K step pm = lane / 16, lane
+    // group pG = (lane / 4) % 4 and head ph = lane % 4 of each quad; its eight
+    // channels are pbase + i + 8 e (i < 4, e < 2), k slots 8 pG + 2 i + e of
+    // MFMA pm.  The 16 bytes it writes per (quad, hi/lo) are exactly what
+    // reader lane (col 4 ph + hi/lo, pG) loads for MFMA pm.
+    const int pm = lane >> 4, pG = (lane >> 2) & 3, ph = lane & 3;
+    const int pbase = 32 * pG + 16 * (pm >> 1) + 4 * (pm & 1);
 #pragma unroll
-    for (int hh = 0; hh < G; hh++) {
-        qp0[hh] = qf[hh][pc0];
-        qp1[hh] = qf[hh][pc0 + 8];
-    }
+    for (int qd = 0; qd < HQ; qd++)  // q'(head, channel) / 4^sig of this lane's slots
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int e = 0; e < 2; e++) {
+                int hh = 4 * qd + ph;
+                float sig = 1.0f / (float)(1 << (2 * code_sig(4 * (pm & 1) + i)));
+                tqs[qd][lane][2 * i + e] = hh < G ? qf[hh][pbase + i + 8 * e] * sig : 0.0f;
+            }
+    // hi-plane producer role: lane group hG and head ph (group = lane / 16)
+    const int hG = (lane >> 2) & 3;
+    const int hjb = 16 * (hG >> 1) + 4 * (hG & 1);
+    float qmax = 0.0f;
     for (int i = lane; i < G * D; i += 64) qmax = fmaxf(qmax, fabsf(qf[i / D][i % D]));
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) qmax = fmaxf(qmax, shfl_xor(qmax, o));
 
-    // hi-plane weight slots beyond k stay zero
-    for (int i = lane; i < (int)(sizeof(wB) / 4); i += 64) (&wB[0][0][0][0][0][0])[i] = 0u;
-
-    // PV accumulators: lane (r, G4) keeps, per quad and 16-channel tile n, the
-    // one useful MFMA element (row = head G4, Value group n / 2).  Each 32-token
-    // step starts its MFMA chain from zero and is added here in fp32 with
-    // round-to-nearest: the matrix cores truncate when adding into a large
-    // accumulator, which would bias long chains of non-negative products.
-    float acc[HQ][8];
-#pragma unroll
-    for (int qd = 0; qd < HQ; qd++)
-#pragma unroll
-        for (int n = 0; n < 8; n++) acc[qd][n] = 0.0f;
+    float acc[HQ][8];  // lane (r, G4): head 4 qd + G4, channel 16 n + r (scaled by 2^Eu ...)
     float m_run[HQ], l_part[HQ], zt[HQ];
-    // PV operand exponent: u = p s_v is scaled by 2^Eu so that its fp16 hi and
-    // lo parts stay normal; Eu only decreases along a split, and the
-    // accumulators are rescaled exactly when it does.
-    int Eu = 1000;
 #pragma unroll
     for (int qd = 0; qd < HQ; qd++) {
         m_run[qd] = -INFINITY;
         l_part[qd] = 0.0f;
         zt[qd] = 0.0f;
+#pragma unroll
+        for (int n = 0; n < 8; n++) acc[qd][n] = 0.0f;
     }
+    int Eu = 1000;
 
     const int p0 = split * pps;
     const int p1 = min(n_pages, p0 + pps);
     const uint8_t *ubase = cache + (size_t)unit * max_pages * page_bytes;
     PageRegs cur;
-    load_page<KH>(cur, ubase + (size_t)p0 * page_bytes, Ly, k, lane, meta_chunks, meta_a);
+    load_codes<KH>(cur, ubase + (size_t)p0 * page_bytes, Ly, k, lane);
+    load_meta(cur, ubase + (size_t)p0 * page_bytes, Ly, lane, meta_chunks, meta_a);
 
     for (int p = p0; p < p1; p++) {
+        // prefetch of the next page (the last page is loaded again at the end:
+        // harmless): codes now, metadata once this page's copy is in LDS
+        const uint8_t *pnext = ubase + (size_t)min(p + 1, p1 - 1) * page_bytes;
         PageRegs nxt;
-        if (p + 1 < p1)
-            load_page<KH>(nxt, ubase + (size_t)(p + 1) * page_bytes, Ly, k, lane, meta_chunks,
-                          meta_a);
-        __syncthreads();  // previous page's metadata reads are done
+        load_codes<KH>(nxt, pnext, Ly, k, lane);
+        wave_sync();  // previous page's LDS reads are done
 #pragma unroll
-        for (int i = 0; i < 5; i++) {
-            int ch = lane + 64 * i;
-            if (ch < meta_chunks) reinterpret_cast<uint4 *>(meta)[ch] = cur.meta[i];
-        }
-        __syncthreads();
+        for (int i = 0; i < 5; i++) reinterpret_cast<uint4 *>(meta)[lane + 64 * i] = cur.meta[i];
+        load_meta(nxt, pnext, Ly, lane, meta_chunks, meta_a);
 
-        // Page exponent: every weight operand |4 w 2^E / 4^sig| <= |w| 2^(E-2) <=
-        // qmax max(s) 2^(E-2) <= 2^14.
+        // Page exponent of the weights: |4 w 2^E / 4^sig| <= qmax max(s) 2^(E-2) <= 2^14.
         float smax = 0.0f;
         {
             uint4 c = cur.meta[0];  // chunks 0..63 are exactly K_scale (1024 B)
@@ -378,25 +392,47 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
         }
         int eb;
         frexpf(qmax * smax, &eb);
-        const int E = min(100, max(-60, 16 - eb));
-        float vsmax = 0.0f;
-        {
-            const uint4 c = *reinterpret_cast<const uint4 *>(mvs + 8 * lane);  // V_scale[4][128]
-            uint32_t wv[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                vsmax = fmaxf(vsmax, fabsf(dec<DT>((uint16_t)(wv[e >> 1] >> (16 * (e & 1))))));
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) vsmax = fmaxf(vsmax, shfl_xor(vsmax, o));
-        }
-        int ev;
-        frexpf(vsmax, &ev);
-        const int Eu_new = min(Eu, min(100, max(-60, 14 - ev)));
-        const float urescale = ldexpf(1.0f, max(Eu_new - Eu, -126));
-        Eu = Eu_new;
-        const float uscale = ldexpf(1.0f, Eu);
+        const int E = __builtin_amdgcn_readfirstlane(min(100, max(-60, 16 - eb)));
         const float wscale = ldexpf(1.0f, E);
         const float sback = ldexpf(1.0f, 24 - E);
+        wave_sync();
+
+        // Value scales and zeros as fp32 tables (padded rows: conflict-free reads),
+        // scales multiplied by 2^Eu so that u = p s_v splits into normal fp16 parts.
+        float vsr[8], vzr[8];
+        {
+            const int cg = lane >> 4, t8 = 8 * (lane & 15);
+            uint4 sv = *reinterpret_cast<const uint4 *>(mvs + cg * P + t8);
+            uint4 zv = *reinterpret_cast<const uint4 *>(mvz + cg * P + t8);
+            uint32_t sw4[4] = {sv.x, sv.y, sv.z, sv.w}, zw4[4] = {zv.x, zv.y, zv.z, zv.w};
+            float vmax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                vsr[e] = dec<DT>((uint16_t)(sw4[e >> 1] >> (16 * (e & 1))));
+                vzr[e] = dec<DT>((uint16_t)(zw4[e >> 1] >> (16 * (e & 1))));
+                vmax = fmaxf(vmax, fabsf(vsr[e]));
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) vmax = fmaxf(vmax, shfl_xor(vmax, o));
+            int ev;
+            frexpf(vmax, &ev);
+            const int Eu_new = __builtin_amdgcn_readfirstlane(min(Eu, min(100, max(-60, 14 - ev))));
+            const float urescale = ldexpf(1.0f, max(Eu_new - Eu, -126));
+            Eu = Eu_new;
+            const float uscale = ldexpf(1.0f, Eu);
+#pragma unroll
+            for (int e = 0; e < 8; e++) vsr[e] *= uscale;
+            float *vst = &vsf[cg][t8];
+            float *vzt = &vzf[cg][t8];
+            *reinterpret_cast<float4 *>(vst) = make_float4(vsr[0], vsr[1], vsr[2], vsr[3]);
+            *reinterpret_cast<float4 *>(vst + 4) = make_float4(vsr[4], vsr[5], vsr[6], vsr[7]);
+            *reinterpret_cast<float4 *>(vzt) = make_float4(vzr[0], vzr[1], vzr[2], vzr[3]);
+            *reinterpret_cast<float4 *>(vzt + 4) = make_float4(vzr[4], vzr[5], vzr[6], vzr[7]);
+#pragma unroll
+            for (int qd = 0; qd < HQ; qd++)
+#pragma unroll
+                for (int n = 0; n < 8; n++) acc[qd][n] *= urescale;
+        }
 
         // Zero-point term per (head, group): bias = sum_c q'(h, c) z(g, c).
         float bias[HQ][4];
@@ -410,7 +446,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
             for (int qd = 0; qd < HQ; qd++) {
                 f4_t cb = {0, 0, 0, 0};
 #pragma unroll
-                for (int m = 0; m < 4; m++) cb = mfma_dt<DT>(az[m], bq3[qd][m], cb);
+                for (int m = 0; m < 4; m++) cb = mfma_dt<DT>(az[m], tq3[qd][m][lane], cb);
 #pragma unroll
                 for (int g = 0; g < 4; g++) {
                     float v = cb[g];
@@ -420,48 +456,81 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
                 }
             }
         }
-
-        float sc[HQ][4][2][4];  // scores: [quad][group][M-tile][row] for head 4 qd + r / 4
+        // Hi-plane weights of all four groups, once per page: lane = 16 g + 4 hG + ph
+        // computes 4 q'(head, idx[j]) s(g, idx[j]) 2^E / 4^sig_hi(i) for the boosted
+        // slots j = 32 ms + 16 (hG / 2) + 4 (hG % 2) + i + 8 e of K step ms.
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-            // --- produce this group's B operands (weights) into LDS ---
-            __syncthreads();
-            {
-                float s0 = dec<DT>(mks[g * D + pc0]) * wscale * psig;
-                float s1 = dec<DT>(mks[g * D + pc0 + 8]) * wscale * psig;
+        for (int ms = 0; ms < KH; ms++) {
+            const int hg = lane >> 4;
+            float wv[HQ][4][2];
 #pragma unroll
-                for (int hh = 0; hh < G; hh++) {
-                    uint32_t hi, lo;
-                    split2(qp0[hh] * s0, qp1[hh] * s1, hi, lo);
-                    wB[hh >> 2][pm][pG4][hh & 3][0][pi] = hi;
-                    wB[hh >> 2][pm][pG4][hh & 3][1][pi] = lo;
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int e = 0; e < 2; e++) {
+                    const int j = 32 * ms + hjb + i + 8 * e;
+                    const int c = j < k ? (int)midx[j] : -1;
+                    const float sv = c >= 0 ? dec<DT>(mks[hg * D + c]) : 0.0f;
+                    const float f = 4.0f * wscale / (float)(1 << (2 * (2 + (i & 1))));
+#pragma unroll
+                    for (int qd = 0; qd < HQ; qd++) {
+                        const int hh = 4 * qd + ph;
+                        wv[qd][i][e] = c >= 0 && hh < G ? qf[hh][c] * sv * f : 0.0f;
+                    }
                 }
-                // hi plane: pairs (j0, j0 + 8) of boosted channels, weight 4 w / 4^i
-                const int ntask = G * (KH * 16);
-                for (int task = lane; task < ntask; task += 64) {
-                    int hh = task / (KH * 16), jj = task % (KH * 16);
-                    int ms = jj >> 4, rem = jj & 15;  // rem: 16 (G4b / 2) + 4 (G4b % 2) + i
-                    int j0 = 32 * ms + 16 * (rem >> 3) + (rem & 7);
-                    if (j0 >= k) continue;
-                    int G4b = 2 * (rem >> 3) + ((rem & 7) >> 2), i = rem & 3;
-                    float f = 4.0f * wscale / (float)(1 << (2 * (2 + (i & 1))));
-                    int ca = midx[j0], cb = j0 + 8 < k ? midx[j0 + 8] : -1;
-                    float wa = qf[hh][ca] * dec<DT>(mks[g * D + ca]) * f;
-                    float wb = cb >= 0 ? qf[hh][cb] * dec<DT>(mks[g * D + cb]) * f : 0.0f;
-                    uint32_t hi, lo;
-                    split2(wa, wb, hi, lo);
-                    wB[hh >> 2][4 + ms][G4b][hh & 3][0][i] = hi;
-                    wB[hh >> 2][4 + ms][G4b][hh & 3][1][i] = lo;
-                }
-            }
-            __syncthreads();
-            // --- QK on the matrix cores ---
 #pragma unroll
             for (int qd = 0; qd < HQ; qd++) {
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) split2(wv[qd][i][0], wv[qd][i][1], hi[i], lo[i]);
+                wBh[qd][hg][ms][0][lane & 15] = u4_t{hi[0], hi[1], hi[2], hi[3]};
+                wBh[qd][hg][ms][1][lane & 15] = u4_t{lo[0], lo[1], lo[2], lo[3]};
+            }
+        }
+        float qlo[HQ][4][2];
+#pragma unroll
+        for (int qd = 0; qd < HQ; qd++) {
+            float4 a = *reinterpret_cast<const float4 *>(&tqs[qd][lane][0]);
+            float4 c = *reinterpret_cast<const float4 *>(&tqs[qd][lane][4]);
+            const float t8[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int e = 0; e < 2; e++) qlo[qd][i][e] = t8[2 * i + e] * wscale;
+        }
+
+        const int cgr = r & 3;  // Value group of this lane's PV row
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            // --- weights of this group into LDS: lo plane and hi plane ---
+            wave_sync();  // previous group's weight reads are done
+            {
+                uint2 sa = *reinterpret_cast<const uint2 *>(mks + g * D + pbase);
+                uint2 sb = *reinterpret_cast<const uint2 *>(mks + g * D + pbase + 8);
+                float s0[4] = {dec<DT>((uint16_t)(sa.x & 0xffff)), dec<DT>((uint16_t)(sa.x >> 16)),
+                               dec<DT>((uint16_t)(sa.y & 0xffff)), dec<DT>((uint16_t)(sa.y >> 16))};
+                float s1[4] = {dec<DT>((uint16_t)(sb.x & 0xffff)), dec<DT>((uint16_t)(sb.x >> 16)),
+                               dec<DT>((uint16_t)(sb.y & 0xffff)), dec<DT>((uint16_t)(sb.y >> 16))};
+#pragma unroll
+                for (int qd = 0; qd < HQ; qd++) {
+                    uint32_t hi[4], lo[4];
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        split2(qlo[qd][i][0] * s0[i], qlo[qd][i][1] * s1[i], hi[i], lo[i]);
+                    wB[qd][0][lane] = u4_t{hi[0], hi[1], hi[2], hi[3]};
+                    wB[qd][1][lane] = u4_t{lo[0], lo[1], lo[2], lo[3]};
+                }
+            }
+            wave_sync();
+#pragma unroll
+            for (int qd = 0; qd < HQ; qd++) {
+                // --- QK on the matrix cores: two 16-token tiles ---
+                const int hl = r & 1, hp = r >> 2;
                 u4_t bw[4 + (KH > 0 ? KH : 1)];
 #pragma unroll
-                for (int m = 0; m < 4 + KH; m++)
-                    bw[m] = *reinterpret_cast<const u4_t *>(&wB[qd][m][G4][r >> 2][r & 1][0]);
+                for (int m = 0; m < 4; m++) bw[m] = wB[qd][hl][16 * m + 4 * G4 + hp];
+#pragma unroll
+                for (int ms = 0; ms < KH; ms++) bw[4 + ms] = wBh[qd][g][ms][hl][4 * G4 + hp];
+                float sc[2][4];
 #pragma unroll
                 for (int mt = 0; mt < 2; mt++) {
                     const uint2 kl = cur.klo[2 * g + mt];
@@ -485,97 +554,66 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
                         c = mfma_f16(a, bw[4 + ms], c);
                     }
 #pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        float v = c[e];
-                        v += dpp_quad_swap1(v);  // hi + lo columns
-                        sc[qd][g][mt][e] = fmaf(v, sback, bias[qd][g]);
-                    }
+                    for (int e = 0; e < 4; e++)
+                        sc[mt][e] = fmaf(c[e] + dpp_quad_swap1(c[e]), sback, bias[qd][g]);
                 }
-            }
-        }
 
-        // --- online softmax over the page's 128 tokens, per head ---
-        float alpha[HQ];
+                // --- online softmax over these 32 tokens, per head ---
+                float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                                 fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+                mx = fmaxf(mx, shfl_xor(mx, 16));
+                mx = fmaxf(mx, shfl_xor(mx, 32));
+                if (__any(mx > m_run[qd])) {  // wave-uniform: rescale only when a max grows
+                    float mnew = fmaxf(m_run[qd], mx);
+                    float alpha = exp2f(m_run[qd] - mnew);
+                    m_run[qd] = mnew;
+                    l_part[qd] *= alpha;
+                    zt[qd] *= alpha;
+                    // accumulator lanes hold head G4 of the quad: that head's alpha
+                    float al = shfl(alpha, 4 * G4);
 #pragma unroll
-        for (int qd = 0; qd < HQ; qd++) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int g = 0; g < 4; g++)
-#pragma unroll
-                for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) mx = fmaxf(mx, sc[qd][g][mt][e]);
-            mx = fmaxf(mx, shfl_xor(mx, 16));
-            mx = fmaxf(mx, shfl_xor(mx, 32));
-            float mnew = fmaxf(m_run[qd], mx);
-            alpha[qd] = exp2f(m_run[qd] - mnew);
-            m_run[qd] = mnew;
-            float ls = 0.0f;
-#pragma unroll
-            for (int g = 0; g < 4; g++)
+                    for (int n = 0; n < 8; n++) acc[qd][n] *= al;
+                }
+                float pr[2][4];
 #pragma unroll
                 for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        float pv = exp2f(sc[qd][g][mt][e] - mnew);
-                        sc[qd][g][mt][e] = pv;
-                        ls += pv;
+                        pr[mt][e] = exp2f(sc[mt][e] - m_run[qd]);
+                        l_part[qd] += pr[mt][e];
                     }
-            l_part[qd] = l_part[qd] * alpha[qd] + ls;
-            zt[qd] *= alpha[qd];
-            // accumulator lanes hold head G4 of the quad: fetch that head's alpha
-            float al = shfl(alpha[qd], 4 * G4) * urescale;
-#pragma unroll
-            for (int n = 0; n < 8; n++) acc[qd][n] *= al;
-        }
 
-        // --- PV on the matrix cores, one 32-token step per Key group ---
-        const int cgr = r & 3;  // Value group of this lane's PV row
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const uint4 vb = cur.vc[g];
-            const uint32_t vx[4] = {vb.x, vb.y, vb.z, vb.w};
-            // token scales and zeros of this row's group, tokens 4 G4 + e and 16 + 4 G4 + e
-            float vs[8], vz[8];
-#pragma unroll
-            for (int mt = 0; mt < 2; mt++) {
-                const int t = 32 * g + 16 * mt + 4 * G4;
-                uint2 sv = *reinterpret_cast<const uint2 *>(mvs + cgr * P + t);
-                uint2 zv = *reinterpret_cast<const uint2 *>(mvz + cgr * P + t);
-                vs[4 * mt + 0] = dec<DT>((uint16_t)(sv.x & 0xffff)) * uscale;
-                vs[4 * mt + 1] = dec<DT>((uint16_t)(sv.x >> 16)) * uscale;
-                vs[4 * mt + 2] = dec<DT>((uint16_t)(sv.y & 0xffff)) * uscale;
-                vs[4 * mt + 3] = dec<DT>((uint16_t)(sv.y >> 16)) * uscale;
-                vz[4 * mt + 0] = dec<DT>((uint16_t)(zv.x & 0xffff));
-                vz[4 * mt + 1] = dec<DT>((uint16_t)(zv.x >> 16));
-                vz[4 * mt + 2] = dec<DT>((uint16_t)(zv.y & 0xffff));
-                vz[4 * mt + 3] = dec<DT>((uint16_t)(zv.y >> 16));
-            }
-            const Codes8 v0(vx[0]), v1(vx[1]), v2(vx[2]), v3(vx[3]);
-            u4_t bv[8];
-#pragma unroll
-            for (int n = 0; n < 8; n++) bv[n] = u4_t{v0[n], v1[n], v2[n], v3[n]};
-#pragma unroll
-            for (int qd = 0; qd < HQ; qd++) {
+                // --- PV on the matrix cores (32 tokens x 16-channel tiles) ---
                 uint32_t ahi[4], alo[4];
+                {
+                    const int t = 32 * g + 4 * G4;
+                    float4 s0 = *reinterpret_cast<const float4 *>(&vsf[cgr][t]);
+                    float4 s1 = *reinterpret_cast<const float4 *>(&vsf[cgr][t + 16]);
+                    float4 z0 = *reinterpret_cast<const float4 *>(&vzf[cgr][t]);
+                    float4 z1 = *reinterpret_cast<const float4 *>(&vzf[cgr][t + 16]);
+                    const float vs8[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+                    const float vz8[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
-                for (int e2 = 0; e2 < 4; e2++) {
-                    float pa = sc[qd][g][e2 >> 1][2 * (e2 & 1)];
-                    float pb = sc[qd][g][e2 >> 1][2 * (e2 & 1) + 1];
-                    split2(pa * vs[2 * e2], pb * vs[2 * e2 + 1], ahi[e2], alo[e2]);
-                    zt[qd] = fmaf(pa, vz[2 * e2], fmaf(pb, vz[2 * e2 + 1], zt[qd]));
+                    for (int e2 = 0; e2 < 4; e2++) {
+                        float pa = pr[e2 >> 1][2 * (e2 & 1)], pb = pr[e2 >> 1][2 * (e2 & 1) + 1];
+                        split2(pa * vs8[2 * e2], pb * vs8[2 * e2 + 1], ahi[e2], alo[e2]);
+                        zt[qd] = fmaf(pa, vz8[2 * e2], fmaf(pb, vz8[2 * e2 + 1], zt[qd]));
+                    }
                 }
-                u4_t a_hi = {ahi[0], ahi[1], ahi[2], ahi[3]};
-                u4_t a_lo = {alo[0], alo[1], alo[2], alo[3]};
+                const u4_t a_hi = {ahi[0], ahi[1], ahi[2], ahi[3]};
+                const u4_t a_lo = {alo[0], alo[1], alo[2], alo[3]};
+                const uint4 vb = cur.vc[g];
+                const Codes8 v0(vb.x), v1(vb.y), v2(vb.z), v3(vb.w);
 #pragma unroll
                 for (int n = 0; n < 8; n++) {
-                    f4_t cs = mfma_f16(a_hi, bv[n], f4_t{0, 0, 0, 0});
-                    cs = mfma_f16(a_lo, bv[n], cs);
+                    const u4_t bv = {v0[n], v1[n], v2[n], v3[n]};
+                    f4_t cs = mfma_f16(a_hi, bv, f4_t{0, 0, 0, 0});
+                    cs = mfma_f16(a_lo, bv, cs);
                     acc[qd][n] += cs[n >> 1];
                 }
             }
         }
-        if (p + 1 < p1) cur = nxt;
+        cur = nxt;
     }
 
     // --- partials: lane (c_local = r, G4) owns head 4 qd + G4, channels 16 n + r ---
@@ -626,6 +664,25 @@ __global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ ws
     out[bq * D + c] = num / den;
 }
 
+// Resident workgroups of this instantiation on the whole device (occupancy API),
+// cached; 2048 when no device answers (host-only use).
+template <int DT, int G, int KH>
+int slots3() {
+    static int cached = 0;
+    if (cached) return cached;
+    int per_cu = 0, dev = 0;
+    hipDeviceProp_t prop;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<DT, G, KH>,
+                                                     64, 0) != hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+        per_cu <= 0) {
+        (void)hipGetLastError();
+        return 2048;
+    }
+    cached = per_cu * prop.multiProcessorCount;
+    return cached;
+}
+
 template <int DT, int G, int KH>
 hipError_t launch3(const Geometry &Gm, const uint8_t *cache, const uint16_t *q, float *ml,
                    float *acc, const DecodePlan &pl, hipStream_t st) {
@@ -663,7 +720,32 @@ hipError_t launch1(const Geometry &Gm, const uint8_t *cache, const uint16_t *q, 
     }
 }
 
+template <int DT, int G>
+int slots2(int k) {
+    switch ((k + 31) / 32) {
+        case 0: return slots3<DT, G, 0>();
+        case 1: return slots3<DT, G, 1>();
+        case 2: return slots3<DT, G, 2>();
+        case 3: return slots3<DT, G, 3>();
+        default: return slots3<DT, G, 4>();
+    }
+}
+template <int DT>
+int slots1(int g, int k) {
+    switch (g) {
+        case 1: return slots2<DT, 1>(k);
+        case 2: return slots2<DT, 2>(k);
+        case 4: return slots2<DT, 4>(k);
+        case 8: return slots2<DT, 8>(k);
+        default: return slots2<DT, 16>(k);
+    }
+}
+
 }  // namespace
+
+int decode_slots(const Geometry &G) {
+    return G.dtype == F16 ? slots1<F16>(G.g, G.k) : slots1<BF16>(G.g, G.k);
+}
 
 size_t decode_workspace_bytes(const Geometry &G, int max_splits) {
     size_t rows = (size_t)G.B * G.Hq * max_splits;

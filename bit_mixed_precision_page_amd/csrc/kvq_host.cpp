@@ -79,9 +79,11 @@ kvq::DecodePlan plan_of(const kvq_cache *c) {
         if (c->splits_override > 0) {
             S = c->splits_override;
         } else {
-            // aim for ~8 workgroups per compute unit (256 CUs)
+            // One round of resident single-wave workgroups (occupancy of this
+            // kernel instance x compute units), shared with the window splits.
             int units = c->G.B * c->G.Hkv;
-            S = (2048 + units - 1) / units;
+            int win = (c->n_res + 31) / 32;
+            S = std::max(1, kvq::decode_slots(c->G) / units - win);
         }
         S = std::max(1, std::min(S, std::min(c->n_pages, kMaxSplits)));
         pl.pages_per_split = (c->n_pages + S - 1) / S;

@@ -81,6 +81,8 @@ struct DecodePlan {
     int max_splits;       // workspace stride (splits per (b, hq))
 };
 size_t decode_workspace_bytes(const Geometry &G, int max_splits);
+// Workgroups of the decode kernel the device holds at once (2048 without a device).
+int decode_slots(const Geometry &G);
 hipError_t launch_decode(const Geometry &G, const uint8_t *cache, const uint16_t *q,
                          float *out, void *workspace, const DecodePlan &plan,
                          hipEvent_t ev_before, hipEvent_t ev_after, hipStream_t stream);
