@@ -116,6 +116,44 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 __device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src, 64); }
+
+// Cross-lane steps on the VALU (no LDS round trip).  permlane16/32_swap of a
+// value with itself returns, in every lane l, the values of lanes l and
+// l ^ 16 (resp. l ^ 32) of the pair.
+__device__ __forceinline__ float xmax16(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax32(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <int CTRL>
+__device__ __forceinline__ float dppc(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// max over the whole wave, in every lane
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dppc<0x128>(v));  // row_ror:8
+    v = fmaxf(v, dppc<0x124>(v));  // row_ror:4
+    v = fmaxf(v, dppc<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dppc<0xB1>(v));   // quad_perm [1,0,3,2]
+    return xmax32(xmax16(v));
+}
+// every lane gets the value of lane (l % 16) of the first row
+__device__ __forceinline__ float bcast_row0(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    auto b = __builtin_amdgcn_permlane32_swap(a[0], a[0], false, false);
+    return __uint_as_float(b[0]);
+}
+// lane (r, G4) gets the value of lane 4 G4 (a per-row broadcast from row 0)
+__device__ __forceinline__ float from_lane4g(float v, int G4) {
+    float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 4));
+    float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 8));
+    float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 12));
+    return G4 == 0 ? a0 : G4 == 1 ? a1 : G4 == 2 ? a2 : a3;
+}
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
 // Code extraction: word x holds 16 two-bit codes, code e of each 16-bit half
@@ -141,42 +179,57 @@ struct PageRegs {
     uint4 meta[5];      // metadata copy, 16-byte chunks lane + 64 i
 };
 
-__device__ __forceinline__ void load_meta(PageRegs &R, const uint8_t *pg, const PageLayout &Ly,
-                                          int lane, int meta_chunks, uint32_t meta_a_bytes) {
+// Page loads go through a buffer descriptor of the page itself: 32-bit lane
+// offsets (constant parts folded into the instruction), no 64-bit address
+// arithmetic, and any offset past the page reads zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *pg, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(pg), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ void load_meta(PageRegs &R, __amdgpu_buffer_rsrc_t rs,
+                                          const PageLayout &Ly, int lane, int meta_chunks,
+                                          uint32_t meta_a_bytes) {
     // metadata: [K_scale K_zero K_idx] then [V_scale V_zero]
 #pragma unroll
     for (int i = 0; i < 5; i++) {
         int ch = min(lane + 64 * i, meta_chunks - 1);
         uint32_t off = 16u * ch;
         off = off < meta_a_bytes ? Ly.ks + off : Ly.vs + (off - meta_a_bytes);
-        R.meta[i] = *reinterpret_cast<const uint4 *>(pg + off);
+        u4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+        R.meta[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
 }
 
 template <int KH>
-__device__ __forceinline__ void load_codes(PageRegs &R, const uint8_t *pg, const PageLayout &Ly,
-                                           int k, int lane) {
+__device__ __forceinline__ void load_codes(PageRegs &R, __amdgpu_buffer_rsrc_t rs,
+                                           const PageLayout &Ly, int k, int lane) {
     const int r = lane & 15, G4 = lane >> 4;
-#pragma unroll
-    for (int mt = 0; mt < 8; mt++)
-        R.klo[mt] = *reinterpret_cast<const uint2 *>(pg + Ly.klo + (16 * mt + r) * 32 + 8 * G4);
     // Every load is issued unconditionally (indices clamped into the page) so
     // the number of loads in flight is static and the compiler can wait for
     // the current page's data without draining the prefetch of the next.
+    const int klo_off = (int)Ly.klo + r * 32 + 8 * G4;
+#pragma unroll
+    for (int mt = 0; mt < 8; mt++) {
+        auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, klo_off + 512 * mt, 0, 0);
+        R.klo[mt] = make_uint2(v[0], v[1]);
+    }
 #pragma unroll
     for (int mt = 0; mt < 8; mt++) {
 #pragma unroll
         for (int ms = 0; ms < KH; ms++) {
             int dw = 2 * ms + (G4 >> 1);
             int dwc = dw < k / 16 ? dw : k / 16 - 1;
-            uint32_t v = *reinterpret_cast<const uint32_t *>(pg + Ly.khi + (16 * mt + r) * (k / 4) +
-                                                             4 * dwc);
+            uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(
+                rs, (int)Ly.khi + (16 * mt + r) * (k / 4) + 4 * dwc, 0, 0);
             R.khi[mt][ms] = dw < k / 16 ? v : 0u;
         }
     }
 #pragma unroll
-    for (int s = 0; s < 4; s++)
-        R.vc[s] = *reinterpret_cast<const uint4 *>(pg + Ly.vc + 1024 * s + 16 * lane);
+    for (int s = 0; s < 4; s++) {
+        u4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)Ly.vc + 16 * lane + 1024 * s, 0, 0);
+        R.vc[s] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
 }
 
 template <int DT, int G, int KH>
@@ -247,7 +300,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
             float mx = s[j];
 #pragma unroll
             for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
-            float p = tl < nt ? exp2f(s[j] - mx) : 0.0f;
+            float p = tl < nt ? __builtin_amdgcn_exp2f(s[j] - mx) : 0.0f;
             float l = p;
 #pragma unroll
             for (int o = 16; o > 0; o >>= 1) l += shfl_xor(l, o);
@@ -346,8 +399,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const int hjb = 16 * (hG >> 1) + 4 * (hG & 1);
     float qmax = 0.0f;
     for (int i = lane; i < G * D; i += 64) qmax = fmaxf(qmax, fabsf(qf[i / D][i % D]));
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) qmax = fmaxf(qmax, shfl_xor(qmax, o));
+    qmax = wave_max(qmax);
 
     float acc[HQ][8];  // lane (r, G4): head 4 qd + G4, channel 16 n + r (scaled by 2^Eu ...)
     float m_run[HQ], l_part[HQ], zt[HQ];
@@ -365,19 +417,23 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const int p1 = min(n_pages, p0 + pps);
     const uint8_t *ubase = cache + (size_t)unit * max_pages * page_bytes;
     PageRegs cur;
-    load_codes<KH>(cur, ubase + (size_t)p0 * page_bytes, Ly, k, lane);
-    load_meta(cur, ubase + (size_t)p0 * page_bytes, Ly, lane, meta_chunks, meta_a);
+    {
+        const __amdgpu_buffer_rsrc_t rs0 = page_rsrc(ubase + (size_t)p0 * page_bytes, page_bytes);
+        load_codes<KH>(cur, rs0, Ly, k, lane);
+        load_meta(cur, rs0, Ly, lane, meta_chunks, meta_a);
+    }
 
     for (int p = p0; p < p1; p++) {
         // prefetch of the next page (the last page is loaded again at the end:
         // harmless): codes now, metadata once this page's copy is in LDS
-        const uint8_t *pnext = ubase + (size_t)min(p + 1, p1 - 1) * page_bytes;
+        const __amdgpu_buffer_rsrc_t rsn =
+            page_rsrc(ubase + (size_t)min(p + 1, p1 - 1) * page_bytes, page_bytes);
         PageRegs nxt;
-        load_codes<KH>(nxt, pnext, Ly, k, lane);
+        load_codes<KH>(nxt, rsn, Ly, k, lane);
         wave_sync();  // previous page's LDS reads are done
 #pragma unroll
         for (int i = 0; i < 5; i++) reinterpret_cast<uint4 *>(meta)[lane + 64 * i] = cur.meta[i];
-        load_meta(nxt, pnext, Ly, lane, meta_chunks, meta_a);
+        load_meta(nxt, rsn, Ly, lane, meta_chunks, meta_a);
 
         // Page exponent of the weights: |4 w 2^E / 4^sig| <= qmax max(s) 2^(E-2) <= 2^14.
         float smax = 0.0f;
@@ -387,8 +443,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 #pragma unroll
             for (int e = 0; e < 8; e++)
                 smax = fmaxf(smax, fabsf(dec<DT>((uint16_t)(wv[e >> 1] >> (16 * (e & 1))))));
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) smax = fmaxf(smax, shfl_xor(smax, o));
+            smax = wave_max(smax);
         }
         int eb;
         frexpf(qmax * smax, &eb);
@@ -412,8 +467,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
                 vzr[e] = dec<DT>((uint16_t)(zw4[e >> 1] >> (16 * (e & 1))));
                 vmax = fmaxf(vmax, fabsf(vsr[e]));
             }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) vmax = fmaxf(vmax, shfl_xor(vmax, o));
+            vmax = wave_max(vmax);
             int ev;
             frexpf(vmax, &ev);
             const int Eu_new = __builtin_amdgcn_readfirstlane(min(Eu, min(100, max(-60, 14 - ev))));
@@ -452,7 +506,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
                     float v = cb[g];
                     v += dpp_quad_swap1(v);
                     v += dpp_quad_swap2(v);
-                    bias[qd][g] = shfl(v, r);  // rows 0..3 live in lanes 0..15
+                    bias[qd][g] = bcast_row0(v);  // rows 0..3 live in lanes 0..15
                 }
             }
         }
@@ -561,16 +615,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
                 // --- online softmax over these 32 tokens, per head ---
                 float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                                  fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-                mx = fmaxf(mx, shfl_xor(mx, 16));
-                mx = fmaxf(mx, shfl_xor(mx, 32));
+                mx = xmax32(xmax16(mx));
                 if (__any(mx > m_run[qd])) {  // wave-uniform: rescale only when a max grows
                     float mnew = fmaxf(m_run[qd], mx);
-                    float alpha = exp2f(m_run[qd] - mnew);
+                    float alpha = __builtin_amdgcn_exp2f(m_run[qd] - mnew);
                     m_run[qd] = mnew;
                     l_part[qd] *= alpha;
                     zt[qd] *= alpha;
                     // accumulator lanes hold head G4 of the quad: that head's alpha
-                    float al = shfl(alpha, 4 * G4);
+                    float al = from_lane4g(alpha, G4);
 #pragma unroll
                     for (int n = 0; n < 8; n++) acc[qd][n] *= al;
                 }
@@ -579,7 +632,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
                 for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        pr[mt][e] = exp2f(sc[mt][e] - m_run[qd]);
+                        pr[mt][e] = __builtin_amdgcn_exp2f(sc[mt][e] - m_run[qd]);
                         l_part[qd] += pr[mt][e];
                     }
 
@@ -657,7 +710,7 @@ __global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ ws
     for (int s = 0; s < total_splits; s++) M = fmaxf(M, ws_ml[(bq * max_splits + s) * 2]);
     float num = 0.0f, den = 0.0f;
     for (int s = 0; s < total_splits; s++) {
-        float w = exp2f(ws_ml[(bq * max_splits + s) * 2] - M);
+        float w = __builtin_amdgcn_exp2f(ws_ml[(bq * max_splits + s) * 2] - M);
         num = fmaf(w, ws_acc[(bq * max_splits + s) * D + c], num);
         den = fmaf(w, ws_ml[(bq * max_splits + s) * 2 + 1], den);
     }
