@@ -1,36 +1,41 @@
 // kvq_decode.hip -- split-K GQA decode attention over the packed cache (gfx950).
 //
 // Grid (split, KV head, sequence); one 64-lane wave per workgroup.  A page
-// split streams its pages with 128-bit loads (the next page is in flight
-// while the current one is computed) and contracts them on the matrix cores:
+// split streams its pages one 32-token Key group at a time (two 16-token
+// tiles): while a group is computed, the next group's codes and metadata
+// (about 3.2 KB) are already in flight in a second register set, so a wave
+// needs few registers and four waves share each SIMD.
 //
-//  QK  (16 tokens x 32 channels) x (32 channels x 16 columns) per MFMA.  The
-//      A operand is the 2-bit Key code itself: masking a packed word (or the
+//  QK  (16 rows of weights) x (32 channels x 16 tokens) per MFMA.  The B
+//      operand is the 2-bit Key code itself: masking a packed word (or the
 //      word shifted by 4 or -6) leaves two codes at mantissa bits 4..9 of two
 //      fp16 halves, i.e. the exact subnormals code * 4^sig * 2^-24 with sig in
 //      {2, 3, 4}, so unpacking costs about one instruction per two codes.  (The
 //      matrix cores keep full precision for such operands only when the code
 //      sits at bit 4 or above: at bits 0..3 low-order product bits are lost.)
-//      The B operand holds the per-group weights w = q * scale * log2(e) * s
-//      (Key scale of the channel and 32-token group) * 2^E / 4^sig, split
-//      into an fp16 hi and lo part in neighbouring columns so that the
-//      products keep ~22 bits.  Boosted channels (Kitty
-//      abstract: two uniform 2-bit planes per mixed-precision Key page) add a
-//      second contraction of the hi plane against 4 w of the listed channels.
-//      The zero-point term q . z per group comes from one small MFMA of the
-//      page's Key zeros against q split into three pieces.
+//      The A operand holds the group's weights w = q * scale * log2(e) * s
+//      (Key scale of the channel and group) * 2^E / 4^sig, split into an fp16
+//      hi and lo row so that the products keep ~22 bits.  Rows are laid out so
+//      that output lane (token, row block) holds hi and lo of its own head:
+//      every lane owns distinct (head, token) scores and the softmax does no
+//      duplicate work.  Boosted channels (Kitty abstract: two uniform 2-bit
+//      planes per mixed-precision Key page) add a contraction of the hi plane
+//      against 4 w of the listed channels.  The zero-point term q . z per
+//      group and head comes from a small MFMA of q (split into three pieces of
+//      the cache dtype) against the group's Key zeros.
 //  PV  (16 rows = 4 heads x 4 Value groups) x (32 tokens x 16 channels): the
 //      A operand is p * s_v (softmax weight times the token's Value scale for
-//      the group), again split hi/lo; the B operand is the Value code read the
-//      same way as the Key codes.  Only the row whose group matches the
-//      channel is kept; the zero-point term p . z_v accumulates on the VALU.
+//      the group), split hi/lo; p reaches that layout through a 512-byte LDS
+//      transpose.  The B operand is the Value code read the same way as the
+//      Key codes.  Only the row whose group matches the channel is kept; the
+//      zero-point term p . z_v accumulates on the VALU.
 //
-// Columns of QK are laid out as 4 per query head (hi, lo, hi, lo), so after
-// adding neighbours every lane of a head's quad holds that head's scores for
-// exactly the tokens its PV operand needs: no transposes or shuffles between
-// the two contractions.  An online softmax in the log2 domain keeps (m, l)
-// per head (MiniKV summary: unpack fused into the decode matmul; one read of
-// a page serves the whole query group, notes.yuuk.io open questions on GQA).
+// The softmax runs in the log2 domain with a per-head running maximum; the
+// weights carry an extra factor 2^Eu (Eu from the largest Value scale seen)
+// so that p * s_v always splits into normal fp16 parts.  Partials store
+// (m - Eu, l, acc), which the combine step treats like any other maximum.
+// (MiniKV summary: unpack fused into the decode matmul; one read of a page
+// serves the whole query group, notes.yuuk.io open questions on GQA.)
 //
 // The window split reads the newest n_res exact tokens (KIVI explainer,
 // section 3: full-precision residual) on the VALU, 32 tokens per workgroup.
@@ -101,12 +106,6 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
     lo = pack_rne(a - lo_half(hi), b - hi_half(hi));
 }
 
-__device__ __forceinline__ float dpp_quad_swap1(float v) {  // lane ^ 1 within a quad
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float dpp_quad_swap2(float v) {  // lane ^ 2 within a quad
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
-}
 // The workgroup is a single wave and LDS operations of a wave complete in
 // order, so ordering LDS writes before other lanes' reads needs only a
 // wave-scope fence; a workgroup barrier would also wait for the next page's
@@ -140,20 +139,6 @@ __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dppc<0xB1>(v));   // quad_perm [1,0,3,2]
     return xmax32(xmax16(v));
 }
-// every lane gets the value of lane (l % 16) of the first row
-__device__ __forceinline__ float bcast_row0(float v) {
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    auto b = __builtin_amdgcn_permlane32_swap(a[0], a[0], false, false);
-    return __uint_as_float(b[0]);
-}
-// lane (r, G4) gets the value of lane 4 G4 (a per-row broadcast from row 0)
-__device__ __forceinline__ float from_lane4g(float v, int G4) {
-    float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 4));
-    float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 8));
-    float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 12));
-    return G4 == 0 ? a0 : G4 == 1 ? a1 : G4 == 2 ? a2 : a3;
-}
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
 // Code extraction: word x holds 16 two-bit codes, code e of each 16-bit half
@@ -172,11 +157,53 @@ struct Codes8 {
     }
 };
 
-struct PageRegs {
-    uint2 klo[8];       // K lo plane: token 16 mt + (lane & 15), channels 32 (lane >> 4) + [0, 32)
-    uint32_t khi[8][4]; // K hi plane dwords 2 ms + ((lane >> 4) >> 1) of the same tokens
-    uint4 vc[4];        // V codes: 16-byte block (step, lane)
-    uint4 meta[5];      // metadata copy, 16-byte chunks lane + 64 i
+typedef unsigned short us2_t __attribute__((ext_vector_type(2)));
+
+// max / sum over the 16 lanes of a row, in every lane of the row
+__device__ __forceinline__ float row_max(float v) {
+    v = fmaxf(v, dppc<0x128>(v));  // row_ror:8
+    v = fmaxf(v, dppc<0x124>(v));  // row_ror:4
+    v = fmaxf(v, dppc<0x4E>(v));   // quad_perm [2,3,0,1]
+    return fmaxf(v, dppc<0xB1>(v));  // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ float row_sum(float v) {
+    v += dppc<0x128>(v);
+    v += dppc<0x124>(v);
+    v += dppc<0x4E>(v);
+    return v + dppc<0xB1>(v);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+    v = max(v, dppu<0x128>(v));
+    v = max(v, dppu<0x124>(v));
+    v = max(v, dppu<0x4E>(v));
+    return max(v, dppu<0xB1>(v));
+}
+// lane (r, R) gets the value held by row (r / 4) (every lane of a row holds the same)
+__device__ __forceinline__ float from_row(float v, int row) {
+    float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return row == 0 ? a0 : row == 1 ? a1 : row == 2 ? a2 : a3;
+}
+
+// Query head served by slot s of lane row R (rows repeat heads when G < 4).
+template <int G>
+__device__ __forceinline__ int head_of(int R, int s) {
+    return G >= 4 ? 4 * s + R : R % G;
+}
+
+// Registers of one 32-token Key group (two 16-token tiles) of a page.
+template <int KHE>
+struct GroupRegs {
+    uint2 klo[2];          // K lo plane, tile mt: token 16 mt + (lane & 15), channels 32 (lane >> 4) + [0, 32)
+    uint32_t khi[2][KHE];  // K hi plane dwords 2 ms + (lane >> 5) of the same tokens
+    u4_t vc;               // V codes: this lane's 16-byte block of the group
+    u4_t meta;             // one 16-byte chunk of the group's metadata
 };
 
 // Page loads go through a buffer descriptor of the page itself: 32-bit lane
@@ -187,87 +214,90 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *pg, u
                                              0x00020000);
 }
 
-__device__ __forceinline__ void load_meta(PageRegs &R, __amdgpu_buffer_rsrc_t rs,
-                                          const PageLayout &Ly, int lane, int meta_chunks,
-                                          uint32_t meta_a_bytes) {
-    // metadata: [K_scale K_zero K_idx] then [V_scale V_zero]
+// Byte offsets of this lane's loads inside a page (fixed for the whole split).
+template <int KHE>
+struct LaneOffs {
+    int klo, vc, meta, mstride, khi_tile;
+    int khi[KHE];
+    int idx[KHE][2];
+};
+
+// Every load is issued unconditionally (offsets clamped into the page) so the
+// number of loads in flight is static and the compiler can wait for one
+// group's data without draining the loads of the next.
+template <int KH, int KHE>
+__device__ __forceinline__ void load_group(GroupRegs<KHE> &Gr, __amdgpu_buffer_rsrc_t rs,
+                                           const LaneOffs<KHE> &O, int g) {
 #pragma unroll
-    for (int i = 0; i < 5; i++) {
-        int ch = min(lane + 64 * i, meta_chunks - 1);
-        uint32_t off = 16u * ch;
-        off = off < meta_a_bytes ? Ly.ks + off : Ly.vs + (off - meta_a_bytes);
-        u4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
-        R.meta[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    for (int mt = 0; mt < 2; mt++) {
+        auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, O.klo + 512 * (2 * g + mt), 0, 0);
+        Gr.klo[mt] = make_uint2(v[0], v[1]);
     }
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+        for (int ms = 0; ms < KH; ms++)
+            Gr.khi[mt][ms] = __builtin_amdgcn_raw_buffer_load_b32(
+                rs, O.khi[ms] + (2 * g + mt) * O.khi_tile, 0, 0);
+    Gr.vc = __builtin_amdgcn_raw_buffer_load_b128(rs, O.vc + 1024 * g, 0, 0);
+    Gr.meta = __builtin_amdgcn_raw_buffer_load_b128(rs, O.meta + g * O.mstride, 0, 0);
+}
+template <int KH, int KHE>
+__device__ __forceinline__ void load_idx(uint32_t (&ib)[KHE][2], __amdgpu_buffer_rsrc_t rs,
+                                         const LaneOffs<KHE> &O) {
+#pragma unroll
+    for (int ms = 0; ms < KH; ms++)
+#pragma unroll
+        for (int t = 0; t < 2; t++) ib[ms][t] = __builtin_amdgcn_raw_buffer_load_b8(rs, O.idx[ms][t], 0, 0);
 }
 
-template <int KH>
-__device__ __forceinline__ void load_codes(PageRegs &R, __amdgpu_buffer_rsrc_t rs,
-                                           const PageLayout &Ly, int k, int lane) {
-    const int r = lane & 15, G4 = lane >> 4;
-    // Every load is issued unconditionally (indices clamped into the page) so
-    // the number of loads in flight is static and the compiler can wait for
-    // the current page's data without draining the prefetch of the next.
-    const int klo_off = (int)Ly.klo + r * 32 + 8 * G4;
-#pragma unroll
-    for (int mt = 0; mt < 8; mt++) {
-        auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, klo_off + 512 * mt, 0, 0);
-        R.klo[mt] = make_uint2(v[0], v[1]);
-    }
-#pragma unroll
-    for (int mt = 0; mt < 8; mt++) {
-#pragma unroll
-        for (int ms = 0; ms < KH; ms++) {
-            int dw = 2 * ms + (G4 >> 1);
-            int dwc = dw < k / 16 ? dw : k / 16 - 1;
-            uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(
-                rs, (int)Ly.khi + (16 * mt + r) * (k / 4) + 4 * dwc, 0, 0);
-            R.khi[mt][ms] = dw < k / 16 ? v : 0u;
-        }
-    }
-#pragma unroll
-    for (int s = 0; s < 4; s++) {
-        u4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)Ly.vc + 16 * lane + 1024 * s, 0, 0);
-        R.vc[s] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
+// Waves per SIMD the register allocation aims at (more registers per wave
+// beyond that would spill).
+constexpr int waves_target(int G, int KH) {
+    return G <= 4 ? (KH == 0 || (KH == 1 && G > 1) ? 4 : KH <= 3 ? 3 : 2) : G == 8 ? (KH <= 3 ? 2 : 1) : 1;
 }
 
 template <int DT, int G, int KH>
-__global__ __launch_bounds__(64) void decode_split_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target(G, KH)))) void decode_split_kernel(
     const uint8_t *__restrict__ cache, const uint16_t *__restrict__ q, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, int Hkv, int max_pages, uint32_t page_bytes, int k,
     size_t res_base, int n_pages, int n_res, int page_splits, int pps, int max_splits,
     float qscale) {
-    constexpr int HQ = (G + 3) / 4;       // quads of query heads
-    constexpr int NHW = (G + 1) / 2;      // heads per lane in the window path
-    __shared__ float qf[G][D];            // q * scale * log2(e)
-    __shared__ __align__(16) uint8_t meta[5 * 64 * 16];  // page metadata copy (16-byte chunks)
-    __shared__ __align__(16) u4_t wB[HQ][2][64];                     // lo-plane weights [hi/lo][lane]
-    __shared__ __align__(16) u4_t wBh[HQ][4][KH > 0 ? KH : 1][2][16];  // hi-plane weights [group]
-    __shared__ __align__(16) float vsf[D / GV][144];                   // V scale x 2^Eu, padded rows
-    __shared__ __align__(16) u4_t tq3[HQ][4][64];   // q pieces: B operand of the zero-point MFMA
-    __shared__ __align__(16) float tqs[HQ][64][8];  // q / 4^sig of each producer lane's slots
-    __shared__ __align__(16) float vzf[D / GV][144];                   // V zero, padded rows
-    __shared__ float sw[G][32];
+    constexpr int HQ = (G + 3) / 4;    // head slots per row of lanes
+    constexpr int NQS = (HQ + 1) / 2;  // QK row sets (two slots each)
+    constexpr int KHE = KH > 0 ? KH : 1;
+    constexpr int NHW = (G + 1) / 2;   // heads per lane in the window path
+    // LDS of the page path
+    constexpr int O_Q = 0;                                // u16 [G][D] raw q
+    constexpr int O_WL = O_Q + G * D * 2;                 // u4 [HQ][4 m][2 x][4 R][4 kb] lo-plane weights
+    constexpr int O_WH = O_WL + HQ * 4 * 32 * 16;         // u32 [HQ][KHE][2 x][4 R][4 kb][4] hi plane
+    constexpr int O_BQ = O_WH + HQ * KHE * 2 * 16 * 16;   // u4 [HQ][4 m][64 lanes] q pieces
+    constexpr int O_ST = O_BQ + HQ * 4 * 64 * 16;         // f32 [384] K scale 2^E | V scale | V zero
+    constexpr int O_KZ = O_ST + 384 * 4;                  // u16 [D] K zero of the group
+    constexpr int O_PX = O_KZ + D * 2;                    // f32 [HQ][4][32] softmax weights
+    constexpr int PAGE_LDS = O_PX + HQ * 4 * 32 * 4;
+    constexpr int WIN_LDS = G * D * 4 + G * 32 * 4;
+    __shared__ __align__(16) uint8_t lds[PAGE_LDS > WIN_LDS ? PAGE_LDS : WIN_LDS];
 
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int unit = b * Hkv + h;
     const int Hq = Hkv * G;
-    const int lane = threadIdx.x, r = lane & 15, G4 = lane >> 4;
-
-    // q of the G query heads: one 16-byte load per lane per 64 chunks of 8 channels
-    for (int ch = lane; ch < G * (D / 8); ch += 64) {
-        int hh = ch / (D / 8), c0 = 8 * (ch % (D / 8));
-        uint4 v = *reinterpret_cast<const uint4 *>(q + ((size_t)b * Hq + h * G + hh) * D + c0);
-        uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-            qf[hh][c0 + e] = dec<DT>((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * qscale;
-    }
-    wave_sync();
+    const int lane = threadIdx.x, r = lane & 15, kb = lane >> 4;
+    const uint16_t *qg = q + ((size_t)b * Hq + h * G) * D;
 
     if (split >= page_splits) {
         // ---------------- window split: 32 exact tokens on the VALU ----------------
+        float(*qf)[D] = reinterpret_cast<float(*)[D]>(lds);
+        float(*sw)[32] = reinterpret_cast<float(*)[32]>(lds + G * D * 4);
+        for (int ch = lane; ch < G * (D / 8); ch += 64) {
+            uint4 v = *reinterpret_cast<const uint4 *>(qg + 8 * ch);
+            uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                qf[ch / (D / 8)][8 * (ch % (D / 8)) + e] =
+                    dec<DT>((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * qscale;
+        }
+        wave_sync();
         const int w = split - page_splits;
         const int t0 = 32 * w;
         const int nt = min(32, n_res - t0);
@@ -343,358 +373,359 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 
     // ---------------------------- page split ----------------------------
     const PageLayout Ly = page_layout(k);
-    const uint32_t meta_a = (P / GK) * D * 4 + (uint32_t)((k + 15) / 16 * 16);  // K scale, zero, idx
-    const int meta_chunks = (int)(meta_a + (D / GV) * P * 4) / 16;
-    const uint16_t *mks = reinterpret_cast<const uint16_t *>(meta);            // [4][128]
-    const uint16_t *mkz = mks + (P / GK) * D;                                  // [4][128]
-    const uint8_t *midx = meta + (P / GK) * D * 4;                             // [k]
-    const uint16_t *mvs = reinterpret_cast<const uint16_t *>(meta + meta_a);   // [4][128]
-    const uint16_t *mvz = mvs + (D / GV) * P;                                  // [4][128]
+    uint16_t *qr = reinterpret_cast<uint16_t *>(lds + O_Q);
+    float *st = reinterpret_cast<float *>(lds + O_ST);
+    uint16_t *kz = reinterpret_cast<uint16_t *>(lds + O_KZ);
+    float *px = reinterpret_cast<float *>(lds + O_PX);
 
-    // Fixed per call: q pieces as the B operand of the zero-point MFMA
-    // (column 4 h' + piece, pieces 0..2; k slot 8 G4 + e <-> channel 32 m + 8 G4 + e).
+    for (int ch = lane; ch < G * (D / 8); ch += 64)
+        *reinterpret_cast<uint4 *>(qr + 8 * ch) = *reinterpret_cast<const uint4 *>(qg + 8 * ch);
+    wave_sync();
+    auto qv = [&](int hh, int c) { return dec<DT>(qr[hh * D + c]) * qscale; };
+
+    // max |q'| < 2^eq bounds the weights together with the group's largest Key scale
+    float qmax = 0.0f;
+    for (int i = lane; i < G * D; i += 64) qmax = fmaxf(qmax, fabsf(dec<DT>(qr[i])));
+    qmax = wave_max(qmax) * fabsf(qscale);
+    int eq;
+    frexpf(qmax, &eq);
+    eq = __builtin_amdgcn_readfirstlane(qmax > 0.0f ? max(eq, -100) : -100);
+
+    // Lo-plane weight producer role: K step pm, k block pkb, row block pR; its
+    // eight channels are pcb + i + 8 e (i < 4, e < 2), i.e. operand element
+    // 2 i + e of MFMA pm for lanes (row 4 pR + *, pkb).
+    const int pm = lane >> 4, pkb = (lane >> 2) & 3, pR = lane & 3;
+    const int pcb = 32 * pkb + 16 * (pm >> 1) + 4 * (pm & 1);
+    float qpp[HQ][8];  // q'(head, channel) / 4^sig of those slots
 #pragma unroll
-    for (int qd = 0; qd < HQ; qd++) {
-        int hh = 4 * qd + (r >> 2), pc = r & 3;
+    for (int s = 0; s < HQ; s++)
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-            uint32_t dw[4];
+        for (int e = 0; e < 8; e++) {
+            const int hh = head_of<G>(pR, s);
+            const float sig = (pm & 1) ? 1.0f / (float)(1 << (2 * code_sig(4 + (e >> 1))))
+                                       : 1.0f / (float)(1 << (2 * code_sig(e >> 1)));
+            qpp[s][e] = qv(hh, pcb + (e >> 1) + 8 * (e & 1)) * sig;
+        }
+    // q split into three pieces of the cache dtype: A operand of the zero-point
+    // MFMA, row 4 R + piece (piece 3 zero), channel 32 m + 8 kb + e.
 #pragma unroll
-            for (int e2 = 0; e2 < 4; e2++) {
-                uint16_t pv[2];
+    for (int s = 0; s < HQ; s++) {
+        const int hh = head_of<G>(pR, s);
+        uint32_t pw[3][4];
 #pragma unroll
-                for (int u = 0; u < 2; u++) {
-                    float x = hh < G ? qf[hh][32 * m + 8 * G4 + 2 * e2 + u] : 0.0f;
-                    uint16_t p0 = enc<DT>(x);
-                    float r1 = x - dec<DT>(p0);
-                    uint16_t p1 = enc<DT>(r1);
-                    float r2 = r1 - dec<DT>(p1);
-                    uint16_t p2 = enc<DT>(r2);
-                    pv[u] = pc == 0 ? p0 : pc == 1 ? p1 : pc == 2 ? p2 : (uint16_t)0;
-                }
-                dw[e2] = (uint32_t)pv[0] | ((uint32_t)pv[1] << 16);
+        for (int e2 = 0; e2 < 4; e2++) {
+            uint16_t pv[3][2];
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                const float x = qv(hh, 32 * pm + 8 * pkb + 2 * e2 + u);
+                const uint16_t p0 = enc<DT>(x);
+                const float r1 = x - dec<DT>(p0);
+                const uint16_t p1 = enc<DT>(r1);
+                const float r2 = r1 - dec<DT>(p1);
+                pv[0][u] = p0;
+                pv[1][u] = p1;
+                pv[2][u] = enc<DT>(r2);
             }
-            tq3[qd][m][lane] = u4_t{dw[0], dw[1], dw[2], dw[3]};
+#pragma unroll
+            for (int pc = 0; pc < 3; pc++) pw[pc][e2] = (uint32_t)pv[pc][0] | ((uint32_t)pv[pc][1] << 16);
+        }
+        u4_t *bq = reinterpret_cast<u4_t *>(lds + O_BQ) + (s * 4 + pm) * 64 + 16 * pkb + 4 * pR;
+#pragma unroll
+        for (int pc = 0; pc < 3; pc++) bq[pc] = u4_t{pw[pc][0], pw[pc][1], pw[pc][2], pw[pc][3]};
+        bq[3] = u4_t{0, 0, 0, 0};
+    }
+
+    // Hi-plane producer role: k block hkb, row block hR, operand dword hq; its
+    // boosted slots are j0 = 32 ms + 16 (hkb / 2) + 4 (hkb % 2) + hq and j0 + 8,
+    // at mantissa bits 2 sig_hi with sig_hi = 2 + (hq & 1).
+    const int hkb = lane >> 4, hR = (lane >> 2) & 3, hq = lane & 3;
+    const float fh = (hq & 1) ? 4.0f / 64.0f : 4.0f / 16.0f;
+
+    LaneOffs<KHE> O;
+    O.klo = (int)Ly.klo + r * 32 + 8 * kb;
+    O.vc = (int)Ly.vc + 16 * lane;
+    O.meta = lane < 32 ? (int)Ly.ks + 1024 * (lane >> 4) + 16 * (lane & 15)
+                       : (int)Ly.vs + 1024 * ((lane - 32) >> 4) + 256 * ((lane >> 2) & 3) +
+                             16 * (lane & 3);
+    O.mstride = lane < 32 ? 256 : 64;
+    O.khi_tile = 4 * k;
+#pragma unroll
+    for (int ms = 0; ms < KHE; ms++) {
+        const int dw = min(2 * ms + (kb >> 1), max(k / 16 - 1, 0));
+        O.khi[ms] = (int)Ly.khi + r * (k / 4) + 4 * dw;
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const int j = 32 * ms + 16 * (hkb >> 1) + 4 * (hkb & 1) + hq + 8 * t;
+            O.idx[ms][t] = (int)Ly.kidx + min(j, max(k - 1, 0));
         }
     }
-    // Weight producer role of this lane (lo plane): K step pm = lane / 16, lane
-    // group pG = (lane / 4) % 4 and head ph = lane % 4 of each quad; its eight
-    // channels are pbase + i + 8 e (i < 4, e < 2), k slots 8 pG + 2 i + e of
-    // MFMA pm.  The 16 bytes it writes per (quad, hi/lo) are exactly what
-    // reader lane (col 4 ph + hi/lo, pG) loads for MFMA pm.
-    const int pm = lane >> 4, pG = (lane >> 2) & 3, ph = lane & 3;
-    const int pbase = 32 * pG + 16 * (pm >> 1) + 4 * (pm & 1);
-#pragma unroll
-    for (int qd = 0; qd < HQ; qd++)  // q'(head, channel) / 4^sig of this lane's slots
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int e = 0; e < 2; e++) {
-                int hh = 4 * qd + ph;
-                float sig = 1.0f / (float)(1 << (2 * code_sig(4 * (pm & 1) + i)));
-                tqs[qd][lane][2 * i + e] = hh < G ? qf[hh][pbase + i + 8 * e] * sig : 0.0f;
-            }
-    // hi-plane producer role: lane group hG and head ph (group = lane / 16)
-    const int hG = (lane >> 2) & 3;
-    const int hjb = 16 * (hG >> 1) + 4 * (hG & 1);
-    float qmax = 0.0f;
-    for (int i = lane; i < G * D; i += 64) qmax = fmaxf(qmax, fabsf(qf[i / D][i % D]));
-    qmax = wave_max(qmax);
+    // staging destinations of this lane's metadata chunk
+    const int st_o = lane < 16 ? 8 * lane : 128 + 8 * (lane - 32);
+    const bool st_f32 = lane < 16 || lane >= 32;
 
-    float acc[HQ][8];  // lane (r, G4): head 4 qd + G4, channel 16 n + r (scaled by 2^Eu ...)
+    float acc[HQ][8];  // lane (r, R): head head_of(R, s), channel 16 n + r
     float m_run[HQ], l_part[HQ], zt[HQ];
 #pragma unroll
-    for (int qd = 0; qd < HQ; qd++) {
-        m_run[qd] = -INFINITY;
-        l_part[qd] = 0.0f;
-        zt[qd] = 0.0f;
+    for (int s = 0; s < HQ; s++) {
+        m_run[s] = -INFINITY;
+        l_part[s] = 0.0f;
+        zt[s] = 0.0f;
 #pragma unroll
-        for (int n = 0; n < 8; n++) acc[qd][n] = 0.0f;
+        for (int n = 0; n < 8; n++) acc[s][n] = 0.0f;
     }
-    int Eu = 1000;
+    int Eu = 30;
+    int hc[KHE][2];
+    float qh[HQ][KHE][2];
+
+    auto process = [&](const GroupRegs<KHE> &Gr) __attribute__((always_inline)) {
+        // ---- metadata: exponents from the largest scales (integer max of the
+        // bits: scales are never negative), then fp32 copies into LDS ----
+        const u4_t M = Gr.meta;
+        {
+            us2_t a = __builtin_elementwise_max(__builtin_bit_cast(us2_t, M[0]),
+                                                __builtin_bit_cast(us2_t, M[1]));
+            us2_t c = __builtin_elementwise_max(__builtin_bit_cast(us2_t, M[2]),
+                                                __builtin_bit_cast(us2_t, M[3]));
+            a = __builtin_elementwise_max(a, c);
+            uint32_t mm = row_max_u32(max((uint32_t)a[0], (uint32_t)a[1]));
+            const uint32_t sb = (uint32_t)__builtin_amdgcn_readlane((int)mm, 0);   // K scales
+            const uint32_t vb = (uint32_t)__builtin_amdgcn_readlane((int)mm, 32);  // V scales
+            const int es = DT == BF16 ? (int)(sb >> 7) - 126 : (int)(sb >> 10) - 14;
+            const int ev = DT == BF16 ? (int)(vb >> 7) - 126 : (int)(vb >> 10) - 14;
+            // |w 2^E / 4^sig| < 2^(eq + es + E - 4) <= 2^12 (x4 on the hi plane)
+            const int E = min(100, max(-100, 16 - eq - es));
+            const int Eg = min(30, max(-100, 14 - ev));  // p' s_v < 2^14 with p' <= 2^Eu
+            const float wscale = __uint_as_float((uint32_t)(E + 127) << 23);
+            if (Eg < Eu) {  // wave-uniform: the weights' headroom shrinks
+                const float f = __uint_as_float((uint32_t)(max(Eg - Eu, -126) + 127) << 23);
+#pragma unroll
+                for (int s = 0; s < HQ; s++) {
+                    l_part[s] *= f;
+                    zt[s] *= f;
+#pragma unroll
+                    for (int n = 0; n < 8; n++) acc[s][n] *= f;
+                }
+                Eu = Eg;
+            }
+            const float fac = lane < 16 ? wscale : 1.0f;
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) f[e] = dec<DT>((uint16_t)(M[e >> 1] >> (16 * (e & 1)))) * fac;
+            wave_sync();  // the previous group's reads of these tables are done
+            if (st_f32) {
+                *reinterpret_cast<float4 *>(st + st_o) = make_float4(f[0], f[1], f[2], f[3]);
+                *reinterpret_cast<float4 *>(st + st_o + 4) = make_float4(f[4], f[5], f[6], f[7]);
+            } else {
+                *reinterpret_cast<u4_t *>(kz + 8 * (lane - 16)) = M;
+            }
+            wave_sync();
+            // sback = 2^(24 - E) undoes 2^E and the 2^-24 of the code operand
+            const float sback = __uint_as_float((uint32_t)(151 - E) << 23);
+
+            // ---- lo-plane weights of this group ----
+            {
+                const float4 sa = *reinterpret_cast<const float4 *>(st + pcb);
+                const float4 sc = *reinterpret_cast<const float4 *>(st + pcb + 8);
+                const float s0[4] = {sa.x, sa.y, sa.z, sa.w}, s1[4] = {sc.x, sc.y, sc.z, sc.w};
+#pragma unroll
+                for (int s = 0; s < HQ; s++) {
+                    uint32_t hi[4], lo[4];
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        split2(qpp[s][2 * i] * s0[i], qpp[s][2 * i + 1] * s1[i], hi[i], lo[i]);
+                    u4_t *wl = reinterpret_cast<u4_t *>(lds + O_WL) + (s * 4 + pm) * 32 + 4 * pR + pkb;
+                    wl[0] = u4_t{hi[0], hi[1], hi[2], hi[3]};
+                    wl[16] = u4_t{lo[0], lo[1], lo[2], lo[3]};
+                }
+            }
+            // ---- hi-plane weights of this group ----
+#pragma unroll
+            for (int ms = 0; ms < KH; ms++) {
+                const float s0 = st[hc[ms][0]], s1 = st[hc[ms][1]];
+#pragma unroll
+                for (int s = 0; s < HQ; s++) {
+                    uint32_t hi, lo;
+                    split2(qh[s][ms][0] * s0, qh[s][ms][1] * s1, hi, lo);
+                    uint32_t *wh = reinterpret_cast<uint32_t *>(lds + O_WH) +
+                                   (((s * KHE + ms) * 2) * 16 + 4 * hR + hkb) * 4 + hq;
+                    wh[0] = hi;
+                    wh[64] = lo;
+                }
+            }
+            // ---- zero-point term per head: q pieces x K zero on the matrix cores ----
+            float bias[HQ];
+#pragma unroll
+            for (int s = 0; s < HQ; s++) {
+                f4_t cb = {0, 0, 0, 0};
+#pragma unroll
+                for (int m = 0; m < 4; m++) {
+                    const u4_t a = reinterpret_cast<const u4_t *>(lds + O_BQ)[(s * 4 + m) * 64 + lane];
+                    const u4_t z = *reinterpret_cast<const u4_t *>(kz + 32 * m + 8 * kb);
+                    cb = mfma_dt<DT>(a, z, cb);
+                }
+                bias[s] = cb[0] + cb[1] + cb[2];
+            }
+            wave_sync();
+
+            // ---- QK on the matrix cores: rows (slot pair, row block, hi/lo) ----
+            const Codes8 a0(Gr.klo[0].x), a1(Gr.klo[0].y), b0(Gr.klo[1].x), b1(Gr.klo[1].y);
+#pragma unroll
+            for (int qs = 0; qs < NQS; qs++) {
+                const int slot = min(2 * qs + ((r >> 1) & 1), HQ - 1);
+                const u4_t *wl = reinterpret_cast<const u4_t *>(lds + O_WL) + slot * 128 +
+                                 16 * (r & 1) + 4 * (r >> 2) + kb;
+                f4_t c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0};
+#pragma unroll
+                for (int m = 0; m < 4; m++) {
+                    const u4_t w = wl[32 * m];
+                    const Codes8 &x0 = m < 2 ? a0 : a1;
+                    const Codes8 &x1 = m < 2 ? b0 : b1;
+                    const int jb = 4 * (m & 1);
+                    c0 = mfma_f16(w, u4_t{x0[jb], x0[jb + 1], x0[jb + 2], x0[jb + 3]}, c0);
+                    c1 = mfma_f16(w, u4_t{x1[jb], x1[jb + 1], x1[jb + 2], x1[jb + 3]}, c1);
+                }
+#pragma unroll
+                for (int ms = 0; ms < KH; ms++) {
+                    const u4_t w = reinterpret_cast<const u4_t *>(lds + O_WH)[
+                        ((slot * KHE + ms) * 2 + (r & 1)) * 16 + 4 * (r >> 2) + kb];
+                    // boosted slots 4 (kb & 1) + i and + 8 of dword 2 ms + kb / 2,
+                    // at mantissa bits 2 sig_hi(i), sig_hi = {2, 3, 2, 3}
+#pragma unroll
+                    for (int mt = 0; mt < 2; mt++) {
+                        const uint32_t x = Gr.khi[mt][ms] >> (8 * (kb & 1));
+                        const uint32_t xl = x << 4;
+                        const u4_t bh = {xl & 0x00300030u, xl & 0x00C000C0u, x & 0x00300030u,
+                                         x & 0x00C000C0u};
+                        if (mt == 0) c0 = mfma_f16(w, bh, c0);
+                        else c1 = mfma_f16(w, bh, c1);
+                    }
+                }
+                // ---- online softmax: lane (token r, row kb) owns its head's scores ----
+#pragma unroll
+                for (int a = 0; a < 2; a++) {
+                    const int s = 2 * qs + a;
+                    if (s >= HQ) break;
+                    const float sc0 = fmaf(c0[2 * a] + c0[2 * a + 1], sback, bias[s]);
+                    const float sc1 = fmaf(c1[2 * a] + c1[2 * a + 1], sback, bias[s]);
+                    const float mx = row_max(fmaxf(sc0, sc1));
+                    if (__any(mx > m_run[s])) {  // wave-uniform: rescale only when a max grows
+                        const float mnew = fmaxf(m_run[s], mx);
+                        const float alpha = __builtin_amdgcn_exp2f(m_run[s] - mnew);
+                        m_run[s] = mnew;
+                        l_part[s] *= alpha;
+#pragma unroll
+                        for (int n = 0; n < 8; n++) acc[s][n] *= alpha;
+                        zt[s] *= from_row(alpha, r >> 2);  // zt lanes hold head row r / 4
+                    }
+                    const float mo = m_run[s] - (float)Eu;
+                    const float p0 = __builtin_amdgcn_exp2f(sc0 - mo);
+                    const float p1 = __builtin_amdgcn_exp2f(sc1 - mo);
+                    l_part[s] += p0 + p1;
+                    px[(s * 4 + kb) * 32 + r] = p0;
+                    px[(s * 4 + kb) * 32 + 16 + r] = p1;
+                }
+            }
+            wave_sync();
+        }
+
+        // ---- PV on the matrix cores (32 tokens x 16-channel tiles) ----
+        u4_t ahi[HQ], alo[HQ];
+        {
+            const int cg = r & 3;
+            const float4 va = *reinterpret_cast<const float4 *>(st + 128 + 32 * cg + 4 * kb);
+            const float4 vb = *reinterpret_cast<const float4 *>(st + 128 + 32 * cg + 16 + 4 * kb);
+            const float4 za = *reinterpret_cast<const float4 *>(st + 256 + 32 * cg + 4 * kb);
+            const float4 zb = *reinterpret_cast<const float4 *>(st + 256 + 32 * cg + 16 + 4 * kb);
+            const float v8[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+            const float z8[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+#pragma unroll
+            for (int s = 0; s < HQ; s++) {
+                const float4 pa = *reinterpret_cast<const float4 *>(px + (s * 4 + (r >> 2)) * 32 + 4 * kb);
+                const float4 pb =
+                    *reinterpret_cast<const float4 *>(px + (s * 4 + (r >> 2)) * 32 + 16 + 4 * kb);
+                const float p8[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++) {
+                    split2(p8[2 * e2] * v8[2 * e2], p8[2 * e2 + 1] * v8[2 * e2 + 1], hi[e2], lo[e2]);
+                    zt[s] = fmaf(p8[2 * e2], z8[2 * e2], fmaf(p8[2 * e2 + 1], z8[2 * e2 + 1], zt[s]));
+                }
+                ahi[s] = u4_t{hi[0], hi[1], hi[2], hi[3]};
+                alo[s] = u4_t{lo[0], lo[1], lo[2], lo[3]};
+            }
+        }
+        const Codes8 v0(Gr.vc[0]), v1(Gr.vc[1]), v2(Gr.vc[2]), v3(Gr.vc[3]);
+#pragma unroll
+        for (int n = 0; n < 8; n++) {
+            const u4_t bv = {v0[n], v1[n], v2[n], v3[n]};
+#pragma unroll
+            for (int s = 0; s < HQ; s++) {
+                f4_t cs = mfma_f16(ahi[s], bv, f4_t{0, 0, 0, 0});
+                cs = mfma_f16(alo[s], bv, cs);
+                acc[s][n] += cs[n >> 1];
+            }
+        }
+    };
 
     const int p0 = split * pps;
     const int p1 = min(n_pages, p0 + pps);
     const uint8_t *ubase = cache + (size_t)unit * max_pages * page_bytes;
-    PageRegs cur;
+    GroupRegs<KHE> ga, gb;
+    uint32_t ib[KHE][2];
     {
         const __amdgpu_buffer_rsrc_t rs0 = page_rsrc(ubase + (size_t)p0 * page_bytes, page_bytes);
-        load_codes<KH>(cur, rs0, Ly, k, lane);
-        load_meta(cur, rs0, Ly, lane, meta_chunks, meta_a);
+        load_group<KH>(ga, rs0, O, 0);
+        load_idx<KH>(ib, rs0, O);
     }
-
     for (int p = p0; p < p1; p++) {
-        // prefetch of the next page (the last page is loaded again at the end:
-        // harmless): codes now, metadata once this page's copy is in LDS
+        const __amdgpu_buffer_rsrc_t rs = page_rsrc(ubase + (size_t)p * page_bytes, page_bytes);
+        // the last page is loaded again at the end: harmless
         const __amdgpu_buffer_rsrc_t rsn =
             page_rsrc(ubase + (size_t)min(p + 1, p1 - 1) * page_bytes, page_bytes);
-        PageRegs nxt;
-        load_codes<KH>(nxt, rsn, Ly, k, lane);
-        wave_sync();  // previous page's LDS reads are done
+        // boosted channels of this page: gather q' once for its four groups
 #pragma unroll
-        for (int i = 0; i < 5; i++) reinterpret_cast<uint4 *>(meta)[lane + 64 * i] = cur.meta[i];
-        load_meta(nxt, rsn, Ly, lane, meta_chunks, meta_a);
-
-        // Page exponent of the weights: |4 w 2^E / 4^sig| <= qmax max(s) 2^(E-2) <= 2^14.
-        float smax = 0.0f;
-        {
-            uint4 c = cur.meta[0];  // chunks 0..63 are exactly K_scale (1024 B)
-            uint32_t wv[4] = {c.x, c.y, c.z, c.w};
+        for (int ms = 0; ms < KH; ms++)
 #pragma unroll
-            for (int e = 0; e < 8; e++)
-                smax = fmaxf(smax, fabsf(dec<DT>((uint16_t)(wv[e >> 1] >> (16 * (e & 1))))));
-            smax = wave_max(smax);
-        }
-        int eb;
-        frexpf(qmax * smax, &eb);
-        const int E = __builtin_amdgcn_readfirstlane(min(100, max(-60, 16 - eb)));
-        const float wscale = ldexpf(1.0f, E);
-        const float sback = ldexpf(1.0f, 24 - E);
-        wave_sync();
-
-        // Value scales and zeros as fp32 tables (padded rows: conflict-free reads),
-        // scales multiplied by 2^Eu so that u = p s_v splits into normal fp16 parts.
-        float vsr[8], vzr[8];
-        {
-            const int cg = lane >> 4, t8 = 8 * (lane & 15);
-            uint4 sv = *reinterpret_cast<const uint4 *>(mvs + cg * P + t8);
-            uint4 zv = *reinterpret_cast<const uint4 *>(mvz + cg * P + t8);
-            uint32_t sw4[4] = {sv.x, sv.y, sv.z, sv.w}, zw4[4] = {zv.x, zv.y, zv.z, zv.w};
-            float vmax = 0.0f;
+            for (int t = 0; t < 2; t++) {
+                const int j = 32 * ms + 16 * (hkb >> 1) + 4 * (hkb & 1) + hq + 8 * t;
+                const int c = (int)(ib[ms][t] & 127u);
+                hc[ms][t] = c;
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                vsr[e] = dec<DT>((uint16_t)(sw4[e >> 1] >> (16 * (e & 1))));
-                vzr[e] = dec<DT>((uint16_t)(zw4[e >> 1] >> (16 * (e & 1))));
-                vmax = fmaxf(vmax, fabsf(vsr[e]));
+                for (int s = 0; s < HQ; s++)
+                    qh[s][ms][t] = j < k ? qv(head_of<G>(hR, s), c) * fh : 0.0f;
             }
-            vmax = wave_max(vmax);
-            int ev;
-            frexpf(vmax, &ev);
-            const int Eu_new = __builtin_amdgcn_readfirstlane(min(Eu, min(100, max(-60, 14 - ev))));
-            const float urescale = ldexpf(1.0f, max(Eu_new - Eu, -126));
-            Eu = Eu_new;
-            const float uscale = ldexpf(1.0f, Eu);
-#pragma unroll
-            for (int e = 0; e < 8; e++) vsr[e] *= uscale;
-            float *vst = &vsf[cg][t8];
-            float *vzt = &vzf[cg][t8];
-            *reinterpret_cast<float4 *>(vst) = make_float4(vsr[0], vsr[1], vsr[2], vsr[3]);
-            *reinterpret_cast<float4 *>(vst + 4) = make_float4(vsr[4], vsr[5], vsr[6], vsr[7]);
-            *reinterpret_cast<float4 *>(vzt) = make_float4(vzr[0], vzr[1], vzr[2], vzr[3]);
-            *reinterpret_cast<float4 *>(vzt + 4) = make_float4(vzr[4], vzr[5], vzr[6], vzr[7]);
-#pragma unroll
-            for (int qd = 0; qd < HQ; qd++)
-#pragma unroll
-                for (int n = 0; n < 8; n++) acc[qd][n] *= urescale;
-        }
-
-        // Zero-point term per (head, group): bias = sum_c q'(h, c) z(g, c).
-        float bias[HQ][4];
-        {
-            u4_t az[4];
-#pragma unroll
-            for (int m = 0; m < 4; m++)
-                az[m] = r < 4 ? *reinterpret_cast<const u4_t *>(mkz + r * D + 32 * m + 8 * G4)
-                              : u4_t{0, 0, 0, 0};
-#pragma unroll
-            for (int qd = 0; qd < HQ; qd++) {
-                f4_t cb = {0, 0, 0, 0};
-#pragma unroll
-                for (int m = 0; m < 4; m++) cb = mfma_dt<DT>(az[m], tq3[qd][m][lane], cb);
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    float v = cb[g];
-                    v += dpp_quad_swap1(v);
-                    v += dpp_quad_swap2(v);
-                    bias[qd][g] = bcast_row0(v);  // rows 0..3 live in lanes 0..15
-                }
-            }
-        }
-        // Hi-plane weights of all four groups, once per page: lane = 16 g + 4 hG + ph
-        // computes 4 q'(head, idx[j]) s(g, idx[j]) 2^E / 4^sig_hi(i) for the boosted
-        // slots j = 32 ms + 16 (hG / 2) + 4 (hG % 2) + i + 8 e of K step ms.
-#pragma unroll
-        for (int ms = 0; ms < KH; ms++) {
-            const int hg = lane >> 4;
-            float wv[HQ][4][2];
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int e = 0; e < 2; e++) {
-                    const int j = 32 * ms + hjb + i + 8 * e;
-                    const int c = j < k ? (int)midx[j] : -1;
-                    const float sv = c >= 0 ? dec<DT>(mks[hg * D + c]) : 0.0f;
-                    const float f = 4.0f * wscale / (float)(1 << (2 * (2 + (i & 1))));
-#pragma unroll
-                    for (int qd = 0; qd < HQ; qd++) {
-                        const int hh = 4 * qd + ph;
-                        wv[qd][i][e] = c >= 0 && hh < G ? qf[hh][c] * sv * f : 0.0f;
-                    }
-                }
-#pragma unroll
-            for (int qd = 0; qd < HQ; qd++) {
-                uint32_t hi[4], lo[4];
-#pragma unroll
-                for (int i = 0; i < 4; i++) split2(wv[qd][i][0], wv[qd][i][1], hi[i], lo[i]);
-                wBh[qd][hg][ms][0][lane & 15] = u4_t{hi[0], hi[1], hi[2], hi[3]};
-                wBh[qd][hg][ms][1][lane & 15] = u4_t{lo[0], lo[1], lo[2], lo[3]};
-            }
-        }
-        float qlo[HQ][4][2];
-#pragma unroll
-        for (int qd = 0; qd < HQ; qd++) {
-            float4 a = *reinterpret_cast<const float4 *>(&tqs[qd][lane][0]);
-            float4 c = *reinterpret_cast<const float4 *>(&tqs[qd][lane][4]);
-            const float t8[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int e = 0; e < 2; e++) qlo[qd][i][e] = t8[2 * i + e] * wscale;
-        }
-
-        const int cgr = r & 3;  // Value group of this lane's PV row
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-            // --- weights of this group into LDS: lo plane and hi plane ---
-            wave_sync();  // previous group's weight reads are done
-            {
-                uint2 sa = *reinterpret_cast<const uint2 *>(mks + g * D + pbase);
-                uint2 sb = *reinterpret_cast<const uint2 *>(mks + g * D + pbase + 8);
-                float s0[4] = {dec<DT>((uint16_t)(sa.x & 0xffff)), dec<DT>((uint16_t)(sa.x >> 16)),
-                               dec<DT>((uint16_t)(sa.y & 0xffff)), dec<DT>((uint16_t)(sa.y >> 16))};
-                float s1[4] = {dec<DT>((uint16_t)(sb.x & 0xffff)), dec<DT>((uint16_t)(sb.x >> 16)),
-                               dec<DT>((uint16_t)(sb.y & 0xffff)), dec<DT>((uint16_t)(sb.y >> 16))};
-#pragma unroll
-                for (int qd = 0; qd < HQ; qd++) {
-                    uint32_t hi[4], lo[4];
-#pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        split2(qlo[qd][i][0] * s0[i], qlo[qd][i][1] * s1[i], hi[i], lo[i]);
-                    wB[qd][0][lane] = u4_t{hi[0], hi[1], hi[2], hi[3]};
-                    wB[qd][1][lane] = u4_t{lo[0], lo[1], lo[2], lo[3]};
-                }
-            }
-            wave_sync();
-#pragma unroll
-            for (int qd = 0; qd < HQ; qd++) {
-                // --- QK on the matrix cores: two 16-token tiles ---
-                const int hl = r & 1, hp = r >> 2;
-                u4_t bw[4 + (KH > 0 ? KH : 1)];
-#pragma unroll
-                for (int m = 0; m < 4; m++) bw[m] = wB[qd][hl][16 * m + 4 * G4 + hp];
-#pragma unroll
-                for (int ms = 0; ms < KH; ms++) bw[4 + ms] = wBh[qd][g][ms][hl][4 * G4 + hp];
-                float sc[2][4];
-#pragma unroll
-                for (int mt = 0; mt < 2; mt++) {
-                    const uint2 kl = cur.klo[2 * g + mt];
-                    f4_t c = {0, 0, 0, 0};
-                    const Codes8 c0(kl.x), c1(kl.y);
-#pragma unroll
-                    for (int m = 0; m < 4; m++) {
-                        const Codes8 &cx = m < 2 ? c0 : c1;
-                        int jb = 4 * (m & 1);
-                        u4_t a = {cx[jb], cx[jb + 1], cx[jb + 2], cx[jb + 3]};
-                        c = mfma_f16(a, bw[m], c);
-                    }
-#pragma unroll
-                    for (int ms = 0; ms < KH; ms++) {
-                        // boosted columns 4 (G4 & 1) + i and + 8 of dword 2 ms + G4 / 2,
-                        // at mantissa bits 2 sig_hi(i), sig_hi = {2, 3, 2, 3}
-                        uint32_t x = cur.khi[2 * g + mt][ms] >> (8 * (G4 & 1));
-                        uint32_t xl = x << 4;
-                        u4_t a = {xl & 0x00300030u, xl & 0x00C000C0u, x & 0x00300030u,
-                                  x & 0x00C000C0u};
-                        c = mfma_f16(a, bw[4 + ms], c);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        sc[mt][e] = fmaf(c[e] + dpp_quad_swap1(c[e]), sback, bias[qd][g]);
-                }
-
-                // --- online softmax over these 32 tokens, per head ---
-                float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                                 fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-                mx = xmax32(xmax16(mx));
-                if (__any(mx > m_run[qd])) {  // wave-uniform: rescale only when a max grows
-                    float mnew = fmaxf(m_run[qd], mx);
-                    float alpha = __builtin_amdgcn_exp2f(m_run[qd] - mnew);
-                    m_run[qd] = mnew;
-                    l_part[qd] *= alpha;
-                    zt[qd] *= alpha;
-                    // accumulator lanes hold head G4 of the quad: that head's alpha
-                    float al = from_lane4g(alpha, G4);
-#pragma unroll
-                    for (int n = 0; n < 8; n++) acc[qd][n] *= al;
-                }
-                float pr[2][4];
-#pragma unroll
-                for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        pr[mt][e] = __builtin_amdgcn_exp2f(sc[mt][e] - m_run[qd]);
-                        l_part[qd] += pr[mt][e];
-                    }
-
-                // --- PV on the matrix cores (32 tokens x 16-channel tiles) ---
-                uint32_t ahi[4], alo[4];
-                {
-                    const int t = 32 * g + 4 * G4;
-                    float4 s0 = *reinterpret_cast<const float4 *>(&vsf[cgr][t]);
-                    float4 s1 = *reinterpret_cast<const float4 *>(&vsf[cgr][t + 16]);
-                    float4 z0 = *reinterpret_cast<const float4 *>(&vzf[cgr][t]);
-                    float4 z1 = *reinterpret_cast<const float4 *>(&vzf[cgr][t + 16]);
-                    const float vs8[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-                    const float vz8[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; e2++) {
-                        float pa = pr[e2 >> 1][2 * (e2 & 1)], pb = pr[e2 >> 1][2 * (e2 & 1) + 1];
-                        split2(pa * vs8[2 * e2], pb * vs8[2 * e2 + 1], ahi[e2], alo[e2]);
-                        zt[qd] = fmaf(pa, vz8[2 * e2], fmaf(pb, vz8[2 * e2 + 1], zt[qd]));
-                    }
-                }
-                const u4_t a_hi = {ahi[0], ahi[1], ahi[2], ahi[3]};
-                const u4_t a_lo = {alo[0], alo[1], alo[2], alo[3]};
-                const uint4 vb = cur.vc[g];
-                const Codes8 v0(vb.x), v1(vb.y), v2(vb.z), v3(vb.w);
-#pragma unroll
-                for (int n = 0; n < 8; n++) {
-                    const u4_t bv = {v0[n], v1[n], v2[n], v3[n]};
-                    f4_t cs = mfma_f16(a_hi, bv, f4_t{0, 0, 0, 0});
-                    cs = mfma_f16(a_lo, bv, cs);
-                    acc[qd][n] += cs[n >> 1];
-                }
-            }
-        }
-        cur = nxt;
+        load_group<KH>(gb, rs, O, 1);
+        process(ga);
+        load_group<KH>(ga, rs, O, 2);
+        process(gb);
+        load_group<KH>(gb, rs, O, 3);
+        process(ga);
+        load_group<KH>(ga, rsn, O, 0);
+        load_idx<KH>(ib, rsn, O);
+        process(gb);
     }
 
-    // --- partials: lane (c_local = r, G4) owns head 4 qd + G4, channels 16 n + r ---
+    // --- partials: lane (r, R) owns head head_of(R, s), channels 16 n + r ---
 #pragma unroll
-    for (int qd = 0; qd < HQ; qd++) {
-        // l and the Value zero term: sum over the four lane groups G4
-        float l = l_part[qd];
-        l += shfl_xor(l, 16);
-        l += shfl_xor(l, 32);
-        float z = zt[qd];
+    for (int s = 0; s < HQ; s++) {
+        const float l = row_sum(l_part[s]);
+        // zt: lanes (4 R' + cg, kb) hold head row R', Value group cg: sum over kb
+        float z = zt[s];
         z += shfl_xor(z, 16);
-        z += shfl_xor(z, 32);  // lanes (4 h' + cg, *) hold head h', group cg
-        const int hh = 4 * qd + G4;
-        float lh = shfl(l, 4 * G4);
-        float mh = shfl(m_run[qd], 4 * G4);
+        z += shfl_xor(z, 32);
         float zg[4];
 #pragma unroll
-        for (int cg = 0; cg < 4; cg++) zg[cg] = shfl(z, 4 * G4 + cg);
-        if (hh < G) {
-            size_t bq = (size_t)b * Hq + h * G + hh;
+        for (int cg = 0; cg < 4; cg++) zg[cg] = shfl(z, 4 * kb + cg);
+        const int hh = head_of<G>(kb, s);
+        if (G >= 4 || kb < G) {
+            const size_t bq = (size_t)b * Hq + h * G + hh;
             float *dst = ws_acc + (bq * max_splits + split) * D;
 #pragma unroll
             for (int n = 0; n < 8; n++)
-                dst[16 * n + r] =
-                    acc[qd][n] * ldexpf(1.0f, 24 - 2 * code_sig(n) - Eu) + zg[n >> 1];
+                dst[16 * n + r] = acc[s][n] * ldexpf(1.0f, 24 - 2 * code_sig(n)) + zg[n >> 1];
             if (r == 0) {
-                ws_ml[(bq * max_splits + split) * 2 + 0] = mh;
-                ws_ml[(bq * max_splits + split) * 2 + 1] = lh;
+                ws_ml[(bq * max_splits + split) * 2 + 0] = m_run[s] - (float)Eu;
+                ws_ml[(bq * max_splits + split) * 2 + 1] = l;
             }
         }
     }
