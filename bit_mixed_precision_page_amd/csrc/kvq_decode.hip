@@ -48,6 +48,7 @@ namespace kvq {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxCombine = 272;  // splits one combine workgroup merges (>= 256 + 4 window splits)
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
@@ -138,6 +139,15 @@ __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dppc<0x4E>(v));   // quad_perm [2,3,0,1]
     v = fmaxf(v, dppc<0xB1>(v));   // quad_perm [1,0,3,2]
     return xmax32(xmax16(v));
+}
+// sum over the whole wave, in every lane
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dppc<0x128>(v);
+    v += dppc<0x124>(v);
+    v += dppc<0x4E>(v);
+    v += dppc<0xB1>(v);
+    v += __shfl_xor(v, 16, 64);
+    return v + __shfl_xor(v, 32, 64);
 }
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
@@ -731,21 +741,63 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
     }
 }
 
-__global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ ws_ml,
-                                                    const float *__restrict__ ws_acc,
-                                                    float *__restrict__ out, int total_splits,
-                                                    int max_splits) {
+// One workgroup of four waves per (sequence, query head): the split weights
+// exp2(m_s - M) are computed once into LDS, each wave sums a quarter of the
+// splits for all 128 channels with four loads in flight per lane, and LDS
+// adds the four partial sums (the partials are read once, latency hidden).
+constexpr int kCombineThreads = 256;
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *__restrict__ ws_ml,
+                                                                  const float *__restrict__ ws_acc,
+                                                                  float *__restrict__ out, int n,
+                                                                  int max_splits) {
+    __shared__ float wsh[kMaxCombine];
+    __shared__ float red[4], dred[4];
+    __shared__ float2 part[4][64];
     const size_t bq = blockIdx.x;
-    const int c = threadIdx.x;
-    float M = -INFINITY;
-    for (int s = 0; s < total_splits; s++) M = fmaxf(M, ws_ml[(bq * max_splits + s) * 2]);
-    float num = 0.0f, den = 0.0f;
-    for (int s = 0; s < total_splits; s++) {
-        float w = __builtin_amdgcn_exp2f(ws_ml[(bq * max_splits + s) * 2] - M);
-        num = fmaf(w, ws_acc[(bq * max_splits + s) * D + c], num);
-        den = fmaf(w, ws_ml[(bq * max_splits + s) * 2 + 1], den);
+    const int t = threadIdx.x, wv = t >> 6, ln = t & 63;
+    const float *ml = ws_ml + bq * max_splits * 2;
+    float m = -INFINITY;
+    for (int s = t; s < n; s += kCombineThreads) m = fmaxf(m, ml[2 * s]);
+    m = wave_max(m);
+    if (ln == 0) red[wv] = m;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float den = 0.0f;
+    for (int s = t; s < n; s += kCombineThreads) {
+        const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
+        wsh[s] = w;
+        den = fmaf(w, ml[2 * s + 1], den);
     }
-    out[bq * D + c] = num / den;
+    den = wave_sum(den);
+    if (ln == 0) dred[wv] = den;
+    __syncthreads();
+    const float2 *a = reinterpret_cast<const float2 *>(ws_acc + bq * max_splits * D) + ln;
+    float2 acc = make_float2(0.0f, 0.0f);
+    int s = wv;
+    for (; s + 12 < n; s += 16) {
+        const float2 x0 = a[(s + 0) * (D / 2)], x1 = a[(s + 4) * (D / 2)];
+        const float2 x2 = a[(s + 8) * (D / 2)], x3 = a[(s + 12) * (D / 2)];
+        const float w0 = wsh[s], w1 = wsh[s + 4], w2 = wsh[s + 8], w3 = wsh[s + 12];
+        acc.x = fmaf(w0, x0.x, fmaf(w1, x1.x, fmaf(w2, x2.x, fmaf(w3, x3.x, acc.x))));
+        acc.y = fmaf(w0, x0.y, fmaf(w1, x1.y, fmaf(w2, x2.y, fmaf(w3, x3.y, acc.y))));
+    }
+    for (; s < n; s += 4) {
+        const float2 x = a[s * (D / 2)];
+        acc.x = fmaf(wsh[s], x.x, acc.x);
+        acc.y = fmaf(wsh[s], x.y, acc.y);
+    }
+    part[wv][ln] = acc;
+    __syncthreads();
+    if (wv == 0) {
+        float2 r = part[0][ln];
+#pragma unroll
+        for (int i = 1; i < 4; i++) {
+            r.x += part[i][ln].x;
+            r.y += part[i][ln].y;
+        }
+        const float inv = 1.0f / (dred[0] + dred[1] + dred[2] + dred[3]);
+        reinterpret_cast<float2 *>(out + bq * D)[ln] = make_float2(r.x * inv, r.y * inv);
+    }
 }
 
 // Resident workgroups of this instantiation on the whole device (occupancy API),
@@ -847,7 +899,8 @@ hipError_t launch_decode(const Geometry &G, const uint8_t *cache, const uint16_t
                        : launch1<BF16>(G, cache, q, ml, acc, pl, st);
     if (e != hipSuccess) return e;
     if (ev_after && (e = hipEventRecord(ev_after, st)) != hipSuccess) return e;
-    hipLaunchKernelGGL(combine_kernel, dim3(G.B * G.Hq), dim3(D), 0, st, ml, acc, out,
+    if (pl.total_splits > kMaxCombine) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(combine_kernel, dim3(G.B * G.Hq), dim3(kCombineThreads), 0, st, ml, acc, out,
                        pl.total_splits, pl.max_splits);
     return hipGetLastError();
 }
