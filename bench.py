@@ -43,6 +43,10 @@ def parse():
                     help="bytes of cache replicas the steps rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="page splits (0 = automatic)")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="bracket the split kernel with HIP events on every N-th timed step")
+    ap.add_argument("--event-fence", action="store_true",
+                    help="events with the default system-scope fence (slower markers)")
     return ap.parse_args()
 
 
@@ -75,6 +79,36 @@ def pmc_traffic(kernel, workload):
     if rec.get("source_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+class HipEvents:
+    """Timing events created through the HIP runtime with an explicit flag:
+    hipEventDisableSystemFence leaves out the system-scope fence when the
+    marker completes, which shortens the gap a marker opens in the stream."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n, fence):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        flags = 0 if fence else self.DISABLE_SYSTEM_FENCE
+        self.ev = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(flags))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.ev.append(e)
+
+    def pair(self, i):
+        return self.ev[2 * i].value, self.ev[2 * i + 1].value
+
+    def elapsed_ms(self, i):
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ev[2 * i], self.ev[2 * i + 1])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
 
 
 def main():
@@ -136,11 +170,9 @@ def main():
         kts.append(to_dev(kt))
         vts.append(to_dev(vt))
     out = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device=dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(a.steps)]
-    for e0, e1 in evs:  # materialize the events so their handles exist
-        e0.record()
-        e1.record()
+    timed = [i for i in range(a.steps) if a.event_every > 0 and i % a.event_every == 0]
+    hev = HipEvents(len(timed), a.event_fence)
+    ev_of = {i: hev.pair(j) for j, i in enumerate(timed)}
     torch.cuda.synchronize()
     print(f"[bench] setup {time.time() - t0:.1f}s; {layers} layer replicas of "
           f"{base.nbytes / 1e6:.1f} MB; state {n_pages0} pages + {n_res0} window",
@@ -153,8 +185,7 @@ def main():
         li = s % layers
         c = caches[li]
         if ev is not None:
-            kvq.kvq_set_kernel_events(c.handle, ev[0]._as_parameter_.value,
-                                      ev[1]._as_parameter_.value)
+            kvq.kvq_set_kernel_events(c.handle, ev[0], ev[1])
         flushed = c.append_token(kts[s], vts[s])
         c.decode_attention(qs[s], out)
         if ev is not None:
@@ -173,25 +204,26 @@ def main():
     start.record()
     for i in range(a.steps):
         s = a.warmup + i
-        flushed, n_pages, n_res = step(s, evs[i])
+        flushed, n_pages, n_res = step(s, ev_of.get(i))
         ab = attention_bytes(w, pb, n_pages, n_res)
         attn_bytes_sum += ab
         total_bytes += ab + append_bytes(w, pb, flushed)
-        split_bytes.append(ab - w.B * w.Hq * 128 * 4)  # pages + window + query
+        if i in ev_of:
+            split_bytes.append(ab - w.B * w.Hq * 128 * 4)  # pages + window + query
         n_flush += int(flushed)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
     ms_step = ms / a.steps
-    kern_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
-    kern_avg_s = float(kern_ms.mean()) / 1e3
-    achieved = float(np.mean(split_bytes)) / kern_avg_s / 1e9
+    kern_ms = np.array([hev.elapsed_ms(j) for j in range(len(timed))])
+    kern_avg_s = float(kern_ms.mean()) / 1e3 if len(timed) else float("nan")
+    achieved = float(np.mean(split_bytes)) / kern_avg_s / 1e9 if len(timed) else float("nan")
     value = total_bytes / (ms / 1e3) / 1e9
     attn_gbs = attn_bytes_sum / (ms / 1e3) / 1e9
     splits = kvq.kvq_get_decode_splits(caches[0].handle)
     print(f"[bench] {a.steps} steps in {ms:.3f} ms ({ms_step * 1e3:.1f} us/step, "
-          f"split kernel avg {kern_avg_s * 1e6:.1f} us, {n_flush} flushes)", file=sys.stderr,
-          flush=True)
+          f"split kernel avg {kern_avg_s * 1e6:.1f} us over {len(timed)} launches, "
+          f"{n_flush} flushes)", file=sys.stderr, flush=True)
 
     cpu = None
     if not a.no_cpu_baseline:

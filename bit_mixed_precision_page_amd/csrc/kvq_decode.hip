@@ -214,6 +214,7 @@ struct GroupRegs {
     uint32_t khi[2][KHE];  // K hi plane dwords 2 ms + (lane >> 5) of the same tokens
     u4_t vc;               // V codes: this lane's 16-byte block of the group
     u4_t meta;             // one 16-byte chunk of the group's metadata
+    uint32_t ib[KHE][2];   // indices of this lane's two boosted slots (page data)
 };
 
 // Page loads go through a buffer descriptor of the page itself: 32-bit lane
@@ -232,15 +233,17 @@ struct LaneOffs {
     int idx[KHE][2];
 };
 
-// Every load is issued unconditionally (offsets clamped into the page) so the
-// number of loads in flight is static and the compiler can wait for one
-// group's data without draining the loads of the next.
+// Group g (0..3) of a page: the part of each offset common to all lanes goes
+// into the scalar offset.  Every load is issued unconditionally (offsets
+// clamped into the page) so the number of loads in flight is static and the
+// compiler can wait for one group's data without draining the loads of the
+// next.
 template <int KH, int KHE>
 __device__ __forceinline__ void load_group(GroupRegs<KHE> &Gr, __amdgpu_buffer_rsrc_t rs,
                                            const LaneOffs<KHE> &O, int g) {
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
-        auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, O.klo + 512 * (2 * g + mt), 0, 0);
+        auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, O.klo + 512 * mt, 1024 * g, 0);
         Gr.klo[mt] = make_uint2(v[0], v[1]);
     }
 #pragma unroll
@@ -248,17 +251,13 @@ __device__ __forceinline__ void load_group(GroupRegs<KHE> &Gr, __amdgpu_buffer_r
 #pragma unroll
         for (int ms = 0; ms < KH; ms++)
             Gr.khi[mt][ms] = __builtin_amdgcn_raw_buffer_load_b32(
-                rs, O.khi[ms] + (2 * g + mt) * O.khi_tile, 0, 0);
-    Gr.vc = __builtin_amdgcn_raw_buffer_load_b128(rs, O.vc + 1024 * g, 0, 0);
+                rs, O.khi[ms] + mt * O.khi_tile, 2 * g * O.khi_tile, 0);
+    Gr.vc = __builtin_amdgcn_raw_buffer_load_b128(rs, O.vc, 1024 * g, 0);
     Gr.meta = __builtin_amdgcn_raw_buffer_load_b128(rs, O.meta + g * O.mstride, 0, 0);
-}
-template <int KH, int KHE>
-__device__ __forceinline__ void load_idx(uint32_t (&ib)[KHE][2], __amdgpu_buffer_rsrc_t rs,
-                                         const LaneOffs<KHE> &O) {
 #pragma unroll
     for (int ms = 0; ms < KH; ms++)
 #pragma unroll
-        for (int t = 0; t < 2; t++) ib[ms][t] = __builtin_amdgcn_raw_buffer_load_b8(rs, O.idx[ms][t], 0, 0);
+        for (int t = 0; t < 2; t++) Gr.ib[ms][t] = __builtin_amdgcn_raw_buffer_load_b8(rs, O.idx[ms][t], 0, 0);
 }
 
 // Waves per SIMD the register allocation aims at (more registers per wave
@@ -271,7 +270,7 @@ template <int DT, int G, int KH>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target(G, KH)))) void decode_split_kernel(
     const uint8_t *__restrict__ cache, const uint16_t *__restrict__ q, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, int Hkv, int max_pages, uint32_t page_bytes, int k,
-    size_t res_base, int n_pages, int n_res, int page_splits, int pps, int max_splits,
+    size_t res_base, int n_pages, int n_res, int page_splits, int gps, int win_splits, int max_splits,
     float qscale) {
     constexpr int HQ = (G + 3) / 4;    // head slots per row of lanes
     constexpr int NQS = (HQ + 1) / 2;  // QK row sets (two slots each)
@@ -286,28 +285,32 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
     constexpr int O_KZ = O_ST + 384 * 4;                  // u16 [D] K zero of the group
     constexpr int O_PX = O_KZ + D * 2;                    // f32 [HQ][4][32] softmax weights
     constexpr int PAGE_LDS = O_PX + HQ * 4 * 32 * 4;
-    constexpr int WIN_LDS = G * D * 4 + G * 32 * 4;
+    constexpr int WIN_LDS = G * D * 4 + 32 * G * 4;
     __shared__ __align__(16) uint8_t lds[PAGE_LDS > WIN_LDS ? PAGE_LDS : WIN_LDS];
 
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int unit = b * Hkv + h;
+    // 1-D grid: every page split of every (sequence, KV head) first, then the
+    // window splits, so the hardware places the long page waves evenly before
+    // the short window waves fill the remaining slots.
+    const int n_units = gridDim.x / (page_splits + win_splits);
+    int unit, split;
+    if ((int)blockIdx.x < page_splits * n_units) {
+        unit = blockIdx.x / page_splits;
+        split = blockIdx.x % page_splits;
+    } else {
+        const int l = blockIdx.x - page_splits * n_units;
+        unit = l / win_splits;
+        split = page_splits + l % win_splits;
+    }
+    const int h = unit % Hkv, b = unit / Hkv;
     const int Hq = Hkv * G;
     const int lane = threadIdx.x, r = lane & 15, kb = lane >> 4;
     const uint16_t *qg = q + ((size_t)b * Hq + h * G) * D;
 
     if (split >= page_splits) {
         // ---------------- window split: 32 exact tokens on the VALU ----------------
-        float(*qf)[D] = reinterpret_cast<float(*)[D]>(lds);
-        float(*sw)[32] = reinterpret_cast<float(*)[32]>(lds + G * D * 4);
-        for (int ch = lane; ch < G * (D / 8); ch += 64) {
-            uint4 v = *reinterpret_cast<const uint4 *>(qg + 8 * ch);
-            uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                qf[ch / (D / 8)][8 * (ch % (D / 8)) + e] =
-                    dec<DT>((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * qscale;
-        }
-        wave_sync();
+        // Every global load of the split (the token's K row, the V values of
+        // this lane's two channels for all 32 tokens, q) is issued before any
+        // arithmetic, so the split pays one memory latency.
         const int w = split - page_splits;
         const int t0 = 32 * w;
         const int nt = min(32, n_res - t0);
@@ -315,50 +318,93 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
                                                                 (size_t)unit * 2 * R * D * 2);
         const uint16_t *vw = kw + (size_t)R * D;
         const int tl = lane & 31, hs = lane >> 5;
+        constexpr int QCH = (G * (D / 8) + 63) / 64;
+        uint4 qraw[QCH];
+#pragma unroll
+        for (int i = 0; i < QCH; i++)
+            qraw[i] = *reinterpret_cast<const uint4 *>(qg + 8 * min(lane + 64 * i, G * (D / 8) - 1));
+        // lane (token tl, half hs) holds channels 64 hs + [0, 64) of its token
+        uint4 kr[D / 16];
+        {
+            const uint4 *row =
+                reinterpret_cast<const uint4 *>(kw + (size_t)(t0 + min(tl, nt - 1)) * D + 64 * hs);
+#pragma unroll
+            for (int c8 = 0; c8 < D / 16; c8++) kr[c8] = row[c8];
+        }
+        uint32_t vr[32];
+#pragma unroll
+        for (int t = 0; t < 32; t++)
+            vr[t] = *reinterpret_cast<const uint32_t *>(vw + (size_t)(t0 + min(t, nt - 1)) * D + 2 * lane);
+
+        float(*qf)[D] = reinterpret_cast<float(*)[D]>(lds);
+        float(*sw)[G] = reinterpret_cast<float(*)[G]>(lds + G * D * 4);  // [token][head]
+#pragma unroll
+        for (int i = 0; i < QCH; i++) {
+            const int ch = lane + 64 * i;
+            const uint32_t wv[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
+            if (ch < G * (D / 8)) {
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    qf[ch / (D / 8)][8 * (ch % (D / 8)) + e] =
+                        dec<DT>((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * qscale;
+            }
+        }
+        wave_sync();
+        float sg[G];
+#pragma unroll
+        for (int hh = 0; hh < G; hh++) sg[hh] = 0.0f;
+#pragma unroll
+        for (int c8 = 0; c8 < D / 16; c8++) {
+            const uint32_t wv[4] = {kr[c8].x, kr[c8].y, kr[c8].z, kr[c8].w};
+            float kv[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) kv[e] = dec<DT>((uint16_t)(wv[e >> 1] >> (16 * (e & 1))));
+#pragma unroll
+            for (int hh = 0; hh < G; hh++) {
+                const float4 qa = *reinterpret_cast<const float4 *>(&qf[hh][64 * hs + 8 * c8]);
+                const float4 qb = *reinterpret_cast<const float4 *>(&qf[hh][64 * hs + 8 * c8 + 4]);
+                const float q8[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+                for (int e = 0; e < 8; e++) sg[hh] = fmaf(q8[e], kv[e], sg[hh]);
+            }
+        }
+        // both halves of a token: add the partial dot products (lanes l, l ^ 32)
         float s[NHW];
 #pragma unroll
-        for (int j = 0; j < NHW; j++) s[j] = tl < nt ? 0.0f : -INFINITY;
-        if (tl < nt) {
-            const uint4 *row = reinterpret_cast<const uint4 *>(kw + (size_t)(t0 + tl) * D);
-            for (int c8 = 0; c8 < D / 8; c8++) {
-                uint4 v = row[c8];
-                uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+        for (int j = 0; j < NHW; j++) s[j] = 0.0f;
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    float kv = dec<DT>((uint16_t)(wv[e >> 1] >> (16 * (e & 1))));
-#pragma unroll
-                    for (int j = 0; j < NHW; j++) {
-                        int hh = hs + 2 * j;
-                        if (hh < G) s[j] = fmaf(qf[hh][8 * c8 + e], kv, s[j]);
-                    }
-                }
-            }
+        for (int hh = 0; hh < G; hh++) {
+            auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(sg[hh]), __float_as_uint(sg[hh]),
+                                                       false, false);
+            const float tot = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+            if ((hh & 1) == hs) s[hh >> 1] = tot;  // lane half hs keeps heads hs + 2 j
         }
         float mrow[NHW], lrow[NHW];
 #pragma unroll
         for (int j = 0; j < NHW; j++) {
-            float mx = s[j];
+            const float sj = tl < nt ? s[j] : -INFINITY;
+            float mx = sj;
 #pragma unroll
             for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
-            float p = tl < nt ? __builtin_amdgcn_exp2f(s[j] - mx) : 0.0f;
+            float p = tl < nt ? __builtin_amdgcn_exp2f(sj - mx) : 0.0f;
             float l = p;
 #pragma unroll
             for (int o = 16; o > 0; o >>= 1) l += shfl_xor(l, o);
             mrow[j] = mx;
             lrow[j] = l;
-            int hh = hs + 2 * j;
-            if (hh < G) sw[hh][tl] = p;
+            const int hh = hs + 2 * j;
+            if (hh < G) sw[tl][hh] = p;
         }
         wave_sync();
         float acc[G][2];
 #pragma unroll
         for (int hh = 0; hh < G; hh++) acc[hh][0] = acc[hh][1] = 0.0f;
-        for (int t = 0; t < nt; t++) {
-            uint32_t vv = *reinterpret_cast<const uint32_t *>(vw + (size_t)(t0 + t) * D + 2 * lane);
-            float v0 = dec<DT>((uint16_t)(vv & 0xffffu)), v1 = dec<DT>((uint16_t)(vv >> 16));
+#pragma unroll
+        for (int t = 0; t < 32; t++) {
+            const float v0 = dec<DT>((uint16_t)(vr[t] & 0xffffu)), v1 = dec<DT>((uint16_t)(vr[t] >> 16));
 #pragma unroll
             for (int hh = 0; hh < G; hh++) {
-                float p = sw[hh][t];
+                const float p = sw[t][hh];  // 0 past the last token
                 acc[hh][0] = fmaf(p, v0, acc[hh][0]);
                 acc[hh][1] = fmaf(p, v1, acc[hh][1]);
             }
@@ -488,6 +534,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
     float qh[HQ][KHE][2];
 
     auto process = [&](const GroupRegs<KHE> &Gr) __attribute__((always_inline)) {
+        // boosted channels of the group's page: gather their q'
+#pragma unroll
+        for (int ms = 0; ms < KH; ms++)
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const int j = 32 * ms + 16 * (hkb >> 1) + 4 * (hkb & 1) + hq + 8 * t;
+                const int c = (int)(Gr.ib[ms][t] & 127u);
+                hc[ms][t] = c;
+#pragma unroll
+                for (int s = 0; s < HQ; s++)
+                    qh[s][ms][t] = j < k ? qv(head_of<G>(hR, s), c) * fh : 0.0f;
+            }
         // ---- metadata: exponents from the largest scales (integer max of the
         // bits: scales are never negative), then fp32 copies into LDS ----
         const u4_t M = Gr.meta;
@@ -677,42 +735,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
         }
     };
 
-    const int p0 = split * pps;
-    const int p1 = min(n_pages, p0 + pps);
+    // groups [g0, g1) of this unit (four per page), two register sets in turn
+    const int g0 = split * gps;
+    const int g1 = min(4 * n_pages, g0 + gps);
     const uint8_t *ubase = cache + (size_t)unit * max_pages * page_bytes;
+    auto rs_of = [&](int gi) { return page_rsrc(ubase + (size_t)(gi >> 2) * page_bytes, page_bytes); };
     GroupRegs<KHE> ga, gb;
-    uint32_t ib[KHE][2];
-    {
-        const __amdgpu_buffer_rsrc_t rs0 = page_rsrc(ubase + (size_t)p0 * page_bytes, page_bytes);
-        load_group<KH>(ga, rs0, O, 0);
-        load_idx<KH>(ib, rs0, O);
-    }
-    for (int p = p0; p < p1; p++) {
-        const __amdgpu_buffer_rsrc_t rs = page_rsrc(ubase + (size_t)p * page_bytes, page_bytes);
-        // the last page is loaded again at the end: harmless
-        const __amdgpu_buffer_rsrc_t rsn =
-            page_rsrc(ubase + (size_t)min(p + 1, p1 - 1) * page_bytes, page_bytes);
-        // boosted channels of this page: gather q' once for its four groups
-#pragma unroll
-        for (int ms = 0; ms < KH; ms++)
-#pragma unroll
-            for (int t = 0; t < 2; t++) {
-                const int j = 32 * ms + 16 * (hkb >> 1) + 4 * (hkb & 1) + hq + 8 * t;
-                const int c = (int)(ib[ms][t] & 127u);
-                hc[ms][t] = c;
-#pragma unroll
-                for (int s = 0; s < HQ; s++)
-                    qh[s][ms][t] = j < k ? qv(head_of<G>(hR, s), c) * fh : 0.0f;
-            }
-        load_group<KH>(gb, rs, O, 1);
+    load_group<KH>(ga, rs_of(g0), O, g0 & 3);
+    for (int gi = g0;;) {
+        {
+            const int gn = min(gi + 1, g1 - 1);  // the last group is loaded again: harmless
+            load_group<KH>(gb, rs_of(gn), O, gn & 3);
+        }
         process(ga);
-        load_group<KH>(ga, rs, O, 2);
+        if (++gi >= g1) break;
+        {
+            const int gn = min(gi + 1, g1 - 1);
+            load_group<KH>(ga, rs_of(gn), O, gn & 3);
+        }
         process(gb);
-        load_group<KH>(gb, rs, O, 3);
-        process(ga);
-        load_group<KH>(ga, rsn, O, 0);
-        load_idx<KH>(ib, rsn, O);
-        process(gb);
+        if (++gi >= g1) break;
     }
 
     // --- partials: lane (r, R) owns head head_of(R, s), channels 16 n + r ---
@@ -822,10 +864,11 @@ int slots3() {
 template <int DT, int G, int KH>
 hipError_t launch3(const Geometry &Gm, const uint8_t *cache, const uint16_t *q, float *ml,
                    float *acc, const DecodePlan &pl, hipStream_t st) {
-    dim3 grid(pl.total_splits, Gm.Hkv, Gm.B);
+    dim3 grid(pl.total_splits * Gm.Hkv * Gm.B);
     hipLaunchKernelGGL((decode_split_kernel<DT, G, KH>), grid, dim3(64), 0, st, cache, q, ml,
                        acc, Gm.Hkv, Gm.max_pages, Gm.page_bytes, Gm.k, Gm.res_base,
-                       pl.n_pages, pl.n_res, pl.page_splits, pl.pages_per_split,
+                       pl.n_pages, pl.n_res, pl.page_splits, pl.groups_per_split,
+                       pl.total_splits - pl.page_splits,
                        pl.max_splits, Gm.scale * kLog2e);
     return hipGetLastError();
 }

@@ -65,8 +65,9 @@ size_t cache_bytes_of(const kvq::Geometry &G) {
 }
 
 int max_splits_of(const kvq::Geometry &G) {
-    // page splits + window splits (32 window tokens per split)
-    return std::min(G.max_pages, kMaxSplits) + kvq::R / 32;
+    // page splits (at most one per 32-token group) + window splits (32 window
+    // tokens per split)
+    return std::min(4 * G.max_pages, kMaxSplits) + kvq::R / 32;
 }
 
 kvq::DecodePlan plan_of(const kvq_cache *c) {
@@ -85,9 +86,10 @@ kvq::DecodePlan plan_of(const kvq_cache *c) {
             int win = (c->n_res + 31) / 32;
             S = std::max(1, kvq::decode_slots(c->G) / units - win);
         }
-        S = std::max(1, std::min(S, std::min(c->n_pages, kMaxSplits)));
-        pl.pages_per_split = (c->n_pages + S - 1) / S;
-        pl.page_splits = (c->n_pages + pl.pages_per_split - 1) / pl.pages_per_split;
+        const int groups = 4 * c->n_pages;
+        S = std::max(1, std::min(S, std::min(groups, kMaxSplits)));
+        pl.groups_per_split = (groups + S - 1) / S;
+        pl.page_splits = (groups + pl.groups_per_split - 1) / pl.groups_per_split;
     }
     pl.total_splits = pl.page_splits + (c->n_res + 31) / 32;
     return pl;

@@ -75,8 +75,8 @@ hipError_t launch_quantize_groups(int dtype, int L, const uint16_t *x, int n_gro
 
 struct DecodePlan {
     int n_pages, n_res;
-    int page_splits;      // splits over pages (0 when n_pages == 0)
-    int pages_per_split;
+    int page_splits;      // splits over the 32-token page groups (0 when n_pages == 0)
+    int groups_per_split;
     int total_splits;     // page_splits + ceil(n_res / 32) window splits
     int max_splits;       // workspace stride (splits per (b, hq))
 };

@@ -138,9 +138,11 @@ int kvq_decode_workspace_bytes(const kvq_cache *cache, size_t *bytes);
 int kvq_decode_attention(kvq_cache *cache, const void *q, float *out, void *workspace,
                          size_t ws_bytes, void *stream);
 
-/* Number of page splits per (sequence, KV head) decode attention uses:
-   splits = 0 restores the automatic choice; otherwise it is clamped to
-   [1, n_pages] at each call.  Results do not depend on it beyond rounding. */
+/* Number of page splits per (sequence, KV head) decode attention uses; a
+   split covers consecutive 32-token page groups.  splits = 0 restores the
+   automatic choice (one round of resident waves); otherwise it is clamped to
+   [1, min(4 n_pages, 256)] at each call.  Results do not depend on it beyond
+   rounding. */
 int kvq_set_decode_splits(kvq_cache *cache, int32_t splits);
 
 /* The page split count the next kvq_decode_attention call will use. */

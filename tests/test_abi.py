@@ -155,13 +155,14 @@ def test_decode_split_choice(kvq):
     h, c = _handle(kvq, max_pages=64)
     kvq.kvq_set_state(h, 63, 128)
     auto = kvq.kvq_get_decode_splits(h)
-    assert 1 <= auto <= 63
-    for s, want in [(1, 1), (7, 7), (63, 63), (1000, 63)]:
+    groups = 4 * 63  # splits cover 32-token page groups
+    assert 1 <= auto <= min(groups, 256)
+    for s, want in [(1, 1), (7, 7), (63, 63), (100, 100), (1000, 252)]:
         kvq.kvq_set_decode_splits(h, s)
         got = kvq.kvq_get_decode_splits(h)
-        # pages per split = ceil(63 / s); splits = ceil(63 / pages per split)
-        pps = -(-63 // want)
-        assert got == -(-63 // pps)
+        # groups per split = ceil(252 / s); splits = ceil(252 / groups per split)
+        gps = -(-groups // want)
+        assert got == -(-groups // gps)
     kvq.kvq_set_decode_splits(h, 0)
     assert kvq.kvq_get_decode_splits(h) == auto
     kvq.kvq_cache_destroy(h)
