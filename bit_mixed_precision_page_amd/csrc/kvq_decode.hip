@@ -739,20 +739,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
     const int g0 = split * gps;
     const int g1 = min(4 * n_pages, g0 + gps);
     const uint8_t *ubase = cache + (size_t)unit * max_pages * page_bytes;
-    auto rs_of = [&](int gi) { return page_rsrc(ubase + (size_t)(gi >> 2) * page_bytes, page_bytes); };
+    // The prefetch past the split's last group goes through an empty
+    // descriptor: every offset is out of range, so it reads zeros without
+    // touching memory and the number of loads in flight stays static.
+    auto rs_of = [&](int gi) {
+        return page_rsrc(ubase + (size_t)(min(gi, g1 - 1) >> 2) * page_bytes,
+                         gi < g1 ? page_bytes : 0u);
+    };
     GroupRegs<KHE> ga, gb;
     load_group<KH>(ga, rs_of(g0), O, g0 & 3);
     for (int gi = g0;;) {
-        {
-            const int gn = min(gi + 1, g1 - 1);  // the last group is loaded again: harmless
-            load_group<KH>(gb, rs_of(gn), O, gn & 3);
-        }
+        load_group<KH>(gb, rs_of(gi + 1), O, (gi + 1) & 3);
         process(ga);
         if (++gi >= g1) break;
-        {
-            const int gn = min(gi + 1, g1 - 1);
-            load_group<KH>(ga, rs_of(gn), O, gn & 3);
-        }
+        load_group<KH>(ga, rs_of(gi + 1), O, (gi + 1) & 3);
         process(gb);
         if (++gi >= g1) break;
     }

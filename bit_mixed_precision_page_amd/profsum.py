@@ -1,0 +1,112 @@
+"""Turn rocprofv3 CSV output of the decode benchmark into the short text
+summaries kept under profiles/.
+
+  python -m bit_mixed_precision_page_amd.profsum trace DIR WORKLOAD "COMMAND"
+      DIR holds run_kernel_stats.csv of a --kernel-trace --stats run;
+      writes profiles/kernel_trace__WORKLOAD.txt.
+  python -m bit_mixed_precision_page_amd.profsum pmc FETCH_DIR WRITE_DIR WORKLOAD "CMD1" "CMD2" COPY_BYTES
+      FETCH_DIR / WRITE_DIR hold run_counter_collection.csv of a --pmc FETCH_SIZE and a
+      --pmc WRITE_SIZE run of the benchmark; writes
+      profiles/decode_split_kernel__WORKLOAD__pmc.txt (JSON) with the split
+      kernel's HBM bytes per launch.
+
+Counter scaling: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are divided by
+what they read for the runtime's device-to-device copy kernel
+(__amd_rocclr_copyBuffer) on the benchmark's cache replicas, whose size is
+known exactly (one replica per copy, read once and written once; the
+benchmark prints it as "replica bytes").
+"""
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+DECODE_SRC = os.path.join(HERE, "csrc", "kvq_decode.hip")
+SPLIT = "decode_split_kernel"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def short(name):
+    s = name.replace("kvq::(anonymous namespace)::", "").replace("void ", "")
+    return re.sub(r"\(.*", "", s)
+
+
+def trace(d, workload, command):
+    path = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0]
+    rows = list(csv.DictReader(open(path)))
+    lines = ["# rocprofv3 kernel trace summary (durations in microseconds)",
+             f"# workload: {workload}",
+             f"# command: {command}", "",
+             f"{'kernel':<46} {'calls':>6} {'total_us':>11} {'avg_us':>9} {'min_us':>9} "
+             f"{'max_us':>9} {'pct':>6}"]
+    for r in rows:
+        lines.append(f"{short(r['Name']):<46} {int(r['Calls']):>6} "
+                     f"{float(r['TotalDurationNs']) / 1e3:>11.1f} "
+                     f"{float(r['AverageNs']) / 1e3:>9.2f} {float(r['MinNs']) / 1e3:>9.2f} "
+                     f"{float(r['MaxNs']) / 1e3:>9.2f} {float(r['Percentage']):>6.2f}")
+    out = os.path.join(ROOT, "profiles", f"kernel_trace__{workload}.txt")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return out
+
+
+def counter_means(d, counter):
+    """Mean counter value per dispatch of the split kernel and of the copy kernel."""
+    vals = {SPLIT: [], COPY: []}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            for key in vals:
+                if key in r["Kernel_Name"]:
+                    vals[key].append(float(r["Counter_Value"]))
+    for key, v in vals.items():
+        if not v:
+            raise SystemExit(f"no {counter} samples for {key} under {d}")
+    return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+
+def pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, copy_bytes):
+    f, nf = counter_means(fetch_dir, "FETCH_SIZE")
+    w, nw = counter_means(write_dir, "WRITE_SIZE")
+    copy_kib = copy_bytes / 1024.0
+    f_scale = copy_kib / f[COPY]
+    w_scale = copy_kib / w[COPY]
+    fetch_b = f[SPLIT] * f_scale * 1024.0
+    write_b = w[SPLIT] * w_scale * 1024.0
+    rec = {
+        "kernel": SPLIT, "workload": workload,
+        "fetch_kib_per_dispatch_raw": round(f[SPLIT], 1),
+        "write_kib_per_dispatch_raw": round(w[SPLIT], 1),
+        "copy_kernel": COPY, "copy_bytes": copy_bytes,
+        "copy_fetch_kib_raw": round(f[COPY], 1), "copy_write_kib_raw": round(w[COPY], 1),
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "hbm_read_bytes_per_launch": round(fetch_b),
+        "hbm_write_bytes_per_launch": round(write_b),
+        "hbm_bytes_per_launch": round(fetch_b + write_b),
+        "dispatches": {"fetch": nf, "write": nw},
+        "commands": [cmd_fetch, cmd_write],
+        "source_sha256": hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest(),
+    }
+    out = os.path.join(ROOT, "profiles", f"{SPLIT}__{workload}__pmc.txt")
+    open(out, "w").write(json.dumps(rec, indent=1) + "\n")
+    print(json.dumps(rec, indent=1))
+    return out
+
+
+def main(argv):
+    if argv[:1] == ["trace"]:
+        trace(argv[1], argv[2], argv[3])
+    elif argv[:1] == ["pmc"]:
+        pmc(argv[1], argv[2], argv[3], argv[4], argv[5], int(argv[6]))
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
