@@ -3,7 +3,8 @@
 
 One step = one decode step of one attention layer: append the new token's K
 and V into the window (flushing a full window into a page when needed) and
-run split-K decode attention of the new query over the whole cache.  Layers
+run split-K decode attention of the new query over the whole cache, through
+the fused kvq_append_decode entry point (--unfused: the two separate calls).  Layers
 rotate over enough independent cache replicas (>= 1 GiB) that every step
 reads its cache from HBM, not from the 256 MB Infinity Cache.  Inputs are
 seeded synthetic tensors of the workload's shape, resident in HBM before the
@@ -45,6 +46,9 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="page splits (0 = automatic)")
     ap.add_argument("--event-every", type=int, default=4,
                     help="bracket the split kernel with HIP events on every N-th timed step")
+    ap.add_argument("--unfused", action="store_true",
+                    help="step = kvq_append_token + kvq_decode_attention (default: the fused "
+                         "kvq_append_decode, same results)")
     ap.add_argument("--event-fence", action="store_true",
                     help="events with the default system-scope fence (slower markers)")
     return ap.parse_args()
@@ -125,7 +129,7 @@ def main():
 
     w = gen.WORKLOADS[a.workload]
     if w.decode_steps:
-        raise SystemExit("the long streaming workload is a parity case, not a bench line")
+        return stream_main(a, w, torch, gen, kvq)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -186,8 +190,11 @@ def main():
         c = caches[li]
         if ev is not None:
             kvq.kvq_set_kernel_events(c.handle, ev[0], ev[1])
-        flushed = c.append_token(kts[s], vts[s])
-        c.decode_attention(qs[s], out)
+        if a.unfused:
+            flushed = c.append_token(kts[s], vts[s])
+            c.decode_attention(qs[s], out)
+        else:
+            flushed = c.append_decode(kts[s], vts[s], qs[s], out)
         if ev is not None:
             kvq.kvq_set_kernel_events(c.handle, None, None)
         n_pages, n_res = c.state
@@ -260,7 +267,8 @@ def main():
                    "head_dim": 128, "ctx": w.ctx, "boost_channels": w.boost,
                    "key_group": 32, "value_group": 32, "window": 128,
                    "storage": "2-bit K/V pages + bf16 window",
-                   "layers_rotated": layers, "page_splits": splits},
+                   "layers_rotated": layers, "page_splits": splits,
+                   "step": "append + attention, " + ("two calls" if a.unfused else "fused")},
         "tokens_per_s": round(w.B / (ms_step / 1e3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "attention_gbs": round(attn_gbs, 2),
@@ -268,6 +276,102 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def stream_main(a, w, torch, gen, kvq):
+    """The long-context streaming workload: bulk quantization of the prefill
+    (timed once, after an untimed pass on a scratch cache), then its decode
+    steps, each an append plus a decode attention on every one of L layer
+    replicas in turn (L sized to defeat the Infinity Cache), timed per step."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+
+    bulk = w.prefill_pages
+    print(f"[bench] workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} prefill {bulk} pages, "
+          f"{w.decode_steps} decode steps", file=sys.stderr, flush=True)
+    K, V = gen.prefill_kv(w, ntok=bulk * PAGE)
+    Kd, Vd = to_dev(K), to_dev(V)
+    del K, V
+    cfg = kvq.config(w.B, w.Hq, w.Hkv, w.boost, w.max_pages, w.dtype)
+    scratch = kvq.Cache(cfg, device=dev)
+    scratch.quantize_page(Kd, Vd, bulk)
+    base = kvq.Cache(cfg, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    base.quantize_page(Kd, Vd, bulk)
+    e1.record()
+    torch.cuda.synchronize()
+    q_ms = e0.elapsed_time(e1)
+    pb = base.page_bytes
+    units = w.B * w.Hkv
+    q_in = units * bulk * PAGE * 128 * 2 * 2
+    q_out = units * bulk * pb
+    del scratch, Kd, Vd
+    layers = max(2, math.ceil(a.rotate_bytes / base.nbytes))
+    caches = [base]
+    for _ in range(layers - 1):
+        c = kvq.Cache(cfg, device=dev)
+        c.mem.copy_(base.mem)
+        kvq.kvq_set_state(c.handle, bulk, 0)
+        caches.append(c)
+    qs, kts, vts = [], [], []
+    for s in range(1, w.decode_steps + 1):
+        qs.append(to_dev(gen.query(w, step=s)))
+        kt, vt = gen.step_kv(w, s)
+        kts.append(to_dev(kt))
+        vts.append(to_dev(vt))
+    out = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(w.decode_steps)]
+    torch.cuda.synchronize()
+    flush_step = None
+    bytes_steps = []
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(w.decode_steps):
+        evs[i][0].record()
+        for c in caches:
+            if a.unfused:
+                flushed = c.append_token(kts[i], vts[i])
+                c.decode_attention(qs[i], out)
+            else:
+                flushed = c.append_decode(kts[i], vts[i], qs[i], out)
+        evs[i][1].record()
+        if flushed:
+            flush_step = i + 1
+        n_pages, n_res = caches[0].state
+        bytes_steps.append(attention_bytes(w, pb, n_pages, n_res) + append_bytes(w, pb, flushed))
+    end.record()
+    torch.cuda.synchronize()
+    step_ms = np.array([x.elapsed_time(y) for x, y in evs]) / layers  # per layer step
+    total_ms = start.elapsed_time(end)
+    value = float(np.sum(bytes_steps)) * layers / (total_ms / 1e3) / 1e9
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": w.decode_steps, "warmup": 0,
+        "ms_per_step": round(total_ms / w.decode_steps / layers, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": 128, "ctx": bulk * PAGE, "decode_steps": w.decode_steps,
+                   "boost_channels": w.boost, "layers_rotated": layers,
+                   "step": "append + attention, " + ("two calls" if a.unfused else "fused")},
+        "tokens_per_s": round(w.B / (total_ms / w.decode_steps / layers / 1e3), 1),
+        "step_us": {"p10": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
+                    "median": round(float(np.median(step_ms)) * 1e3, 2),
+                    "p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
+                    "flush_step": flush_step,
+                    "flush_step_us": round(float(step_ms[flush_step - 1]) * 1e3, 2)
+                    if flush_step else None},
+        "prefill_quantize": {"pages": units * bulk, "ms": round(q_ms, 3),
+                             "gbs": round((q_in + q_out) / (q_ms / 1e3) / 1e9, 1)},
+        "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)
 

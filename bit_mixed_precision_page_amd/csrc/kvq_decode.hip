@@ -268,7 +268,9 @@ constexpr int waves_target(int G, int KH) {
 
 template <int DT, int G, int KH>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target(G, KH)))) void decode_split_kernel(
-    const uint8_t *__restrict__ cache, const uint16_t *__restrict__ q, float *__restrict__ ws_ml,
+    const uint8_t *__restrict__ cache, uint8_t *__restrict__ window_w,
+    const uint16_t *__restrict__ knew, const uint16_t *__restrict__ vnew, int slot,
+    const uint16_t *__restrict__ q, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, int Hkv, int max_pages, uint32_t page_bytes, int k,
     size_t res_base, int n_pages, int n_res, int page_splits, int gps, int win_splits, int max_splits,
     float qscale) {
@@ -324,17 +326,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
         for (int i = 0; i < QCH; i++)
             qraw[i] = *reinterpret_cast<const uint4 *>(qg + 8 * min(lane + 64 * i, G * (D / 8) - 1));
         // lane (token tl, half hs) holds channels 64 hs + [0, 64) of its token
+        // A fused append hands the newest token (window slot `slot`) in knew /
+        // vnew: it is read from there and stored into its slot by this split.
+        const uint16_t *kn = knew + (size_t)unit * D, *vn = vnew + (size_t)unit * D;
         uint4 kr[D / 16];
         {
-            const uint4 *row =
-                reinterpret_cast<const uint4 *>(kw + (size_t)(t0 + min(tl, nt - 1)) * D + 64 * hs);
+            const int tk = t0 + min(tl, nt - 1);
+            const uint4 *row = reinterpret_cast<const uint4 *>(
+                (tk == slot ? kn : kw + (size_t)tk * D) + 64 * hs);
 #pragma unroll
             for (int c8 = 0; c8 < D / 16; c8++) kr[c8] = row[c8];
         }
         uint32_t vr[32];
 #pragma unroll
-        for (int t = 0; t < 32; t++)
-            vr[t] = *reinterpret_cast<const uint32_t *>(vw + (size_t)(t0 + min(t, nt - 1)) * D + 2 * lane);
+        for (int t = 0; t < 32; t++) {
+            const int tv = t0 + min(t, nt - 1);
+            vr[t] = *reinterpret_cast<const uint32_t *>((tv == slot ? vn : vw + (size_t)tv * D) +
+                                                        2 * lane);
+        }
+        if (slot >= t0 && slot < t0 + nt && lane < 32) {
+            uint16_t *dst = reinterpret_cast<uint16_t *>(window_w + res_base +
+                                                         (size_t)unit * 2 * R * D * 2) +
+                            (lane < 16 ? 0 : (size_t)R * D) + (size_t)slot * D + 8 * (lane & 15);
+            *reinterpret_cast<uint4 *>(dst) =
+                *reinterpret_cast<const uint4 *>((lane < 16 ? kn : vn) + 8 * (lane & 15));
+        }
 
         float(*qf)[D] = reinterpret_cast<float(*)[D]>(lds);
         float(*sw)[G] = reinterpret_cast<float(*)[G]>(lds + G * D * 4);  // [token][head]
@@ -862,10 +878,12 @@ int slots3() {
 }
 
 template <int DT, int G, int KH>
-hipError_t launch3(const Geometry &Gm, const uint8_t *cache, const uint16_t *q, float *ml,
-                   float *acc, const DecodePlan &pl, hipStream_t st) {
+hipError_t launch3(const Geometry &Gm, uint8_t *cache, const uint16_t *kn, const uint16_t *vn,
+                   int slot, const uint16_t *q, float *ml, float *acc, const DecodePlan &pl,
+                   hipStream_t st) {
     dim3 grid(pl.total_splits * Gm.Hkv * Gm.B);
-    hipLaunchKernelGGL((decode_split_kernel<DT, G, KH>), grid, dim3(64), 0, st, cache, q, ml,
+    hipLaunchKernelGGL((decode_split_kernel<DT, G, KH>), grid, dim3(64), 0, st, cache, cache,
+                       kn, vn, slot, q, ml,
                        acc, Gm.Hkv, Gm.max_pages, Gm.page_bytes, Gm.k, Gm.res_base,
                        pl.n_pages, pl.n_res, pl.page_splits, pl.groups_per_split,
                        pl.total_splits - pl.page_splits,
@@ -874,27 +892,29 @@ hipError_t launch3(const Geometry &Gm, const uint8_t *cache, const uint16_t *q, 
 }
 
 template <int DT, int G>
-hipError_t launch2(const Geometry &Gm, const uint8_t *cache, const uint16_t *q, float *ml,
-                   float *acc, const DecodePlan &pl, hipStream_t st) {
+hipError_t launch2(const Geometry &Gm, uint8_t *cache, const uint16_t *kn, const uint16_t *vn,
+                   int slot, const uint16_t *q, float *ml, float *acc, const DecodePlan &pl,
+                   hipStream_t st) {
     switch ((Gm.k + 31) / 32) {
-        case 0: return launch3<DT, G, 0>(Gm, cache, q, ml, acc, pl, st);
-        case 1: return launch3<DT, G, 1>(Gm, cache, q, ml, acc, pl, st);
-        case 2: return launch3<DT, G, 2>(Gm, cache, q, ml, acc, pl, st);
-        case 3: return launch3<DT, G, 3>(Gm, cache, q, ml, acc, pl, st);
-        case 4: return launch3<DT, G, 4>(Gm, cache, q, ml, acc, pl, st);
+        case 0: return launch3<DT, G, 0>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
+        case 1: return launch3<DT, G, 1>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
+        case 2: return launch3<DT, G, 2>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
+        case 3: return launch3<DT, G, 3>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
+        case 4: return launch3<DT, G, 4>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int DT>
-hipError_t launch1(const Geometry &Gm, const uint8_t *cache, const uint16_t *q, float *ml,
-                   float *acc, const DecodePlan &pl, hipStream_t st) {
+hipError_t launch1(const Geometry &Gm, uint8_t *cache, const uint16_t *kn, const uint16_t *vn,
+                   int slot, const uint16_t *q, float *ml, float *acc, const DecodePlan &pl,
+                   hipStream_t st) {
     switch (Gm.g) {
-        case 1: return launch2<DT, 1>(Gm, cache, q, ml, acc, pl, st);
-        case 2: return launch2<DT, 2>(Gm, cache, q, ml, acc, pl, st);
-        case 4: return launch2<DT, 4>(Gm, cache, q, ml, acc, pl, st);
-        case 8: return launch2<DT, 8>(Gm, cache, q, ml, acc, pl, st);
-        case 16: return launch2<DT, 16>(Gm, cache, q, ml, acc, pl, st);
+        case 1: return launch2<DT, 1>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
+        case 2: return launch2<DT, 2>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
+        case 4: return launch2<DT, 4>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
+        case 8: return launch2<DT, 8>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
+        case 16: return launch2<DT, 16>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -931,15 +951,17 @@ size_t decode_workspace_bytes(const Geometry &G, int max_splits) {
     return rows * 2 * sizeof(float) + rows * D * sizeof(float);
 }
 
-hipError_t launch_decode(const Geometry &G, const uint8_t *cache, const uint16_t *q,
+hipError_t launch_decode(const Geometry &G, uint8_t *cache, const uint16_t *q,
                          float *out, void *workspace, const DecodePlan &pl,
+                         const uint16_t *kn, const uint16_t *vn, int slot,
                          hipEvent_t ev_before, hipEvent_t ev_after, hipStream_t st) {
+    if (slot < 0) kn = vn = q;  // never dereferenced: no window token equals slot -1
     float *ml = reinterpret_cast<float *>(workspace);
     float *acc = ml + (size_t)G.B * G.Hq * pl.max_splits * 2;
     hipError_t e;
     if (ev_before && (e = hipEventRecord(ev_before, st)) != hipSuccess) return e;
-    e = G.dtype == F16 ? launch1<F16>(G, cache, q, ml, acc, pl, st)
-                       : launch1<BF16>(G, cache, q, ml, acc, pl, st);
+    e = G.dtype == F16 ? launch1<F16>(G, cache, kn, vn, slot, q, ml, acc, pl, st)
+                       : launch1<BF16>(G, cache, kn, vn, slot, q, ml, acc, pl, st);
     if (e != hipSuccess) return e;
     if (ev_after && (e = hipEventRecord(ev_after, st)) != hipSuccess) return e;
     if (pl.total_splits > kMaxCombine) return hipErrorInvalidValue;

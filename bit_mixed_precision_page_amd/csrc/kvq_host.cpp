@@ -23,6 +23,7 @@ struct kvq_cache {
 namespace {
 
 constexpr int kMaxSplits = 256;  // page splits per (sequence, KV head)
+constexpr int kRoundGroups = 32;  // groups per split when one round of waves cannot hold every unit
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -81,10 +82,14 @@ kvq::DecodePlan plan_of(const kvq_cache *c) {
             S = c->splits_override;
         } else {
             // One round of resident single-wave workgroups (occupancy of this
-            // kernel instance x compute units), shared with the window splits.
+            // kernel instance x compute units), shared with the window
+            // splits, with equal groups per split.  When the units alone fill
+            // more than a round, splits of about kRoundGroups groups run in
+            // several rounds and the hardware's dispatch balances them.
             int units = c->G.B * c->G.Hkv;
             int win = (c->n_res + 31) / 32;
-            S = std::max(1, kvq::decode_slots(c->G) / units - win);
+            int per_unit = kvq::decode_slots(c->G) / units - win;
+            S = per_unit >= 1 ? per_unit : (4 * c->n_pages + kRoundGroups - 1) / kRoundGroups;
         }
         const int groups = 4 * c->n_pages;
         S = std::max(1, std::min(S, std::min(groups, kMaxSplits)));
@@ -197,8 +202,38 @@ int kvq_decode_attention(kvq_cache *c, const void *q, float *out, void *workspac
     if (c->n_pages == 0 && c->n_res == 0) return KVQ_EEMPTY;
     kvq::DecodePlan pl = plan_of(c);
     return hip_status(kvq::launch_decode(c->G, c->mem, static_cast<const uint16_t *>(q), out,
-                                         workspace, pl, c->ev_before, c->ev_after,
-                                         static_cast<hipStream_t>(stream)));
+                                         workspace, pl, nullptr, nullptr, -1, c->ev_before,
+                                         c->ev_after, static_cast<hipStream_t>(stream)));
+}
+
+int kvq_append_decode(kvq_cache *c, const void *k, const void *v, const void *q, float *out,
+                      void *workspace, size_t ws_bytes, void *stream, int32_t *flushed) {
+    if (!c || !k || !v || !q || !out || !workspace) return KVQ_EINVAL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(out) ||
+        !aligned16(workspace))
+        return KVQ_EALIGN;
+    if (ws_bytes < kvq::decode_workspace_bytes(c->G, max_splits_of(c->G)))
+        return KVQ_EWORKSPACE;
+    bool flush = c->n_res == kvq::R;
+    if (flush && c->n_pages >= c->G.max_pages) return KVQ_ECAPACITY;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (flush) {
+        hipError_t e = kvq::launch_flush_window(c->G, c->mem, c->n_pages, st);
+        if (e != hipSuccess) return KVQ_EHIP;
+        c->n_pages += 1;
+        c->n_res = 0;
+    }
+    // the plan and the kernel see the window with the new token in it
+    const int slot = c->n_res;
+    c->n_res += 1;
+    kvq::DecodePlan pl = plan_of(c);
+    hipError_t e = kvq::launch_decode(c->G, c->mem, static_cast<const uint16_t *>(q), out,
+                                      workspace, pl, static_cast<const uint16_t *>(k),
+                                      static_cast<const uint16_t *>(v), slot, c->ev_before,
+                                      c->ev_after, st);
+    if (e != hipSuccess) return KVQ_EHIP;
+    if (flushed) *flushed = flush ? 1 : 0;
+    return KVQ_OK;
 }
 
 int kvq_set_decode_splits(kvq_cache *c, int32_t splits) {

@@ -83,8 +83,12 @@ struct DecodePlan {
 size_t decode_workspace_bytes(const Geometry &G, int max_splits);
 // Workgroups of the decode kernel the device holds at once (2048 without a device).
 int decode_slots(const Geometry &G);
-hipError_t launch_decode(const Geometry &G, const uint8_t *cache, const uint16_t *q,
+// knew, vnew ([B][Hkv][D]) and slot >= 0: the newest window token (slot) is
+// read from knew / vnew and written into the window by the kernel itself (a
+// fused append); slot = -1: the window is read as it is.
+hipError_t launch_decode(const Geometry &G, uint8_t *cache, const uint16_t *q,
                          float *out, void *workspace, const DecodePlan &plan,
+                         const uint16_t *knew, const uint16_t *vnew, int slot,
                          hipEvent_t ev_before, hipEvent_t ev_after, hipStream_t stream);
 
 }  // namespace kvq

@@ -21,7 +21,8 @@ ERRORS = {-1: "KVQ_EINVAL", -2: "KVQ_ECAPACITY", -3: "KVQ_ESTATE", -4: "KVQ_EEMP
           -5: "KVQ_EWORKSPACE", -6: "KVQ_EALIGN", -7: "KVQ_EHIP"}
 EXPORTS = ["kvq_cache_bytes", "kvq_page_bytes", "kvq_cache_create", "kvq_cache_destroy",
            "kvq_quantize_page", "kvq_append_token", "kvq_decode_workspace_bytes",
-           "kvq_decode_attention", "kvq_set_decode_splits", "kvq_get_decode_splits",
+           "kvq_decode_attention", "kvq_append_decode", "kvq_set_decode_splits",
+           "kvq_get_decode_splits",
            "kvq_get_state", "kvq_set_state", "kvq_page_offset", "kvq_residual_offset",
            "kvq_quantize_groups", "kvq_set_kernel_events", "kvq_strerror"]
 
@@ -64,6 +65,7 @@ _SIG = {
     "kvq_append_token": [_vp, _vp, _vp, _vp, ctypes.POINTER(_i32)],
     "kvq_decode_workspace_bytes": [_vp, ctypes.POINTER(_sz)],
     "kvq_decode_attention": [_vp, _vp, _vp, _vp, _sz, _vp],
+    "kvq_append_decode": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, ctypes.POINTER(_i32)],
     "kvq_set_decode_splits": [_vp, _i32],
     "kvq_get_decode_splits": [_vp, ctypes.POINTER(_i32)],
     "kvq_get_state": [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
@@ -149,6 +151,13 @@ def kvq_decode_attention(handle, q, out, workspace, ws_bytes, stream=None):
                                    _stream(stream)), "kvq_decode_attention")
 
 
+def kvq_append_decode(handle, k, v, q, out, workspace, ws_bytes, stream=None):
+    f = _i32()
+    _check(_L.kvq_append_decode(handle, _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(workspace),
+                                ws_bytes, _stream(stream), ctypes.byref(f)), "kvq_append_decode")
+    return bool(f.value)
+
+
 def kvq_set_decode_splits(handle, splits):
     _check(_L.kvq_set_decode_splits(handle, splits), "kvq_set_decode_splits")
 
@@ -216,6 +225,9 @@ class Cache:
 
     def decode_attention(self, q, out, stream=None):
         kvq_decode_attention(self.handle, q, out, self.ws, self.ws_bytes, stream)
+
+    def append_decode(self, k, v, q, out, stream=None):
+        return kvq_append_decode(self.handle, k, v, q, out, self.ws, self.ws_bytes, stream)
 
     @property
     def state(self):

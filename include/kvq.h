@@ -138,6 +138,16 @@ int kvq_decode_workspace_bytes(const kvq_cache *cache, size_t *bytes);
 int kvq_decode_attention(kvq_cache *cache, const void *q, float *out, void *workspace,
                          size_t ws_bytes, void *stream);
 
+/* One decode step in fewer launches (NEXT-2 of the design: fused append and
+   decode): exactly kvq_append_token(k, v, &flushed) followed by
+   kvq_decode_attention(q, out, ...), with the same arguments, results (cache
+   bytes and output, bit for bit) and error codes, checked before any launch.
+   The new token is read from k, v and stored into its window slot by the
+   attention kernel itself, so no separate append kernel runs; a full window
+   is still flushed into a page first (one extra launch, as in the append). */
+int kvq_append_decode(kvq_cache *cache, const void *k, const void *v, const void *q, float *out,
+                      void *workspace, size_t ws_bytes, void *stream, int32_t *flushed);
+
 /* Number of page splits per (sequence, KV head) decode attention uses; a
    split covers consecutive 32-token page groups.  splits = 0 restores the
    automatic choice (one round of resident waves); otherwise it is clamped to

@@ -28,9 +28,10 @@ def declared_symbols():
 
 def test_header_declares_the_abi():
     syms = declared_symbols()
-    for name in ("kvq_quantize_page", "kvq_append_token", "kvq_decode_attention"):
+    for name in ("kvq_quantize_page", "kvq_append_token", "kvq_decode_attention",
+                 "kvq_append_decode"):
         assert name in syms
-    assert len(syms) >= 17
+    assert len(syms) >= 18
 
 
 def test_library_exports_every_declared_symbol(kvq):
@@ -128,6 +129,16 @@ def test_call_errors_leave_state_unchanged(kvq):
         kvq.kvq_append_token(h, FAKE, FAKE, 0)
     assert e.value.name == "KVQ_ECAPACITY"
     assert kvq.kvq_get_state(h) == (4, 128)
+    # the fused step checks like the two calls it replaces, before any launch
+    for args, name in [((FAKE, FAKE, FAKE, FAKE, FAKE, ws), "KVQ_ECAPACITY"),
+                       ((FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1), "KVQ_EWORKSPACE"),
+                       ((FAKE, FAKE + 2, FAKE, FAKE, FAKE, ws), "KVQ_EALIGN"),
+                       ((FAKE, FAKE, FAKE, FAKE + 4, FAKE, ws), "KVQ_EALIGN"),
+                       ((FAKE, 0, FAKE, FAKE, FAKE, ws), "KVQ_EINVAL")]:
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_append_decode(h, *args, 0)
+        assert e.value.name == name
+        assert kvq.kvq_get_state(h) == (4, 128)
     # counters
     for bad in [(-1, 0), (5, 0), (0, 129), (0, -1)]:
         with pytest.raises(kvq.KvqError):

@@ -160,3 +160,34 @@ def test_snapshot_restore():
     c2.decode_attention(dev(q), out)
     torch.cuda.synchronize()
     assert (host(out) == a).all()
+
+
+def test_fused_append_decode_equals_two_calls():
+    """kvq_append_decode is kvq_append_token + kvq_decode_attention bit for bit
+    (output, page and window bytes), across a window flush; the two-call cache
+    follows the oracle."""
+    w = W["llama3_8b_decode"]
+    fused = Pair(w, B=2, bulk_pages=2, window=126, with_oracle=False)
+    ref = Pair(w, B=2, bulk_pages=2, window=126)
+    for step in range(4):  # window 127, 128, then flush + 1, 2
+        kt, vt = gen.step_kv(w, 500 + step)
+        kt, vt = kt[:2], vt[:2]
+        q = ref.query(step)
+        out = torch.empty(2, w.Hq, 128, dtype=torch.float32, device="cuda")
+        f1 = fused.gpu.append_decode(dev(kt), dev(vt), dev(q), out)
+        torch.cuda.synchronize()
+        f2 = ref.append(kt, vt)
+        assert f1 == f2 == (step == 2)
+        assert fused.gpu.state == ref.gpu.state
+        got = host(out)
+        assert (got == ref.attention(q)).all(), f"step {step}: fused output differs"
+        n_pages = ref.ora.n_pages  # pages past the written ones are uninitialized in both
+        assert (fused.pages()[:, :, :n_pages] == ref.pages()[:, :, :n_pages]).all()
+        kf, vf = fused.windows()
+        kr, vr = ref.windows()
+        n = ref.ora.n_res
+        assert (kf[:, :, :n] == kr[:, :, :n]).all() and (vf[:, :, :n] == vr[:, :, :n]).all()
+        check_pages(ref)
+        err = np.abs(got - ref.ora.attention(q)).max()
+        say(f"    step {step}: fused == two calls; max |gpu - oracle| = {err:.3e}")
+        assert err <= TOL
