@@ -21,8 +21,8 @@
 //      duplicate work.  Boosted channels (Kitty abstract: two uniform 2-bit
 //      planes per mixed-precision Key page) add a contraction of the hi plane
 //      against 4 w of the listed channels.  The zero-point term q . z per
-//      group and head comes from a small MFMA of q (split into three pieces of
-//      the cache dtype) against the group's Key zeros.
+//      group and head is a VALU dot product: each lane holds q' of eight
+//      channels for its row's head, and a row sum over 16 lanes finishes it.
 //  PV  (16 rows = 4 heads x 4 Value groups) x (32 tokens x 16 channels): the
 //      A operand is p * s_v (softmax weight times the token's Value scale for
 //      the group), split hi/lo; p reaches that layout through a 512-byte LDS
@@ -282,8 +282,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
     constexpr int O_Q = 0;                                // u16 [G][D] raw q
     constexpr int O_WL = O_Q + G * D * 2;                 // u4 [HQ][4 m][2 x][4 R][4 kb] lo-plane weights
     constexpr int O_WH = O_WL + HQ * 4 * 32 * 16;         // u32 [HQ][KHE][2 x][4 R][4 kb][4] hi plane
-    constexpr int O_BQ = O_WH + HQ * KHE * 2 * 16 * 16;   // u4 [HQ][4 m][64 lanes] q pieces
-    constexpr int O_ST = O_BQ + HQ * 4 * 64 * 16;         // f32 [384] K scale 2^E | V scale | V zero
+    constexpr int O_ST = O_WH + HQ * KHE * 2 * 16 * 16;   // f32 [384] K scale 2^E | V scale | V zero
     constexpr int O_KZ = O_ST + 384 * 4;                  // u16 [D] K zero of the group
     constexpr int O_PX = O_KZ + D * 2;                    // f32 [HQ][4][32] softmax weights
     constexpr int PAGE_LDS = O_PX + HQ * 4 * 32 * 4;
@@ -478,34 +477,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
                                        : 1.0f / (float)(1 << (2 * code_sig(e >> 1)));
             qpp[s][e] = qv(hh, pcb + (e >> 1) + 8 * (e & 1)) * sig;
         }
-    // q split into three pieces of the cache dtype: A operand of the zero-point
-    // MFMA, row 4 R + piece (piece 3 zero), channel 32 m + 8 kb + e.
+    // q' of channels 8 r + [0, 8) for the head of row kb: the zero-point term
+    float qz[HQ][8];
 #pragma unroll
-    for (int s = 0; s < HQ; s++) {
-        const int hh = head_of<G>(pR, s);
-        uint32_t pw[3][4];
+    for (int s = 0; s < HQ; s++)
 #pragma unroll
-        for (int e2 = 0; e2 < 4; e2++) {
-            uint16_t pv[3][2];
-#pragma unroll
-            for (int u = 0; u < 2; u++) {
-                const float x = qv(hh, 32 * pm + 8 * pkb + 2 * e2 + u);
-                const uint16_t p0 = enc<DT>(x);
-                const float r1 = x - dec<DT>(p0);
-                const uint16_t p1 = enc<DT>(r1);
-                const float r2 = r1 - dec<DT>(p1);
-                pv[0][u] = p0;
-                pv[1][u] = p1;
-                pv[2][u] = enc<DT>(r2);
-            }
-#pragma unroll
-            for (int pc = 0; pc < 3; pc++) pw[pc][e2] = (uint32_t)pv[pc][0] | ((uint32_t)pv[pc][1] << 16);
-        }
-        u4_t *bq = reinterpret_cast<u4_t *>(lds + O_BQ) + (s * 4 + pm) * 64 + 16 * pkb + 4 * pR;
-#pragma unroll
-        for (int pc = 0; pc < 3; pc++) bq[pc] = u4_t{pw[pc][0], pw[pc][1], pw[pc][2], pw[pc][3]};
-        bq[3] = u4_t{0, 0, 0, 0};
-    }
+        for (int e = 0; e < 8; e++) qz[s][e] = qv(head_of<G>(kb, s), 8 * r + e);
 
     // Hi-plane producer role: k block hkb, row block hR, operand dword hq; its
     // boosted slots are j0 = 32 ms + 16 (hkb / 2) + 4 (hkb % 2) + hq and j0 + 8,
@@ -636,18 +613,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
                     wh[64] = lo;
                 }
             }
-            // ---- zero-point term per head: q pieces x K zero on the matrix cores ----
+            // ---- zero-point term per head: q' . K zero, eight channels per lane ----
             float bias[HQ];
+            {
+                const u4_t zr = *reinterpret_cast<const u4_t *>(kz + 8 * r);
+                float zf[8];
 #pragma unroll
-            for (int s = 0; s < HQ; s++) {
-                f4_t cb = {0, 0, 0, 0};
+                for (int e = 0; e < 8; e++) zf[e] = dec<DT>((uint16_t)(zr[e >> 1] >> (16 * (e & 1))));
 #pragma unroll
-                for (int m = 0; m < 4; m++) {
-                    const u4_t a = reinterpret_cast<const u4_t *>(lds + O_BQ)[(s * 4 + m) * 64 + lane];
-                    const u4_t z = *reinterpret_cast<const u4_t *>(kz + 32 * m + 8 * kb);
-                    cb = mfma_dt<DT>(a, z, cb);
+                for (int s = 0; s < HQ; s++) {
+                    float t = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) t = fmaf(qz[s][e], zf[e], t);
+                    bias[s] = row_sum(t);
                 }
-                bias[s] = cb[0] + cb[1] + cb[2];
             }
             wave_sync();
 
