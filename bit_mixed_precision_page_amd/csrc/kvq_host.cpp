@@ -4,9 +4,11 @@
 // any launch so a failed call leaves the cache unchanged.
 #include "../../include/kvq.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <new>
+#include <vector>
 
 #include "kvq_internal.h"
 
@@ -17,6 +19,20 @@ struct kvq_cache {
     int32_t n_pages;
     int32_t n_res;
     int32_t splits_override;  // 0 = automatic
+    hipEvent_t ev_before, ev_after;
+};
+
+// Block pool: host state of every sequence slot and the free list.
+struct kvq_pool {
+    kvq::Geometry G;  // B = slots, max_pages = pages per sequence, res_base = windows
+    uint8_t *mem;
+    size_t bytes;
+    size_t table_off;
+    int32_t n_blocks;
+    std::vector<uint8_t> live;
+    std::vector<int32_t> n_pages, n_res;
+    std::vector<std::vector<int32_t>> blocks;
+    std::vector<int32_t> free_list;  // back() is handed out next
     hipEvent_t ev_before, ev_after;
 };
 
@@ -101,6 +117,122 @@ kvq::DecodePlan plan_of(const kvq_cache *c) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
+
+// ---------------------------------------------------------------- pool ----
+constexpr int kPoolMaxPages = 65535;  // page counts travel as 16-bit values
+constexpr int kPoolMaxKvHeads = 63;   // window workgroup prefix sums fit 16 bits
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_pool_config(const kvq_config *c, int32_t n_blocks) {
+    int rc = check_config(c);
+    if (rc) return rc;
+    if (c->batch > kvq::kPoolMaxSeqs || c->max_pages > kPoolMaxPages ||
+        c->num_kv_heads > kPoolMaxKvHeads || n_blocks < 1)
+        return KVQ_EINVAL;
+    return KVQ_OK;
+}
+
+// Geometry of a pool plus the byte offsets of its windows and table.
+kvq::Geometry pool_geometry(const kvq_config *c, int32_t n_blocks, size_t *table_off,
+                            size_t *total) {
+    kvq::Geometry G = geometry_of(c);
+    const size_t blocks = (size_t)n_blocks * G.Hkv * G.page_bytes;
+    G.res_base = align256(blocks);
+    const size_t win = (size_t)G.B * G.Hkv * 2 * kvq::R * kvq::D * 2;
+    *table_off = align256(G.res_base + win);
+    *total = *table_off + (size_t)G.B * G.max_pages * sizeof(int32_t);
+    return G;
+}
+
+int32_t *pool_table(kvq_pool *p) { return reinterpret_cast<int32_t *>(p->mem + p->table_off); }
+
+// Split plan of one decode launch over the live sequences (slot_of[b] >= 0:
+// the fused append's window slot of sequence b).
+kvq::PoolPlan pool_plan(const kvq_pool *p, const int *slot_of) {
+    const kvq::Geometry &G = p->G;
+    kvq::PoolPlan pl{};
+    pl.n_seq = G.B;
+    pl.max_splits = max_splits_of(G);
+    int64_t unit_groups = 0;
+    int units_with_pages = 0, max_groups = 0, win_wgs = 0;
+    for (int b = 0; b < G.B; b++) {
+        if (!p->live[b]) continue;
+        unit_groups += (int64_t)4 * p->n_pages[b] * G.Hkv;
+        units_with_pages += p->n_pages[b] > 0 ? G.Hkv : 0;
+        max_groups = std::max(max_groups, 4 * p->n_pages[b]);
+        win_wgs += G.Hkv * ((p->n_res[b] + 31) / 32);
+    }
+    // One round of resident waves shared with the window splits, equal
+    // groups per split across all sequences; several rounds of about
+    // kRoundGroups groups when the units alone fill more than a round.
+    int gps = 1;
+    if (units_with_pages > 0) {
+        const int target = kvq::pool_decode_slots(G) - win_wgs;
+        if (target >= units_with_pages)
+            gps = (int)std::max<int64_t>(1, (unit_groups + target - 1) / target);
+        else
+            gps = kRoundGroups;
+        gps = std::max(gps, (max_groups + kMaxSplits - 1) / kMaxSplits);
+    }
+    pl.gps = gps;
+    pl.page_pref[0] = 0;
+    pl.win_pref[0] = 0;
+    for (int b = 0; b < G.B; b++) {
+        const bool on = p->live[b] != 0;
+        const int S = on ? (4 * p->n_pages[b] + gps - 1) / gps : 0;
+        const int W = on ? (p->n_res[b] + 31) / 32 : 0;
+        pl.page_pref[b + 1] = pl.page_pref[b] + (uint32_t)(G.Hkv * S);
+        pl.win_pref[b + 1] = (uint16_t)(pl.win_pref[b] + G.Hkv * W);
+        pl.n_pages[b] = (uint16_t)(on ? p->n_pages[b] : 0);
+        pl.n_res[b] = (uint8_t)(on ? p->n_res[b] : 0);
+        pl.slot[b] = (uint8_t)(on && slot_of && slot_of[b] >= 0 ? slot_of[b] : kvq::kPoolNoSlot);
+    }
+    for (int b = G.B; b < kvq::kPoolMaxSeqs; b++) {
+        pl.page_pref[b + 1] = pl.page_pref[b];
+        pl.win_pref[b + 1] = pl.win_pref[b];
+    }
+    pl.page_wgs = (int)pl.page_pref[G.B];
+    return pl;
+}
+
+// Flush every live sequence whose window is full into a new block (checks
+// first; nothing changes on error).  *n receives the number of flushes.
+int pool_flush_full(kvq_pool *p, hipStream_t st, int32_t *n) {
+    const kvq::Geometry &G = p->G;
+    int need = 0;
+    for (int b = 0; b < G.B; b++) {
+        if (!p->live[b] || p->n_res[b] != kvq::R) continue;
+        if (p->n_pages[b] >= G.max_pages) return KVQ_ECAPACITY;
+        need++;
+    }
+    if (need > (int)p->free_list.size()) return KVQ_ECAPACITY;
+    *n = need;
+    if (need == 0) return KVQ_OK;
+    kvq::PoolPages pp{};
+    pp.n = 0;
+    for (int b = 0; b < G.B; b++) {
+        if (!p->live[b] || p->n_res[b] != kvq::R) continue;
+        const int32_t blk = p->free_list[p->free_list.size() - 1 - pp.n];
+        pp.block[pp.n] = blk;
+        pp.tslot[pp.n] = b * G.max_pages + p->n_pages[b];
+        pp.src[pp.n] = b;
+        pp.n++;
+    }
+    const uint16_t *kw = reinterpret_cast<const uint16_t *>(p->mem + G.res_base);
+    hipError_t e = kvq::launch_pool_pages(G, p->mem, pool_table(p), kw, kw + (size_t)kvq::R * kvq::D,
+                                          (size_t)2 * kvq::R * kvq::D,
+                                          (size_t)G.Hkv * 2 * kvq::R * kvq::D, pp, st);
+    if (e != hipSuccess) return KVQ_EHIP;
+    for (int e2 = 0; e2 < pp.n; e2++) {
+        const int b = pp.src[e2];
+        p->free_list.pop_back();
+        p->blocks[b].push_back(pp.block[e2]);
+        p->n_pages[b] += 1;
+        p->n_res[b] = 0;
+    }
+    return KVQ_OK;
+}
 
 }  // namespace
 
@@ -298,6 +430,230 @@ int kvq_set_kernel_events(kvq_cache *c, void *before, void *after) {
     if ((before == nullptr) != (after == nullptr)) return KVQ_EINVAL;
     c->ev_before = static_cast<hipEvent_t>(before);
     c->ev_after = static_cast<hipEvent_t>(after);
+    return KVQ_OK;
+}
+
+int kvq_pool_bytes(const kvq_config *cfg, int32_t n_blocks, size_t *bytes) {
+    int rc = check_pool_config(cfg, n_blocks);
+    if (rc) return rc;
+    if (!bytes) return KVQ_EINVAL;
+    size_t table_off, total;
+    pool_geometry(cfg, n_blocks, &table_off, &total);
+    *bytes = total;
+    return KVQ_OK;
+}
+
+int kvq_pool_create(const kvq_config *cfg, int32_t n_blocks, void *dev_mem, size_t bytes,
+                    kvq_pool **out) {
+    int rc = check_pool_config(cfg, n_blocks);
+    if (rc) return rc;
+    if (!out || !dev_mem) return KVQ_EINVAL;
+    if (!aligned16(dev_mem)) return KVQ_EALIGN;
+    size_t table_off, total;
+    kvq::Geometry G = pool_geometry(cfg, n_blocks, &table_off, &total);
+    if (bytes < total) return KVQ_EINVAL;
+    kvq_pool *p = new (std::nothrow) kvq_pool;
+    if (!p) return KVQ_EINVAL;
+    try {
+        p->G = G;
+        p->mem = static_cast<uint8_t *>(dev_mem);
+        p->bytes = bytes;
+        p->table_off = table_off;
+        p->n_blocks = n_blocks;
+        p->live.assign(G.B, 0);
+        p->n_pages.assign(G.B, 0);
+        p->n_res.assign(G.B, 0);
+        p->blocks.assign(G.B, std::vector<int32_t>());
+        p->free_list.resize(n_blocks);
+        for (int32_t i = 0; i < n_blocks; i++) p->free_list[i] = n_blocks - 1 - i;
+        p->ev_before = nullptr;
+        p->ev_after = nullptr;
+    } catch (...) {
+        delete p;
+        return KVQ_EINVAL;
+    }
+    *out = p;
+    return KVQ_OK;
+}
+
+int kvq_pool_destroy(kvq_pool *pool) {
+    if (!pool) return KVQ_EINVAL;
+    delete pool;
+    return KVQ_OK;
+}
+
+int kvq_pool_prefill(kvq_pool *p, int32_t seq, const void *k, const void *v, int32_t n_tokens,
+                     void *stream) {
+    if (!p || seq < 0 || seq >= p->G.B || n_tokens < 0) return KVQ_EINVAL;
+    if (n_tokens > 0 && (!k || !v)) return KVQ_EINVAL;
+    if (n_tokens > 0 && (!aligned16(k) || !aligned16(v))) return KVQ_EALIGN;
+    if (p->live[seq]) return KVQ_ESTATE;
+    const kvq::Geometry &G = p->G;
+    const int n_full = n_tokens / kvq::P, tail = n_tokens % kvq::P;
+    if (n_full > G.max_pages || n_full > (int)p->free_list.size()) return KVQ_ECAPACITY;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::vector<int32_t> got;
+    try {
+        got.assign(p->free_list.end() - n_full, p->free_list.end());
+    } catch (...) {
+        return KVQ_EINVAL;
+    }
+    std::reverse(got.begin(), got.end());  // handed out from the back of the list
+    const uint16_t *ks = static_cast<const uint16_t *>(k), *vs = static_cast<const uint16_t *>(v);
+    for (int c0 = 0; c0 < n_full; c0 += kvq::kPoolMaxSeqs) {
+        kvq::PoolPages pp{};
+        pp.n = std::min(kvq::kPoolMaxSeqs, n_full - c0);
+        for (int e = 0; e < pp.n; e++) {
+            pp.block[e] = got[c0 + e];
+            pp.tslot[e] = seq * G.max_pages + c0 + e;
+            pp.src[e] = c0 + e;
+        }
+        hipError_t e = kvq::launch_pool_pages(G, p->mem, pool_table(p), ks, vs,
+                                              (size_t)n_tokens * kvq::D,
+                                              (size_t)kvq::P * kvq::D, pp, st);
+        if (e != hipSuccess) return KVQ_EHIP;
+    }
+    hipError_t e = kvq::launch_pool_window_fill(G, p->mem, ks, vs, seq, n_tokens,
+                                                n_full * kvq::P, tail, st);
+    if (e != hipSuccess) return KVQ_EHIP;
+    p->free_list.resize(p->free_list.size() - n_full);
+    p->blocks[seq] = got;
+    p->n_pages[seq] = n_full;
+    p->n_res[seq] = tail;
+    p->live[seq] = 1;
+    return KVQ_OK;
+}
+
+int kvq_pool_append(kvq_pool *p, const void *k, const void *v, void *stream,
+                    int32_t *n_flushed) {
+    if (!p || !k || !v) return KVQ_EINVAL;
+    if (!aligned16(k) || !aligned16(v)) return KVQ_EALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t nf = 0;
+    int rc = pool_flush_full(p, st, &nf);
+    if (rc) return rc;
+    kvq::PoolSlots ps{};
+    for (int b = 0; b < kvq::kPoolMaxSeqs; b++)
+        ps.slot[b] = (uint8_t)(b < p->G.B && p->live[b] ? p->n_res[b] : kvq::kPoolNoSlot);
+    hipError_t e = kvq::launch_pool_append(p->G, p->mem, static_cast<const uint16_t *>(k),
+                                           static_cast<const uint16_t *>(v), ps, st);
+    if (e != hipSuccess) return KVQ_EHIP;
+    for (int b = 0; b < p->G.B; b++)
+        if (p->live[b]) p->n_res[b] += 1;
+    if (n_flushed) *n_flushed = nf;
+    return KVQ_OK;
+}
+
+int kvq_pool_decode_workspace_bytes(const kvq_pool *p, size_t *bytes) {
+    if (!p || !bytes) return KVQ_EINVAL;
+    *bytes = kvq::decode_workspace_bytes(p->G, max_splits_of(p->G));
+    return KVQ_OK;
+}
+
+int kvq_pool_decode_attention(kvq_pool *p, const void *q, float *out, void *workspace,
+                              size_t ws_bytes, void *stream) {
+    if (!p || !q || !out || !workspace) return KVQ_EINVAL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_EALIGN;
+    if (ws_bytes < kvq::decode_workspace_bytes(p->G, max_splits_of(p->G)))
+        return KVQ_EWORKSPACE;
+    const kvq::PoolPlan pl = pool_plan(p, nullptr);
+    return hip_status(kvq::launch_pool_decode(p->G, p->mem, pool_table(p),
+                                              static_cast<const uint16_t *>(q), out, workspace,
+                                              pl, nullptr, nullptr, p->ev_before, p->ev_after,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int kvq_pool_append_decode(kvq_pool *p, const void *k, const void *v, const void *q, float *out,
+                           void *workspace, size_t ws_bytes, void *stream, int32_t *n_flushed) {
+    if (!p || !k || !v || !q || !out || !workspace) return KVQ_EINVAL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(out) ||
+        !aligned16(workspace))
+        return KVQ_EALIGN;
+    if (ws_bytes < kvq::decode_workspace_bytes(p->G, max_splits_of(p->G)))
+        return KVQ_EWORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t nf = 0;
+    int rc = pool_flush_full(p, st, &nf);
+    if (rc) return rc;
+    // the plan and the kernel see every window with its new token in it
+    int slot_of[kvq::kPoolMaxSeqs];
+    for (int b = 0; b < p->G.B; b++) {
+        slot_of[b] = p->live[b] ? p->n_res[b] : -1;
+        if (p->live[b]) p->n_res[b] += 1;
+    }
+    const kvq::PoolPlan pl = pool_plan(p, slot_of);
+    hipError_t e = kvq::launch_pool_decode(p->G, p->mem, pool_table(p),
+                                           static_cast<const uint16_t *>(q), out, workspace, pl,
+                                           static_cast<const uint16_t *>(k),
+                                           static_cast<const uint16_t *>(v), p->ev_before,
+                                           p->ev_after, st);
+    if (e != hipSuccess) return KVQ_EHIP;
+    if (n_flushed) *n_flushed = nf;
+    return KVQ_OK;
+}
+
+int kvq_pool_release(kvq_pool *p, int32_t seq) {
+    if (!p || seq < 0 || seq >= p->G.B) return KVQ_EINVAL;
+    if (!p->live[seq]) return KVQ_ESTATE;
+    std::vector<int32_t> &bl = p->blocks[seq];
+    for (auto it = bl.rbegin(); it != bl.rend(); ++it) p->free_list.push_back(*it);
+    bl.clear();
+    p->live[seq] = 0;
+    p->n_pages[seq] = 0;
+    p->n_res[seq] = 0;
+    return KVQ_OK;
+}
+
+int kvq_pool_get_seq(const kvq_pool *p, int32_t seq, int32_t *live, int32_t *n_pages,
+                     int32_t *n_res) {
+    if (!p || seq < 0 || seq >= p->G.B) return KVQ_EINVAL;
+    if (live) *live = p->live[seq];
+    if (n_pages) *n_pages = p->n_pages[seq];
+    if (n_res) *n_res = p->n_res[seq];
+    return KVQ_OK;
+}
+
+int kvq_pool_block_of(const kvq_pool *p, int32_t seq, int32_t page, int32_t *block) {
+    if (!p || !block || seq < 0 || seq >= p->G.B || !p->live[seq] || page < 0 ||
+        page >= p->n_pages[seq])
+        return KVQ_EINVAL;
+    *block = p->blocks[seq][page];
+    return KVQ_OK;
+}
+
+int kvq_pool_free_blocks(const kvq_pool *p, int32_t *n_free) {
+    if (!p || !n_free) return KVQ_EINVAL;
+    *n_free = (int32_t)p->free_list.size();
+    return KVQ_OK;
+}
+
+int kvq_pool_page_offset(const kvq_pool *p, int32_t block, int32_t h, size_t *off) {
+    if (!p || !off || block < 0 || block >= p->n_blocks || h < 0 || h >= p->G.Hkv)
+        return KVQ_EINVAL;
+    *off = ((size_t)block * p->G.Hkv + h) * p->G.page_bytes;
+    return KVQ_OK;
+}
+
+int kvq_pool_window_offset(const kvq_pool *p, int32_t seq, int32_t h, size_t *k_off,
+                           size_t *v_off) {
+    if (!p || seq < 0 || seq >= p->G.B || h < 0 || h >= p->G.Hkv) return KVQ_EINVAL;
+    const int u = seq * p->G.Hkv + h;
+    if (k_off) *k_off = kvq::res_k_off(p->G, u);
+    if (v_off) *v_off = kvq::res_v_off(p->G, u);
+    return KVQ_OK;
+}
+
+int kvq_pool_table_offset(const kvq_pool *p, size_t *off) {
+    if (!p || !off) return KVQ_EINVAL;
+    *off = p->table_off;
+    return KVQ_OK;
+}
+
+int kvq_pool_set_kernel_events(kvq_pool *p, void *before, void *after) {
+    if (!p) return KVQ_EINVAL;
+    if ((before == nullptr) != (after == nullptr)) return KVQ_EINVAL;
+    p->ev_before = static_cast<hipEvent_t>(before);
+    p->ev_after = static_cast<hipEvent_t>(after);
     return KVQ_OK;
 }
 

@@ -91,4 +91,55 @@ hipError_t launch_decode(const Geometry &G, uint8_t *cache, const uint16_t *q,
                          const uint16_t *knew, const uint16_t *vnew, int slot,
                          hipEvent_t ev_before, hipEvent_t ev_after, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// Block pool (variable-length batches).  A block holds the Hkv pages of one
+// 128-token span of one sequence; sequence b's page p is block
+// table[b * max_pages + p].  Per-launch lists travel by value in the kernel
+// arguments (no host-to-device copies): at most kPoolMaxSeqs entries.
+constexpr int kPoolMaxSeqs = 256;
+constexpr int kPoolNoSlot = 255;
+
+// Pages to quantize into pool blocks: entry e writes block[e] (all KV heads),
+// records it at table[tslot[e]], and reads its rows at element
+// src[e] * src_e_stride + h * src_h_stride of the sources.
+struct PoolPages {
+    int n;
+    int32_t block[kPoolMaxSeqs];
+    int32_t tslot[kPoolMaxSeqs];
+    int32_t src[kPoolMaxSeqs];
+};
+// Window slot of the token each sequence takes (kPoolNoSlot: none).
+struct PoolSlots {
+    uint8_t slot[kPoolMaxSeqs];
+};
+// Decode work of a variable-length batch: sequence b owns Hkv * S_b page-split
+// workgroups [page_pref[b], page_pref[b + 1]) and Hkv * W_b window workgroups
+// [page_wgs + win_pref[b], page_wgs + win_pref[b + 1]), S_b = ceil(4 n_pages / gps),
+// W_b = ceil(n_res / 32).
+struct PoolPlan {
+    int n_seq, page_wgs, gps, max_splits;
+    uint32_t page_pref[kPoolMaxSeqs + 1];
+    uint16_t win_pref[kPoolMaxSeqs + 1];
+    uint16_t n_pages[kPoolMaxSeqs];
+    uint8_t n_res[kPoolMaxSeqs];
+    uint8_t slot[kPoolMaxSeqs];  // fused append: window slot of the new token, or kPoolNoSlot
+};
+
+// G describes the pool: B = sequence slots, max_pages = pages per sequence,
+// res_base = byte offset of the windows ([B][Hkv][K | V][R][D]).
+hipError_t launch_pool_pages(const Geometry &G, uint8_t *pool, int32_t *table,
+                             const uint16_t *k_src, const uint16_t *v_src, size_t src_h_stride,
+                             size_t src_e_stride, const PoolPages &pp, hipStream_t stream);
+hipError_t launch_pool_append(const Geometry &G, uint8_t *mem, const uint16_t *k,
+                              const uint16_t *v, const PoolSlots &ps, hipStream_t stream);
+hipError_t launch_pool_window_fill(const Geometry &G, uint8_t *mem, const uint16_t *k,
+                                   const uint16_t *v, int seq, int n_tokens, int first, int tail,
+                                   hipStream_t stream);
+int pool_decode_slots(const Geometry &G);
+// knew / vnew ([B][Hkv][D]) are read for the sequences whose plan slot is set.
+hipError_t launch_pool_decode(const Geometry &G, uint8_t *mem, const int32_t *table,
+                              const uint16_t *q, float *out, void *workspace, const PoolPlan &pl,
+                              const uint16_t *knew, const uint16_t *vnew, hipEvent_t ev_before,
+                              hipEvent_t ev_after, hipStream_t stream);
+
 }  // namespace kvq

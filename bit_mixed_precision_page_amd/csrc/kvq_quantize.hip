@@ -67,11 +67,11 @@ __device__ __forceinline__ uint32_t quant_code(float x, float zf, float inv, int
     return (uint32_t)r;
 }
 
+// One page: K and V rows [P][D] at ks / vs, the packed page written to pg.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void quantize_pages_kernel(
-    uint8_t *__restrict__ cache, const uint16_t *__restrict__ k_src,
-    const uint16_t *__restrict__ v_src, size_t src_unit_stride, int first_page, int n_new,
-    int max_pages, uint32_t page_bytes, int k) {
+__device__ __forceinline__ void quantize_page_body(uint8_t *__restrict__ pg,
+                                                   const uint16_t *__restrict__ ks,
+                                                   const uint16_t *__restrict__ vs, int k) {
     __shared__ __align__(16) uint16_t tile[P * kRowPad];
     __shared__ __align__(16) uint8_t codes[P * D];
     __shared__ uint32_t amax[2][D];
@@ -81,12 +81,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pages_kernel(
     __shared__ uint64_t mask0;
 
     const int tid = threadIdx.x;
-    const int p = blockIdx.x;
-    const int unit = blockIdx.y;
     const PageLayout Ly = page_layout(k);
-    uint8_t *pg = cache + ((size_t)unit * max_pages + first_page + p) * page_bytes;
-    const uint16_t *ks = k_src + (size_t)unit * src_unit_stride + (size_t)p * P * D;
-    const uint16_t *vs = v_src + (size_t)unit * src_unit_stride + (size_t)p * P * D;
 
     // 1. Issue every load of the K and V tiles (16 B per thread per step).
     uint4 kr[8], vr[8];
@@ -244,6 +239,76 @@ __global__ __launch_bounds__(kThreads) void quantize_pages_kernel(
     }
 }
 
+// Dense cache: page first_page + blockIdx.x of unit blockIdx.y.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void quantize_pages_kernel(
+    uint8_t *__restrict__ cache, const uint16_t *__restrict__ k_src,
+    const uint16_t *__restrict__ v_src, size_t src_unit_stride, int first_page, int n_new,
+    int max_pages, uint32_t page_bytes, int k) {
+    const int p = blockIdx.x;
+    const int unit = blockIdx.y;
+    uint8_t *pg = cache + ((size_t)unit * max_pages + first_page + p) * page_bytes;
+    const uint16_t *ks = k_src + (size_t)unit * src_unit_stride + (size_t)p * P * D;
+    const uint16_t *vs = v_src + (size_t)unit * src_unit_stride + (size_t)p * P * D;
+    quantize_page_body<DT>(pg, ks, vs, k);
+}
+
+// Block pool: entry blockIdx.x of the list, KV head blockIdx.y.  The page
+// goes to pool block pp.block[e] (the block holds the Hkv pages of one
+// 128-token span); its source rows start at element
+// pp.src[e] * src_e_stride + h * src_h_stride; the KV-head-0 workgroup
+// records the block in the block table.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void pool_pages_kernel(
+    uint8_t *__restrict__ pool, int32_t *__restrict__ table, const uint16_t *__restrict__ k_src,
+    const uint16_t *__restrict__ v_src, size_t src_h_stride, size_t src_e_stride, int Hkv,
+    uint32_t page_bytes, int k, const PoolPages pp) {
+    const int e = blockIdx.x, h = blockIdx.y;
+    const int blk = pp.block[e];
+    if (h == 0 && threadIdx.x == 0) table[pp.tslot[e]] = blk;
+    uint8_t *pg = pool + ((size_t)blk * Hkv + h) * page_bytes;
+    const size_t so = (size_t)pp.src[e] * src_e_stride + (size_t)h * src_h_stride;
+    quantize_page_body<DT>(pg, k_src + so, v_src + so, k);
+}
+
+// Block pool: copy one token per (sequence, KV head) into window slot
+// ps.slot[sequence] (kPoolNoSlot: the sequence takes no token).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void pool_append_kernel(
+    uint8_t *__restrict__ mem, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    int Hkv, int n_seq, size_t res_base, const PoolSlots ps) {
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    const int per = n_seq * Hkv * 16;
+    if (i >= 2 * per) return;
+    const bool isv = i >= per;
+    const int j = isv ? i - per : i;
+    const int unit = j >> 4, chunk = j & 15;
+    const int slot = ps.slot[unit / Hkv];
+    if (slot == kPoolNoSlot) return;
+    const uint16_t *src = (isv ? v : k) + (size_t)unit * D + chunk * 8;
+    const size_t dst = res_base + (size_t)unit * 2 * R * D * 2 + (isv ? (size_t)R * D * 2 : 0) +
+                       ((size_t)slot * D + chunk * 8) * 2;
+    *reinterpret_cast<uint4 *>(mem + dst) = *reinterpret_cast<const uint4 *>(src);
+}
+
+// Block pool: tokens [first, first + tail) of one sequence's K and V
+// ([Hkv][n_tokens][D]) into window slots [0, tail) of that sequence.
+__global__ __launch_bounds__(kThreads) void pool_window_fill_kernel(
+    uint8_t *__restrict__ mem, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    int seq, int Hkv, int n_tokens, int first, int tail, size_t res_base) {
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    const int per = Hkv * tail * 16;
+    if (i >= 2 * per) return;
+    const bool isv = i >= per;
+    const int j = isv ? i - per : i;
+    const int h = j / (tail * 16), rem = j % (tail * 16);
+    const int t = rem >> 4, chunk = rem & 15;
+    const uint16_t *src = (isv ? v : k) + ((size_t)h * n_tokens + first + t) * D + chunk * 8;
+    const size_t dst = res_base + (size_t)(seq * Hkv + h) * 2 * R * D * 2 +
+                       (isv ? (size_t)R * D * 2 : 0) + ((size_t)t * D + chunk * 8) * 2;
+    *reinterpret_cast<uint4 *>(mem + dst) = *reinterpret_cast<const uint4 *>(src);
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void append_kernel(uint8_t *__restrict__ cache,
                                                           const uint16_t *__restrict__ k,
@@ -319,6 +384,44 @@ hipError_t launch_append(const Geometry &G, uint8_t *cache, const uint16_t *k,
     else
         hipLaunchKernelGGL(append_kernel<BF16>, grid, dim3(kThreads), 0, stream, cache, k, v,
                            units, G.res_base, slot);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_pages(const Geometry &G, uint8_t *pool, int32_t *table,
+                             const uint16_t *k_src, const uint16_t *v_src, size_t src_h_stride,
+                             size_t src_e_stride, const PoolPages &pp, hipStream_t stream) {
+    if (pp.n <= 0) return hipSuccess;
+    dim3 grid(pp.n, G.Hkv);
+    if (G.dtype == F16)
+        hipLaunchKernelGGL(pool_pages_kernel<F16>, grid, dim3(kThreads), 0, stream, pool, table,
+                           k_src, v_src, src_h_stride, src_e_stride, G.Hkv, G.page_bytes, G.k, pp);
+    else
+        hipLaunchKernelGGL(pool_pages_kernel<BF16>, grid, dim3(kThreads), 0, stream, pool, table,
+                           k_src, v_src, src_h_stride, src_e_stride, G.Hkv, G.page_bytes, G.k, pp);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_append(const Geometry &G, uint8_t *mem, const uint16_t *k,
+                              const uint16_t *v, const PoolSlots &ps, hipStream_t stream) {
+    const int n = 2 * G.B * G.Hkv * 16;
+    dim3 grid((n + kThreads - 1) / kThreads);
+    if (G.dtype == F16)
+        hipLaunchKernelGGL(pool_append_kernel<F16>, grid, dim3(kThreads), 0, stream, mem, k, v,
+                           G.Hkv, G.B, G.res_base, ps);
+    else
+        hipLaunchKernelGGL(pool_append_kernel<BF16>, grid, dim3(kThreads), 0, stream, mem, k, v,
+                           G.Hkv, G.B, G.res_base, ps);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_window_fill(const Geometry &G, uint8_t *mem, const uint16_t *k,
+                                   const uint16_t *v, int seq, int n_tokens, int first, int tail,
+                                   hipStream_t stream) {
+    if (tail <= 0) return hipSuccess;
+    const int n = 2 * G.Hkv * tail * 16;
+    hipLaunchKernelGGL(pool_window_fill_kernel, dim3((n + kThreads - 1) / kThreads),
+                       dim3(kThreads), 0, stream, mem, k, v, seq, G.Hkv, n_tokens, first, tail,
+                       G.res_base);
     return hipGetLastError();
 }
 

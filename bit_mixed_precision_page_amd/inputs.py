@@ -20,7 +20,8 @@ HEAD_DIM = 128
 PAGE = 128
 RESIDUAL = 128
 
-ROLE_CHANNELS, ROLE_K, ROLE_V, ROLE_Q, ROLE_STEP_K, ROLE_STEP_V, ROLE_STEP_Q = range(7)
+(ROLE_CHANNELS, ROLE_K, ROLE_V, ROLE_Q, ROLE_STEP_K, ROLE_STEP_V, ROLE_STEP_Q,
+ ROLE_LENGTHS) = range(8)
 
 
 @dataclass(frozen=True)
@@ -37,6 +38,7 @@ class Workload:
     outliers: int = 0   # outlier channels per KV head ("outlier")
     outlier_gain: float = 1.0
     decode_steps: int = 0  # streaming steps after the prefill
+    ctx_spread: int = 0    # variable-length batch: lengths uniform in ctx +- ctx_spread
 
     @property
     def seed(self):
@@ -60,7 +62,7 @@ class Workload:
 
     @property
     def max_pages(self):
-        return (self.ctx + self.decode_steps) // PAGE + 1
+        return (self.ctx + self.ctx_spread + self.decode_steps) // PAGE + 1
 
 
 WORKLOADS = {
@@ -71,6 +73,8 @@ WORKLOADS = {
         Workload("llama70b_large_batch", 4, 128, 64, 8, 4096, 16, BF16, "outlier", 6, 8.0),
         Workload("long_prefill_decode", 5, 1, 32, 8, 131072, 16, BF16, "student_t",
                  decode_steps=256),
+        Workload("llama3_8b_varlen", 6, 16, 32, 8, 8192, 16, BF16, "outlier", 6, 8.0,
+                 ctx_spread=7168),
     ]
 }
 
@@ -133,6 +137,14 @@ def prefill_kv(w, ntok=None):
         for h in range(w.Hkv):
             K[b, h], V[b, h] = unit_kv(w, b, h, ntok)
     return K, V
+
+
+def seq_lengths(w):
+    """Tokens per sequence [B] (int): uniform in [ctx - ctx_spread, ctx + ctx_spread]."""
+    if not w.ctx_spread:
+        return np.full(w.B, w.ctx, np.int64)
+    r = rng(w.seed, ROLE_LENGTHS)
+    return r.integers(w.ctx - w.ctx_spread, w.ctx + w.ctx_spread + 1, size=w.B)
 
 
 def query(w, step=None):

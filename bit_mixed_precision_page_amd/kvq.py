@@ -24,7 +24,12 @@ EXPORTS = ["kvq_cache_bytes", "kvq_page_bytes", "kvq_cache_create", "kvq_cache_d
            "kvq_decode_attention", "kvq_append_decode", "kvq_set_decode_splits",
            "kvq_get_decode_splits",
            "kvq_get_state", "kvq_set_state", "kvq_page_offset", "kvq_residual_offset",
-           "kvq_quantize_groups", "kvq_set_kernel_events", "kvq_strerror"]
+           "kvq_quantize_groups", "kvq_set_kernel_events", "kvq_strerror",
+           "kvq_pool_bytes", "kvq_pool_create", "kvq_pool_destroy", "kvq_pool_prefill",
+           "kvq_pool_append", "kvq_pool_decode_workspace_bytes", "kvq_pool_decode_attention",
+           "kvq_pool_append_decode", "kvq_pool_release", "kvq_pool_get_seq",
+           "kvq_pool_block_of", "kvq_pool_free_blocks", "kvq_pool_page_offset",
+           "kvq_pool_window_offset", "kvq_pool_table_offset", "kvq_pool_set_kernel_events"]
 
 
 class KvqError(RuntimeError):
@@ -74,6 +79,23 @@ _SIG = {
     "kvq_residual_offset": [_vp, _i32, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)],
     "kvq_quantize_groups": [_i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp],
     "kvq_set_kernel_events": [_vp, _vp, _vp],
+    "kvq_pool_bytes": [_cfgp, _i32, ctypes.POINTER(_sz)],
+    "kvq_pool_create": [_cfgp, _i32, _vp, _sz, ctypes.POINTER(_vp)],
+    "kvq_pool_destroy": [_vp],
+    "kvq_pool_prefill": [_vp, _i32, _vp, _vp, _i32, _vp],
+    "kvq_pool_append": [_vp, _vp, _vp, _vp, ctypes.POINTER(_i32)],
+    "kvq_pool_decode_workspace_bytes": [_vp, ctypes.POINTER(_sz)],
+    "kvq_pool_decode_attention": [_vp, _vp, _vp, _vp, _sz, _vp],
+    "kvq_pool_append_decode": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, ctypes.POINTER(_i32)],
+    "kvq_pool_release": [_vp, _i32],
+    "kvq_pool_get_seq": [_vp, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+                         ctypes.POINTER(_i32)],
+    "kvq_pool_block_of": [_vp, _i32, _i32, ctypes.POINTER(_i32)],
+    "kvq_pool_free_blocks": [_vp, ctypes.POINTER(_i32)],
+    "kvq_pool_page_offset": [_vp, _i32, _i32, ctypes.POINTER(_sz)],
+    "kvq_pool_window_offset": [_vp, _i32, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)],
+    "kvq_pool_table_offset": [_vp, ctypes.POINTER(_sz)],
+    "kvq_pool_set_kernel_events": [_vp, _vp, _vp],
 }
 for _name, _args in _SIG.items():
     _f = getattr(_L, _name)
@@ -204,6 +226,103 @@ def kvq_strerror(code):
     return _L.kvq_strerror(code).decode()
 
 
+# -- block pool (variable-length batches) ---------------------------------------
+def kvq_pool_bytes(cfg, n_blocks):
+    n = _sz()
+    _check(_L.kvq_pool_bytes(ctypes.byref(cfg), n_blocks, ctypes.byref(n)), "kvq_pool_bytes")
+    return n.value
+
+
+def kvq_pool_create(cfg, n_blocks, dev_mem, nbytes):
+    h = _vp()
+    _check(_L.kvq_pool_create(ctypes.byref(cfg), n_blocks, _ptr(dev_mem), nbytes,
+                              ctypes.byref(h)), "kvq_pool_create")
+    return h.value
+
+
+def kvq_pool_destroy(handle):
+    _check(_L.kvq_pool_destroy(handle), "kvq_pool_destroy")
+
+
+def kvq_pool_prefill(handle, seq, k, v, n_tokens, stream=None):
+    _check(_L.kvq_pool_prefill(handle, seq, _ptr(k), _ptr(v), n_tokens, _stream(stream)),
+           "kvq_pool_prefill")
+
+
+def kvq_pool_append(handle, k, v, stream=None):
+    f = _i32()
+    _check(_L.kvq_pool_append(handle, _ptr(k), _ptr(v), _stream(stream), ctypes.byref(f)),
+           "kvq_pool_append")
+    return f.value
+
+
+def kvq_pool_decode_workspace_bytes(handle):
+    n = _sz()
+    _check(_L.kvq_pool_decode_workspace_bytes(handle, ctypes.byref(n)),
+           "kvq_pool_decode_workspace_bytes")
+    return n.value
+
+
+def kvq_pool_decode_attention(handle, q, out, workspace, ws_bytes, stream=None):
+    _check(_L.kvq_pool_decode_attention(handle, _ptr(q), _ptr(out), _ptr(workspace), ws_bytes,
+                                        _stream(stream)), "kvq_pool_decode_attention")
+
+
+def kvq_pool_append_decode(handle, k, v, q, out, workspace, ws_bytes, stream=None):
+    f = _i32()
+    _check(_L.kvq_pool_append_decode(handle, _ptr(k), _ptr(v), _ptr(q), _ptr(out),
+                                     _ptr(workspace), ws_bytes, _stream(stream),
+                                     ctypes.byref(f)), "kvq_pool_append_decode")
+    return f.value
+
+
+def kvq_pool_release(handle, seq):
+    _check(_L.kvq_pool_release(handle, seq), "kvq_pool_release")
+
+
+def kvq_pool_get_seq(handle, seq):
+    a, b, c = _i32(), _i32(), _i32()
+    _check(_L.kvq_pool_get_seq(handle, seq, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
+           "kvq_pool_get_seq")
+    return bool(a.value), b.value, c.value
+
+
+def kvq_pool_block_of(handle, seq, page):
+    b = _i32()
+    _check(_L.kvq_pool_block_of(handle, seq, page, ctypes.byref(b)), "kvq_pool_block_of")
+    return b.value
+
+
+def kvq_pool_free_blocks(handle):
+    n = _i32()
+    _check(_L.kvq_pool_free_blocks(handle, ctypes.byref(n)), "kvq_pool_free_blocks")
+    return n.value
+
+
+def kvq_pool_page_offset(handle, block, h):
+    o = _sz()
+    _check(_L.kvq_pool_page_offset(handle, block, h, ctypes.byref(o)), "kvq_pool_page_offset")
+    return o.value
+
+
+def kvq_pool_window_offset(handle, seq, h):
+    ko, vo = _sz(), _sz()
+    _check(_L.kvq_pool_window_offset(handle, seq, h, ctypes.byref(ko), ctypes.byref(vo)),
+           "kvq_pool_window_offset")
+    return ko.value, vo.value
+
+
+def kvq_pool_table_offset(handle):
+    o = _sz()
+    _check(_L.kvq_pool_table_offset(handle, ctypes.byref(o)), "kvq_pool_table_offset")
+    return o.value
+
+
+def kvq_pool_set_kernel_events(handle, before, after):
+    _check(_L.kvq_pool_set_kernel_events(handle, _ptr(before), _ptr(after)),
+           "kvq_pool_set_kernel_events")
+
+
 # -- convenience owner of the device buffers -----------------------------------
 class Cache:
     """Owns a cache's device memory and workspace (torch tensors) and its handle."""
@@ -249,6 +368,75 @@ class Cache:
     def close(self):
         if self.handle:
             kvq_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Pool:
+    """Owns a block pool's device memory and workspace (torch tensors) and its handle."""
+
+    def __init__(self, cfg, n_blocks, device="cuda"):
+        self.cfg = cfg
+        self.n_blocks = n_blocks
+        self.nbytes = kvq_pool_bytes(cfg, n_blocks)
+        self.mem = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        self.handle = kvq_pool_create(cfg, n_blocks, self.mem, self.nbytes)
+        self.ws_bytes = kvq_pool_decode_workspace_bytes(self.handle)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.page_bytes = kvq_page_bytes(cfg)
+
+    def prefill(self, seq, k, v, stream=None):
+        """k, v: [Hkv][n_tokens][128] device tensors of one sequence."""
+        kvq_pool_prefill(self.handle, seq, k, v, int(k.shape[1]), stream)
+
+    def append(self, k, v, stream=None):
+        return kvq_pool_append(self.handle, k, v, stream)
+
+    def decode_attention(self, q, out, stream=None):
+        kvq_pool_decode_attention(self.handle, q, out, self.ws, self.ws_bytes, stream)
+
+    def append_decode(self, k, v, q, out, stream=None):
+        return kvq_pool_append_decode(self.handle, k, v, q, out, self.ws, self.ws_bytes, stream)
+
+    def release(self, seq):
+        kvq_pool_release(self.handle, seq)
+
+    def seq(self, seq):
+        """(live, n_pages, n_res) of one slot."""
+        return kvq_pool_get_seq(self.handle, seq)
+
+    def block_of(self, seq, page):
+        return kvq_pool_block_of(self.handle, seq, page)
+
+    @property
+    def free_blocks(self):
+        return kvq_pool_free_blocks(self.handle)
+
+    def page_view(self, block, h):
+        o = kvq_pool_page_offset(self.handle, block, h)
+        return self.mem[o:o + self.page_bytes]
+
+    def window_view(self, seq, h):
+        """K and V window of (seq, h), each [128][128] as int16 bit patterns."""
+        ko, vo = kvq_pool_window_offset(self.handle, seq, h)
+        n = 128 * 128 * 2
+        return (self.mem[ko:ko + n].view(torch.int16).view(128, 128),
+                self.mem[vo:vo + n].view(torch.int16).view(128, 128))
+
+    def table_view(self):
+        c = self.cfg
+        o = kvq_pool_table_offset(self.handle)
+        return self.mem[o:o + 4 * c.batch * c.max_pages].view(torch.int32).view(c.batch,
+                                                                                 c.max_pages)
+
+    def close(self):
+        if self.handle:
+            kvq_pool_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

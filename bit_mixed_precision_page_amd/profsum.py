@@ -4,11 +4,12 @@ summaries kept under profiles/.
   python -m bit_mixed_precision_page_amd.profsum trace DIR WORKLOAD "COMMAND"
       DIR holds run_kernel_stats.csv of a --kernel-trace --stats run;
       writes profiles/kernel_trace__WORKLOAD.txt.
-  python -m bit_mixed_precision_page_amd.profsum pmc FETCH_DIR WRITE_DIR WORKLOAD "CMD1" "CMD2" COPY_BYTES
+  python -m bit_mixed_precision_page_amd.profsum pmc FETCH_DIR WRITE_DIR WORKLOAD "CMD1" "CMD2" COPY_BYTES [KERNEL]
       FETCH_DIR / WRITE_DIR hold run_counter_collection.csv of a --pmc FETCH_SIZE and a
       --pmc WRITE_SIZE run of the benchmark; writes
-      profiles/decode_split_kernel__WORKLOAD__pmc.txt (JSON) with the split
-      kernel's HBM bytes per launch.
+      profiles/KERNEL__WORKLOAD__pmc.txt (JSON) with the split kernel's HBM
+      bytes per launch and the SHA-256 of the sources it was built from
+      (KERNEL: decode_split_kernel, the default, or pool_split_kernel).
 
 Counter scaling: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are divided by
 what they read for the runtime's device-to-device copy kernel
@@ -26,9 +27,17 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-DECODE_SRC = os.path.join(HERE, "csrc", "kvq_decode.hip")
-SPLIT = "decode_split_kernel"
 COPY = "__amd_rocclr_copyBuffer"
+# sources each profiled kernel is built from: a counter record holds only for that code
+KERNEL_SRC = {"decode_split_kernel": ["kvq_decode_core.h", "kvq_decode.hip"],
+              "pool_split_kernel": ["kvq_decode_core.h", "kvq_pool.hip"]}
+
+
+def source_sha256(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SRC[kernel]:
+        h.update(open(os.path.join(HERE, "csrc", f), "rb").read())
+    return h.hexdigest()
 
 
 def short(name):
@@ -55,9 +64,9 @@ def trace(d, workload, command):
     return out
 
 
-def counter_means(d, counter):
+def counter_means(d, counter, split):
     """Mean counter value per dispatch of the split kernel and of the copy kernel."""
-    vals = {SPLIT: [], COPY: []}
+    vals = {split: [], COPY: []}
     for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
@@ -71,18 +80,19 @@ def counter_means(d, counter):
     return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
 
 
-def pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, copy_bytes):
-    f, nf = counter_means(fetch_dir, "FETCH_SIZE")
-    w, nw = counter_means(write_dir, "WRITE_SIZE")
+def pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, copy_bytes,
+        split="decode_split_kernel"):
+    f, nf = counter_means(fetch_dir, "FETCH_SIZE", split)
+    w, nw = counter_means(write_dir, "WRITE_SIZE", split)
     copy_kib = copy_bytes / 1024.0
     f_scale = copy_kib / f[COPY]
     w_scale = copy_kib / w[COPY]
-    fetch_b = f[SPLIT] * f_scale * 1024.0
-    write_b = w[SPLIT] * w_scale * 1024.0
+    fetch_b = f[split] * f_scale * 1024.0
+    write_b = w[split] * w_scale * 1024.0
     rec = {
-        "kernel": SPLIT, "workload": workload,
-        "fetch_kib_per_dispatch_raw": round(f[SPLIT], 1),
-        "write_kib_per_dispatch_raw": round(w[SPLIT], 1),
+        "kernel": split, "workload": workload,
+        "fetch_kib_per_dispatch_raw": round(f[split], 1),
+        "write_kib_per_dispatch_raw": round(w[split], 1),
         "copy_kernel": COPY, "copy_bytes": copy_bytes,
         "copy_fetch_kib_raw": round(f[COPY], 1), "copy_write_kib_raw": round(w[COPY], 1),
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
@@ -91,9 +101,9 @@ def pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, copy_bytes):
         "hbm_bytes_per_launch": round(fetch_b + write_b),
         "dispatches": {"fetch": nf, "write": nw},
         "commands": [cmd_fetch, cmd_write],
-        "source_sha256": hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest(),
+        "source_sha256": source_sha256(split),
     }
-    out = os.path.join(ROOT, "profiles", f"{SPLIT}__{workload}__pmc.txt")
+    out = os.path.join(ROOT, "profiles", f"{split}__{workload}__pmc.txt")
     open(out, "w").write(json.dumps(rec, indent=1) + "\n")
     print(json.dumps(rec, indent=1))
     return out
@@ -103,7 +113,7 @@ def main(argv):
     if argv[:1] == ["trace"]:
         trace(argv[1], argv[2], argv[3])
     elif argv[:1] == ["pmc"]:
-        pmc(argv[1], argv[2], argv[3], argv[4], argv[5], int(argv[6]))
+        pmc(argv[1], argv[2], argv[3], argv[4], argv[5], int(argv[6]), *argv[7:8])
     else:
         raise SystemExit(__doc__)
 

@@ -186,6 +186,95 @@ int kvq_set_kernel_events(kvq_cache *cache, void *before, void *after);
 /* Static description of an error code. */
 const char *kvq_strerror(int code);
 
+/* ------------------------------------------------------------------------
+ * Block pool: variable-length batches (a page pool with a block table, as
+ * in paged attention; Kitty abstract: page-centric layout).
+ *
+ * cfg->batch is the number of sequence slots (at most 256) and
+ * cfg->max_pages the pages one sequence may hold (at most 65535); n_blocks
+ * is the pool capacity.  A block holds the Hkv pages of one 128-token span
+ * of one sequence, in the page layout above.  Device memory (caller-owned,
+ * one region):
+ *   blocks   [n_blocks][Hkv][page_bytes]                 at offset 0
+ *   windows  [batch][Hkv][K_res | V_res][128][128] dtype at kvq_pool_window_offset
+ *   table    [batch][max_pages] int32 block ids           at kvq_pool_table_offset
+ * The library keeps per sequence a live flag, its page count, its window
+ * count and its block list, and hands out blocks from a free list (host
+ * state; the table on the device is written by the library's kernels).
+ * Every call checks everything (arguments, capacity, free blocks) before
+ * its first launch; on error no state changes.
+ * ------------------------------------------------------------------------ */
+typedef struct kvq_pool kvq_pool; /* opaque host handle */
+
+/* Device bytes of a pool with n_blocks blocks (n_blocks >= 1). */
+int kvq_pool_bytes(const kvq_config *cfg, int32_t n_blocks, size_t *bytes);
+
+/* Create a handle over dev_mem (16-byte aligned, >= kvq_pool_bytes).  Every
+   slot starts free (not live) and every block unused.  Errors: KVQ_EINVAL
+   (configuration, batch > 256, max_pages > 65535), KVQ_EALIGN. */
+int kvq_pool_create(const kvq_config *cfg, int32_t n_blocks, void *dev_mem, size_t bytes,
+                    kvq_pool **out);
+int kvq_pool_destroy(kvq_pool *pool); /* frees the host handle only */
+
+/* Start sequence `seq` (a free slot) with n_tokens >= 0 prompt tokens.
+   k, v: device [Hkv][n_tokens][128] dtype, contiguous.  The first
+   128 * floor(n_tokens / 128) tokens become quantized pages in newly taken
+   blocks (kernel quantization, Kitty abstract + KIVI section 3), the rest
+   (< 128) the window.  The slot becomes live.
+   Errors: KVQ_EINVAL (seq out of range, n_tokens < 0, null k/v with
+   n_tokens > 0), KVQ_ESTATE (slot live), KVQ_ECAPACITY (more than
+   max_pages pages or not enough free blocks), KVQ_EALIGN. */
+int kvq_pool_prefill(kvq_pool *pool, int32_t seq, const void *k, const void *v, int32_t n_tokens,
+                     void *stream);
+
+/* Append one token to every live sequence.  k, v: device [batch][Hkv][128]
+   dtype (rows of slots that are not live are not read).  A sequence whose
+   window is full first has it quantized into a new block (flush before
+   insert, as for the dense cache); *n_flushed (optional) receives the number
+   of such sequences.  Errors: KVQ_EINVAL, KVQ_EALIGN, KVQ_ECAPACITY (a flush
+   needs a page beyond max_pages or more blocks than are free). */
+int kvq_pool_append(kvq_pool *pool, const void *k, const void *v, void *stream,
+                    int32_t *n_flushed);
+
+/* Workspace bytes of kvq_pool_decode_attention (split partials; fixed per
+   pool). */
+int kvq_pool_decode_workspace_bytes(const kvq_pool *pool, size_t *bytes);
+
+/* Decode attention of every live sequence over its own pages and window.
+   q: device [batch][Hq][128] dtype; out: device [batch][Hq][128] float32.
+   Rows of slots that are not live, or live without a token, are set to 0.
+   Errors: KVQ_EINVAL, KVQ_EALIGN, KVQ_EWORKSPACE. */
+int kvq_pool_decode_attention(kvq_pool *pool, const void *q, float *out, void *workspace,
+                              size_t ws_bytes, void *stream);
+
+/* kvq_pool_append followed by kvq_pool_decode_attention in fewer launches:
+   the new tokens are read from k, v and written to their window slots by the
+   attention kernel itself.  Same results and errors as the two calls. */
+int kvq_pool_append_decode(kvq_pool *pool, const void *k, const void *v, const void *q,
+                           float *out, void *workspace, size_t ws_bytes, void *stream,
+                           int32_t *n_flushed);
+
+/* End sequence `seq`: its blocks return to the free list, the slot becomes
+   free.  Errors: KVQ_EINVAL (seq out of range), KVQ_ESTATE (slot not live). */
+int kvq_pool_release(kvq_pool *pool, int32_t seq);
+
+/* Host state of slot seq: live flag, pages, window tokens. */
+int kvq_pool_get_seq(const kvq_pool *pool, int32_t seq, int32_t *live, int32_t *n_pages,
+                     int32_t *n_res);
+/* Block holding page `page` of live sequence seq (page < n_pages). */
+int kvq_pool_block_of(const kvq_pool *pool, int32_t seq, int32_t page, int32_t *block);
+/* Blocks not held by any sequence. */
+int kvq_pool_free_blocks(const kvq_pool *pool, int32_t *n_free);
+/* Byte offsets inside the pool memory: page of KV head h in block `block`;
+   window of (seq, h); the block table. */
+int kvq_pool_page_offset(const kvq_pool *pool, int32_t block, int32_t h, size_t *off);
+int kvq_pool_window_offset(const kvq_pool *pool, int32_t seq, int32_t h, size_t *k_off,
+                           size_t *v_off);
+int kvq_pool_table_offset(const kvq_pool *pool, size_t *off);
+
+/* Timing hooks of the pool's split kernel (as kvq_set_kernel_events). */
+int kvq_pool_set_kernel_events(kvq_pool *pool, void *before, void *after);
+
 #ifdef __cplusplus
 }
 #endif

@@ -191,3 +191,75 @@ def test_quantize_groups_argument_checks(kvq):
 def test_strerror(kvq):
     for code in range(-7, 1):
         assert kvq.kvq_strerror(code)
+
+
+# -- block pool ------------------------------------------------------------------
+def _pool(kvq, n_blocks=12, **kw):
+    c = _cfg(kvq, **kw)
+    return kvq.kvq_pool_create(c, n_blocks, FAKE, kvq.kvq_pool_bytes(c, n_blocks)), c
+
+
+def test_pool_layout_and_limits(kvq):
+    c = _cfg(kvq, batch=3, max_pages=5)
+    pb = kvq.kvq_page_bytes(c)
+    n = kvq.kvq_pool_bytes(c, 7)
+    h = kvq.kvq_pool_create(c, 7, FAKE, n)
+    try:
+        assert kvq.kvq_pool_page_offset(h, 0, 0) == 0
+        assert kvq.kvq_pool_page_offset(h, 6, 1) == (6 * 2 + 1) * pb
+        ko, vo = kvq.kvq_pool_window_offset(h, 2, 1)
+        wbase = (7 * 2 * pb + 255) // 256 * 256
+        assert ko == wbase + (2 * 2 + 1) * 2 * 128 * 128 * 2 and vo == ko + 128 * 128 * 2
+        t = kvq.kvq_pool_table_offset(h)
+        assert t % 256 == 0 and t >= wbase + 3 * 2 * 2 * 128 * 128 * 2
+        assert n == t + 3 * 5 * 4
+        assert kvq.kvq_pool_free_blocks(h) == 7
+        assert kvq.kvq_pool_get_seq(h, 2) == (False, 0, 0)
+        for bad in [(7, 0), (-1, 0), (0, 2)]:
+            with pytest.raises(kvq.KvqError):
+                kvq.kvq_pool_page_offset(h, *bad)
+    finally:
+        kvq.kvq_pool_destroy(h)
+    for bad in [dict(batch=257), dict(max_pages=65536), dict(num_kv_heads=64, num_q_heads=64)]:
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_pool_bytes(_cfg(kvq, **bad), 4)
+        assert e.value.name == "KVQ_EINVAL"
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_pool_bytes(c, 0)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_pool_create(c, 7, FAKE + 8, n)
+    assert e.value.name == "KVQ_EALIGN"
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_pool_create(c, 7, FAKE, n - 1)
+
+
+def test_pool_call_errors_leave_state(kvq):
+    h, c = _pool(kvq, n_blocks=3)
+    try:
+        def code(f):
+            with pytest.raises(kvq.KvqError) as e:
+                f()
+            return e.value.name
+        # more pages than max_pages (4) or than free blocks (3): nothing launched
+        assert code(lambda: kvq.kvq_pool_prefill(h, 0, FAKE, FAKE, 5 * 128, stream=0)) == \
+            "KVQ_ECAPACITY"
+        assert code(lambda: kvq.kvq_pool_prefill(h, 0, FAKE, FAKE, 4 * 128, stream=0)) == \
+            "KVQ_ECAPACITY"
+        assert code(lambda: kvq.kvq_pool_prefill(h, 2, FAKE, FAKE, 1, stream=0)) == "KVQ_EINVAL"
+        assert code(lambda: kvq.kvq_pool_prefill(h, 0, FAKE, FAKE, -1, stream=0)) == "KVQ_EINVAL"
+        assert code(lambda: kvq.kvq_pool_prefill(h, 0, FAKE + 8, FAKE, 1, stream=0)) == \
+            "KVQ_EALIGN"
+        assert code(lambda: kvq.kvq_pool_release(h, 0)) == "KVQ_ESTATE"
+        assert code(lambda: kvq.kvq_pool_block_of(h, 0, 0)) == "KVQ_EINVAL"
+        ws = kvq.kvq_pool_decode_workspace_bytes(h)
+        assert code(lambda: kvq.kvq_pool_decode_attention(h, FAKE, FAKE, FAKE, ws - 1,
+                                                          stream=0)) == "KVQ_EWORKSPACE"
+        assert code(lambda: kvq.kvq_pool_append_decode(h, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1,
+                                                       stream=0)) == "KVQ_EWORKSPACE"
+        assert code(lambda: kvq.kvq_pool_append(h, FAKE, FAKE + 4, stream=0)) == "KVQ_EALIGN"
+        assert kvq.kvq_pool_free_blocks(h) == 3
+        assert kvq.kvq_pool_get_seq(h, 0) == (False, 0, 0)
+        with pytest.raises(kvq.KvqError):
+            kvq.kvq_pool_set_kernel_events(h, FAKE, None)
+    finally:
+        kvq.kvq_pool_destroy(h)

@@ -1,0 +1,306 @@
+"""Block pool (variable-length batches, pages behind a block table) through the
+C ABI against the CPU oracle on the same seeded inputs.
+
+The oracle models every sequence as its own one-sequence cache (bulk pages,
+then the window, flush before insert); the pool must hold the same page
+bytes in whatever blocks its table names, the same window bytes, and decode
+attention within max-abs 1e-3 of the oracle's fp64 attention for every live
+sequence (rows of free slots are zero).
+"""
+import concurrent.futures as cf
+import dataclasses
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_mixed_precision_page_amd import inputs as gen
+from gpu_util import dev, host
+
+pytestmark = pytest.mark.gpu
+P = 128
+TOL = 1e-3
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+class PoolPair:
+    """A GPU pool and one oracle cache per live sequence, fed the same tokens."""
+
+    def __init__(self, w, n_blocks, max_pages, scale=0.0):
+        from bit_mixed_precision_page_amd import kvq
+        self.kvq, self.w = kvq, w
+        self.max_pages = max_pages
+        self.cfg = kvq.config(w.B, w.Hq, w.Hkv, w.boost, max_pages, w.dtype, softmax_scale=scale)
+        self.gpu = kvq.Pool(self.cfg, n_blocks)
+        self.scale = scale
+        self.ora = {}      # seq -> OracleCache (B = 1)
+        self.tokens = {}   # seq -> tokens so far
+
+    def prefill(self, seq, n_tokens, oracle_side=True):
+        w = self.w
+        K = np.empty((w.Hkv, n_tokens, 128), np.uint16)
+        V = np.empty_like(K)
+        for h in range(w.Hkv):
+            K[h], V[h] = gen.unit_kv(w, seq, h, n_tokens)
+        self.gpu.prefill(seq, dev(K), dev(V))
+        if oracle_side:
+            o = oracle.OracleCache(w.dtype, 1, w.Hq, w.Hkv, w.boost, self.max_pages,
+                                   scale=self.scale)
+            full = n_tokens // P
+            if full:
+                o.quantize_pages(K[None, :, :full * P], V[None, :, :full * P])
+            for t in range(full * P, n_tokens):
+                o.append(K[None, :, t], V[None, :, t])
+            self.ora[seq] = o
+        self.tokens[seq] = n_tokens
+
+    def release(self, seq):
+        self.gpu.release(seq)
+        self.ora.pop(seq, None)
+        self.tokens.pop(seq, None)
+
+    def step_inputs(self, step):
+        w = self.w
+        r = np.random.default_rng(5000 + step)
+        k = gen.to_bits(r.standard_normal((w.B, w.Hkv, 128), dtype=np.float32), w.dtype)
+        v = gen.to_bits(r.standard_normal((w.B, w.Hkv, 128), dtype=np.float32), w.dtype)
+        q = gen.to_bits(r.standard_normal((w.B, w.Hq, 128), dtype=np.float32), w.dtype)
+        return k, v, q
+
+    def oracle_append(self, k, v):
+        flushed = 0
+        for seq, o in self.ora.items():
+            flushed += int(o.append(k[seq:seq + 1], v[seq:seq + 1]))
+            self.tokens[seq] += 1
+        return flushed
+
+    def check_state(self):
+        torch.cuda.synchronize()
+        table = host(self.gpu.table_view())
+        for seq, o in self.ora.items():
+            live, n_pages, n_res = self.gpu.seq(seq)
+            assert live and (n_pages, n_res) == (o.n_pages, o.n_res), (seq, n_pages, n_res)
+            for p in range(n_pages):
+                blk = self.gpu.block_of(seq, p)
+                assert table[seq, p] == blk
+                for h in range(self.w.Hkv):
+                    got = host(self.gpu.page_view(blk, h))
+                    ref = o.pages[0, h, p]
+                    if not np.array_equal(got, ref):
+                        byte = int(np.flatnonzero(got != ref)[0])
+                        raise AssertionError(f"seq {seq} page {p} block {blk} head {h} byte {byte}")
+            for h in range(self.w.Hkv):
+                kw, vw = self.gpu.window_view(seq, h)
+                assert np.array_equal(host(kw).view(np.uint16)[:n_res], o.kres[0, h, :n_res])
+                assert np.array_equal(host(vw).view(np.uint16)[:n_res], o.vres[0, h, :n_res])
+
+    def check_attention(self, out, q):
+        worst = 0.0
+        for seq in range(self.w.B):
+            o = self.ora.get(seq)
+            if o is None or o.n_pages + o.n_res == 0:
+                assert (out[seq] == 0).all(), seq
+                continue
+            ref = o.attention(q[seq:seq + 1])[0]
+            err = float(np.abs(out[seq] - ref).max())
+            worst = max(worst, err)
+            assert err <= TOL, (seq, err)
+        assert np.isfinite(out).all()
+        return worst
+
+
+def small(dtype, Hq, Hkv, boost):
+    return dataclasses.replace(gen.WORKLOADS["tiny"], B=6, Hq=Hq, Hkv=Hkv, boost=boost,
+                               dtype=dtype)
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,boost", [
+    (gen.F16, 8, 2, 16),    # g = 4
+    (gen.BF16, 16, 2, 32),  # g = 8
+    (gen.BF16, 2, 2, 0),    # g = 1, no boosted channels
+])
+def test_pool_varlen_streaming(dtype, Hq, Hkv, boost):
+    w = small(dtype, Hq, Hkv, boost)
+    say(f"  pool B={w.B} Hq={Hq} Hkv={Hkv} k={boost} dtype={dtype}")
+    pair = PoolPair(w, n_blocks=40, max_pages=12)
+    # scatter the blocks: a first sequence takes blocks, is released, and
+    # later prompts reuse them out of order
+    pair.prefill(1, 512, oracle_side=False)
+    pair.prefill(0, 300)
+    pair.prefill(2, 1)
+    pair.release(1)
+    pair.prefill(3, 128)
+    pair.prefill(4, 1000)
+    pair.prefill(5, 129)
+    assert pair.gpu.free_blocks == 40 - (2 + 1 + 7 + 1)
+    pair.check_state()
+    say("    prefill: pages, table and windows bit-exact")
+    k, v, q = pair.step_inputs(0)
+    out = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    pair.gpu.decode_attention(dev(q), out)
+    torch.cuda.synchronize()
+    say(f"    decode after prefill: max |gpu - oracle| = {pair.check_attention(host(out), q):.3e}")
+    for step in range(1, 141):
+        k, v, q = pair.step_inputs(step)
+        nf = pair.gpu.append(dev(k), dev(v))
+        assert nf == pair.oracle_append(k, v), step
+        if step in (1, 25, 26, 85, 129, 140):
+            pair.check_state()
+            pair.gpu.decode_attention(dev(q), out)
+            torch.cuda.synchronize()
+            err = pair.check_attention(host(out), q)
+            say(f"    step {step} (tokens {sorted(pair.tokens.items())}): max err {err:.3e}")
+
+
+def test_pool_fused_equals_two_calls():
+    """append_decode on one pool == append + decode_attention on a twin pool
+    (same calls, same blocks): identical window bytes and bitwise-equal output."""
+    w = small(gen.BF16, 8, 2, 16)
+    a = PoolPair(w, n_blocks=40, max_pages=12)
+    b = PoolPair(w, n_blocks=40, max_pages=12)
+    for pr in (a, b):
+        pr.prefill(0, 300, oracle_side=False)
+        pr.prefill(3, 127, oracle_side=False)
+        pr.prefill(4, 1000, oracle_side=False)
+    oa = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    ob = torch.empty_like(oa)
+    for step in range(1, 30):
+        k, v, q = a.step_inputs(step)
+        kd, vd, qd = dev(k), dev(v), dev(q)
+        na = a.gpu.append_decode(kd, vd, qd, oa)
+        nb = b.gpu.append(kd, vd)
+        b.gpu.decode_attention(qd, ob)
+        torch.cuda.synchronize()
+        assert na == nb, step
+        assert torch.equal(oa, ob), step
+    for seq in (0, 3, 4):
+        live, n_pages, n_res = a.gpu.seq(seq)
+        assert b.gpu.seq(seq) == (live, n_pages, n_res)
+        for h in range(w.Hkv):
+            for x, y in zip(a.gpu.window_view(seq, h), b.gpu.window_view(seq, h)):
+                assert torch.equal(x[:n_res], y[:n_res])  # slots past n_res hold stale tokens
+
+
+def test_pool_matches_dense_cache():
+    """Uniform lengths: the pool's pages equal the dense cache's byte for
+    byte, and both attentions agree (different split plans: 1e-4)."""
+    from bit_mixed_precision_page_amd import kvq
+    w = dataclasses.replace(gen.WORKLOADS["tiny"], B=4, Hq=8, Hkv=2)
+    n_tok = 1000
+    full, tail = divmod(n_tok, P)
+    pair = PoolPair(w, n_blocks=64, max_pages=10)
+    K = np.empty((w.B, w.Hkv, n_tok, 128), np.uint16)
+    V = np.empty_like(K)
+    for s in range(w.B):
+        for h in range(w.Hkv):
+            K[s, h], V[s, h] = gen.unit_kv(w, s, h, n_tok)
+        pair.gpu.prefill(s, dev(K[s]), dev(V[s]))
+    dense = kvq.Cache(kvq.config(w.B, w.Hq, w.Hkv, w.boost, 10, w.dtype))
+    dense.quantize_page(dev(np.ascontiguousarray(K[:, :, :full * P])),
+                        dev(np.ascontiguousarray(V[:, :, :full * P])), full)
+    for t in range(full * P, n_tok):
+        dense.append_token(dev(K[:, :, t]), dev(V[:, :, t]))
+    torch.cuda.synchronize()
+    dp = host(dense.pages_view())
+    for s in range(w.B):
+        for p in range(full):
+            blk = pair.gpu.block_of(s, p)
+            for h in range(w.Hkv):
+                assert np.array_equal(host(pair.gpu.page_view(blk, h)), dp[s, h, p]), (s, p, h)
+    q = gen.to_bits(np.random.default_rng(3).standard_normal((w.B, w.Hq, 128), dtype=np.float32),
+                    w.dtype)
+    o1 = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    o2 = torch.empty_like(o1)
+    pair.gpu.decode_attention(dev(q), o1)
+    dense.decode_attention(dev(q), o2)
+    torch.cuda.synchronize()
+    err = float((o1 - o2).abs().max())
+    say(f"    pool vs dense: max diff {err:.2e}")
+    assert err <= 1e-4
+
+
+def test_pool_errors_leave_state():
+    """Capacity errors are raised before any launch and change nothing."""
+    from bit_mixed_precision_page_amd import kvq
+    w = small(gen.BF16, 8, 2, 16)
+    pair = PoolPair(w, n_blocks=3, max_pages=4)
+    pair.prefill(0, 256 + 127, oracle_side=False)   # 2 blocks + 127 window
+    pair.prefill(1, 128 + 127, oracle_side=False)   # 1 block + 127 window: pool full
+    k, v, q = pair.step_inputs(1)
+    assert pair.gpu.append(dev(k), dev(v)) == 0     # windows now full
+    with pytest.raises(kvq.KvqError) as e:
+        pair.gpu.append(dev(k), dev(v))             # two flushes, no free block
+    assert e.value.name == "KVQ_ECAPACITY"
+    assert pair.gpu.seq(0) == (True, 2, 128) and pair.gpu.seq(1) == (True, 1, 128)
+    pair.release(1)
+    assert pair.gpu.append(dev(k), dev(v)) == 1     # only sequence 0 is live
+    assert pair.gpu.seq(0) == (True, 3, 1)
+    with pytest.raises(kvq.KvqError):
+        pair.gpu.prefill(0, dev(np.zeros((2, 1, 128), np.uint16)),
+                         dev(np.zeros((2, 1, 128), np.uint16)))
+    torch.cuda.synchronize()
+
+
+def test_pool_full_size_varlen():
+    """The variable-length workload at full size (16 sequences of 1K-15K
+    tokens, 32 query / 8 KV heads, bf16, k = 16): every page of every
+    sequence bit-exact, attention of every sequence against the oracle."""
+    w = gen.WORKLOADS["llama3_8b_varlen"]
+    lengths = [int(x) for x in gen.seq_lengths(w)]
+    say(f"  lengths {lengths}")
+    pair = PoolPair(w, n_blocks=sum(n // P for n in lengths) + 8, max_pages=w.max_pages)
+    # the oracle side in threads: one sequence each
+    order = list(range(w.B))[::-1]
+    for s in order:
+        pair.prefill(s, lengths[s], oracle_side=False)
+    ora = {}
+
+    def build(s):
+        n = lengths[s]
+        K = np.empty((w.Hkv, n, 128), np.uint16)
+        V = np.empty_like(K)
+        for h in range(w.Hkv):
+            K[h], V[h] = gen.unit_kv(w, s, h, n)
+        o = oracle.OracleCache(w.dtype, 1, w.Hq, w.Hkv, w.boost, w.max_pages)
+        full = n // P
+        ol = oracle.lib()
+        for h in range(w.Hkv):
+            for p in range(full):
+                sl = slice(p * P, (p + 1) * P)
+                o.pages[0, h, p], _, _ = ol.quantize_page(w.dtype, w.boost, K[h, sl], V[h, sl])
+        o.n_pages = full
+        tail = n - full * P
+        o.kres[0, :, :tail], o.vres[0, :, :tail] = K[:, full * P:], V[:, full * P:]
+        o.n_res = tail
+        return s, o
+
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        for s, o in ex.map(build, range(w.B)):
+            ora[s] = o
+    pair.ora = ora
+    pair.check_state()
+    say(f"    all {sum(n // P for n in lengths) * w.Hkv} pages and every window bit-exact")
+    q = gen.query(w)
+    out = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    pair.gpu.decode_attention(dev(q), out)
+    torch.cuda.synchronize()
+    got = host(out)
+
+    def att(s):
+        return s, ora[s].attention(q[s:s + 1])[0]
+
+    worst = 0.0
+    with cf.ThreadPoolExecutor(4) as ex:
+        for s, ref in ex.map(att, range(w.B)):
+            err = float(np.abs(got[s] - ref).max())
+            worst = max(worst, err)
+            assert err <= TOL, (s, err)
+    say(f"    attention of all {w.B} sequences: max |gpu - oracle| = {worst:.3e}")
