@@ -51,6 +51,15 @@
  *  R8  attention: softmax(scale * q . k) over every page token (dequantized)
  *      and every residual token (exact), no mask, scale = 1/sqrt(128) unless
  *      given; query head hq reads KV head hq / (Hq / Hkv).
+ *  R18 query-aware channel ranking (MixKVQ abstract, fugumt, arXiv
+ *      2512.19206: a Key channel needs high precision according to its
+ *      intrinsic quantization difficulty and its relevance to the query).
+ *      Difficulty of channel c on a page = the sum of its four Key-group
+ *      ranges, (r0 + r1) + (r2 + r3) with r_g = fp32(max - min) over the
+ *      group's 32 tokens; relevance rel_c >= 0 is supplied per (sequence, KV
+ *      head); score = |fp32(difficulty * rel)|; ties go to the lower channel.
+ *      The relevance of a query is the sum over the query heads that share
+ *      the KV head of |q_c|, in fp32, heads in ascending order.
  */
 #include <math.h>
 #include <stdint.h>
@@ -194,6 +203,58 @@ void ora_select_channels(const uint16_t *K, int ntok, int nch, int k,
 }
 
 /* ------------------------------------------------------------------------
+ * R18: query-aware channel selection.  K is one page [P][D] of stored values
+ * of dtype dt; rel[D] the channel relevance.  Outputs as ora_select_channels.
+ * ---------------------------------------------------------------------- */
+void ora_select_channels_rel(int dt, const uint16_t *K, const float *rel, int k,
+                             uint8_t *boosted, uint8_t *idx) {
+    uint64_t key[D];
+    for (int c = 0; c < D; c++) {
+        float r[P / GK];
+        for (int g = 0; g < P / GK; g++) {
+            float lo = dec32(dt, K[(size_t)g * GK * D + c]), hi = lo;
+            for (int t = 1; t < GK; t++) {
+                float v = dec32(dt, K[(size_t)(g * GK + t) * D + c]);
+                if (v < lo) lo = v;
+                if (v > hi) hi = v;
+            }
+            r[g] = hi - lo;
+        }
+        float diff = ORA_PLANT == 15 ? fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3]))
+                                     : (r[0] + r[1]) + (r[2] + r[3]);
+        float score = fabsf(ORA_PLANT == 14 ? diff : diff * rel[c]);
+        uint32_t bits;
+        memcpy(&bits, &score, sizeof bits);
+        key[c] = ((uint64_t)bits << 8) | (uint64_t)(255 - c); /* lower channel wins ties */
+    }
+    int j = 0;
+    for (int c = 0; c < D; c++) {
+        int rank = 0;
+        for (int c2 = 0; c2 < D; c2++)
+            if (key[c2] > key[c]) rank++;
+        boosted[c] = (uint8_t)(rank < k);
+    }
+    for (int c = 0; c < D; c++)
+        if (boosted[c]) idx[j++] = (uint8_t)c;
+}
+
+/* R18: relevance of a query batch, rel[b][h][c] = sum over the g = Hq / Hkv
+   query heads h g + j (j ascending) of |q[b][h g + j][c]|, in fp32. */
+void ora_query_relevance(int dt, int B, int Hq, int Hkv, const uint16_t *q, float *rel) {
+    int g = Hq / Hkv;
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < Hkv; h++)
+            for (int c = 0; c < D; c++) {
+                float acc = 0.0f;
+                for (int j = 0; j < g; j++) {
+                    float a = fabsf(dec32(dt, q[((size_t)b * Hq + h * g + j) * D + c]));
+                    acc = ORA_PLANT == 16 ? fmaxf(acc, a) : acc + a;
+                }
+                rel[((size_t)b * Hkv + h) * D + c] = acc;
+            }
+}
+
+/* ------------------------------------------------------------------------
  * R6: page layout.  One page (128 tokens of one sequence and KV head) is one
  * contiguous blob of segments, in this order, each starting on 16 bytes:
  *   K_lo    [P][D/4]   2-bit lo plane of every Key channel, token-major
@@ -274,13 +335,17 @@ static uint16_t get16(const uint8_t *seg, size_t i) {
  * NULL): kcode[P][D] (4-bit code for boosted channels, 2-bit otherwise) and
  * vcode[P][D], taken before packing.
  * ---------------------------------------------------------------------- */
-int ora_quantize_page(int dt, int k, const uint16_t *Kp, const uint16_t *Vp,
-                      uint8_t *page, uint8_t *kcode_out, uint8_t *vcode_out) {
+static int quantize_page_sel(int dt, int k, const uint16_t *Kp, const uint16_t *Vp,
+                             const float *rel, uint8_t *page, uint8_t *kcode_out,
+                             uint8_t *vcode_out) {
     if (k < 0 || k > D || k % 4) return -1;
     layout_t L = layout_of(k);
     memset(page, 0, L.total);
     uint8_t boosted[D], idx[D];
-    ora_select_channels(Kp, P, D, k, boosted, idx);
+    if (rel)
+        ora_select_channels_rel(dt, Kp, rel, k, boosted, idx);
+    else
+        ora_select_channels(Kp, P, D, k, boosted, idx);
 
     uint8_t kcode[P * D], vcode[P * D];
     /* Keys: per channel, per 32-token group (R2, R4) */
@@ -325,6 +390,18 @@ int ora_quantize_page(int dt, int k, const uint16_t *Kp, const uint16_t *Vp,
     if (kcode_out) memcpy(kcode_out, kcode, sizeof kcode);
     if (vcode_out) memcpy(vcode_out, vcode, sizeof vcode);
     return 0;
+}
+
+int ora_quantize_page(int dt, int k, const uint16_t *Kp, const uint16_t *Vp,
+                      uint8_t *page, uint8_t *kcode_out, uint8_t *vcode_out) {
+    return quantize_page_sel(dt, k, Kp, Vp, NULL, page, kcode_out, vcode_out);
+}
+
+/* The same page with the query-aware selection (R18); rel: [D] relevance. */
+int ora_quantize_page_rel(int dt, int k, const uint16_t *Kp, const uint16_t *Vp,
+                          const float *rel, uint8_t *page, uint8_t *kcode_out,
+                          uint8_t *vcode_out) {
+    return quantize_page_sel(dt, k, Kp, Vp, rel, page, kcode_out, vcode_out);
 }
 
 /* ------------------------------------------------------------------------

@@ -25,6 +25,7 @@ F16, BF16 = 0, 1
 _u8p = ctypes.POINTER(ctypes.c_uint8)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _f64p = ctypes.POINTER(ctypes.c_double)
+_f32p = ctypes.POINTER(ctypes.c_float)
 _i64p = ctypes.POINTER(ctypes.c_int64)
 
 
@@ -70,6 +71,14 @@ class OracleLib:
         L.ora_attention.argtypes = [ctypes.c_int] * 8 + [_u8p, _u16p, _u16p, _u16p,
                                                          ctypes.c_double, _f64p,
                                                          ctypes.c_int, ctypes.c_int]
+        L.ora_select_channels_rel.restype = None
+        L.ora_select_channels_rel.argtypes = [ctypes.c_int, _u16p, _f32p, ctypes.c_int, _u8p,
+                                              _u8p]
+        L.ora_query_relevance.restype = None
+        L.ora_query_relevance.argtypes = [ctypes.c_int] * 4 + [_u16p, _f32p]
+        L.ora_quantize_page_rel.restype = ctypes.c_int
+        L.ora_quantize_page_rel.argtypes = [ctypes.c_int, ctypes.c_int, _u16p, _u16p, _f32p,
+                                            _u8p, _u8p, _u8p]
         L.ora_num_threads.restype = ctypes.c_int
         L.ora_num_threads.argtypes = []
         self.L = L
@@ -124,16 +133,43 @@ class OracleLib:
     def khi_bit(self, k, t, j):
         return int(self.L.ora_khi_bit(k, t, j))
 
-    def quantize_page(self, dt, k, Kp, Vp):
-        """Kp, Vp: [P][D] uint16 -> (page bytes, 4-bit-or-2-bit Key codes, Value codes)."""
+    def select_channels_rel(self, dt, K_bits, rel, k):
+        """Query-aware selection of one page: K [P][D] uint16, rel [D] float32."""
+        K_bits = np.ascontiguousarray(K_bits, dtype=np.uint16)
+        rel = np.ascontiguousarray(rel, dtype=np.float32)
+        assert K_bits.shape == (P, D) and rel.shape == (D,)
+        boosted = np.zeros(D, np.uint8)
+        idx = np.zeros(D, np.uint8)
+        self.L.ora_select_channels_rel(dt, _ptr(K_bits, _u16p), _ptr(rel, _f32p), k,
+                                       _ptr(boosted, _u8p), _ptr(idx, _u8p))
+        return boosted.astype(bool), idx[:k].copy()
+
+    def query_relevance(self, dt, q_bits, Hkv):
+        """q [B][Hq][D] uint16 -> relevance [B][Hkv][D] float32."""
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        B, Hq, _ = q_bits.shape
+        rel = np.zeros((B, Hkv, D), np.float32)
+        self.L.ora_query_relevance(dt, B, Hq, Hkv, _ptr(q_bits, _u16p), _ptr(rel, _f32p))
+        return rel
+
+    def quantize_page(self, dt, k, Kp, Vp, rel=None):
+        """Kp, Vp: [P][D] uint16 -> (page bytes, 4-bit-or-2-bit Key codes, Value codes).
+        rel ([D] float32): query-aware channel selection instead of magnitude."""
         Kp = np.ascontiguousarray(Kp, dtype=np.uint16)
         Vp = np.ascontiguousarray(Vp, dtype=np.uint16)
         assert Kp.shape == (P, D) and Vp.shape == (P, D)
         page = np.zeros(self.page_bytes(k), np.uint8)
         kc = np.zeros((P, D), np.uint8)
         vc = np.zeros((P, D), np.uint8)
-        rc = self.L.ora_quantize_page(dt, k, _ptr(Kp, _u16p), _ptr(Vp, _u16p),
-                                      _ptr(page, _u8p), _ptr(kc, _u8p), _ptr(vc, _u8p))
+        if rel is not None:
+            rel = np.ascontiguousarray(rel, dtype=np.float32)
+            assert rel.shape == (D,)
+            rc = self.L.ora_quantize_page_rel(dt, k, _ptr(Kp, _u16p), _ptr(Vp, _u16p),
+                                              _ptr(rel, _f32p), _ptr(page, _u8p),
+                                              _ptr(kc, _u8p), _ptr(vc, _u8p))
+        else:
+            rc = self.L.ora_quantize_page(dt, k, _ptr(Kp, _u16p), _ptr(Vp, _u16p),
+                                          _ptr(page, _u8p), _ptr(kc, _u8p), _ptr(vc, _u8p))
         if rc:
             raise ValueError(f"ora_quantize_page failed ({rc})")
         return page, kc, vc
@@ -226,6 +262,10 @@ class OracleCache:
         self.vres = np.zeros((B, Hkv, R, D), np.uint16)
         self.n_pages = 0
         self.n_res = 0
+        self.rel = None  # [B][Hkv][D] float32: query-aware selection for later pages
+
+    def _rel(self, b, h):
+        return None if self.rel is None else self.rel[b, h]
 
     def quantize_pages(self, K, V):
         """K, V: [B][Hkv][n*P][D] uint16; appends n pages per sequence."""
@@ -239,7 +279,8 @@ class OracleCache:
             for h in range(self.Hkv):
                 for p in range(n):
                     sl = slice(p * P, (p + 1) * P)
-                    page, _, _ = self.ora.quantize_page(self.dt, self.k, K[b, h, sl], V[b, h, sl])
+                    page, _, _ = self.ora.quantize_page(self.dt, self.k, K[b, h, sl], V[b, h, sl],
+                                                        self._rel(b, h))
                     self.pages[b, h, self.n_pages + p] = page
         self.n_pages += n
 
@@ -252,7 +293,7 @@ class OracleCache:
             for b in range(self.B):
                 for h in range(self.Hkv):
                     page, _, _ = self.ora.quantize_page(self.dt, self.k, self.kres[b, h],
-                                                        self.vres[b, h])
+                                                        self.vres[b, h], self._rel(b, h))
                     self.pages[b, h, self.n_pages] = page
             self.n_pages += 1
             self.n_res = 0

@@ -220,6 +220,111 @@ def pin_selection_planted_outliers(ora):
 
 
 # ---------------------------------------------------------------------------
+# query-aware channel selection (MixKVQ abstract: a Key channel's quantization
+# difficulty and its relevance to the query decide its precision)
+# ---------------------------------------------------------------------------
+def pin_query_selection_follows_relevance(ora):
+    """Relevance zero outside a set S of k channels (all with a nonzero
+    range): exactly S is boosted, whatever the Key magnitudes."""
+    r = np.random.default_rng(21)
+    for dt in (F16, BF16):
+        for k in (1, 16, 32):
+            K = _bits(dt, r.standard_normal((P, D)) * np.exp(r.uniform(-2, 3, D)))
+            S = np.sort(r.choice(D, k, replace=False))
+            rel = np.zeros(D, np.float32)
+            rel[S] = r.uniform(0.01, 4.0, k).astype(np.float32)
+            boosted, idx = ora.select_channels_rel(dt, K, rel, k)
+            assert idx.tolist() == S.tolist()
+            assert np.flatnonzero(boosted).tolist() == S.tolist()
+
+
+def pin_query_selection_sum_of_group_ranges(ora):
+    """Closed form: channel a has range 8 in one Key group only, channel b
+    range 3 in all four (sum 12); every other channel is constant."""
+    a, b = 40, 90
+    Kf = np.full((P, D), 0.5)
+    t = np.arange(P)
+    Kf[:GK, a] = np.where(t[:GK] % 2, 8.0, 0.0)
+    Kf[:, b] = np.where(t % 2, 3.0, 0.0)
+    for dt in (F16, BF16):
+        K = _bits(dt, Kf)
+        rel = np.ones(D, np.float32)
+        assert ora.select_channels_rel(dt, K, rel, 1)[1].tolist() == [b]      # 12 > 8
+        assert ora.select_channels_rel(dt, K, rel, 2)[1].tolist() == [a, b]
+        assert ora.select_channels_rel(dt, K, rel, 3)[1].tolist() == [0, a, b]  # ties: lowest
+        rel[a] = 2.0                                                          # 16 > 12
+        assert ora.select_channels_rel(dt, K, rel, 1)[1].tolist() == [a]
+        rel[a] = 1.5                                                          # 12 = 12: lower
+        assert ora.select_channels_rel(dt, K, rel, 1)[1].tolist() == [a]
+        rel[a], rel[b] = 1.0, 0.0
+        assert ora.select_channels_rel(dt, K, rel, 1)[1].tolist() == [a]
+
+
+def pin_query_selection_constant_outlier(ora):
+    """A channel of constant large value is the magnitude ranking's first
+    choice but has no quantization difficulty: the query-aware ranking skips
+    it however relevant it is."""
+    r = np.random.default_rng(22)
+    Kf = r.standard_normal((P, D))
+    Kf[:, 7] = 1000.0
+    K = _bits(BF16, Kf)
+    assert 7 in ora.select_channels(K, 1)[1].tolist()
+    rel = np.ones(D, np.float32)
+    rel[7] = 1e6
+    assert 7 not in ora.select_channels_rel(BF16, K, rel, 16)[1].tolist()
+
+
+def pin_query_selection_exact_scores(ora):
+    """Integer-valued Keys and relevances: every fp32 step is exact, so the
+    top-k order statistic can be checked against float64 arithmetic."""
+    r = np.random.default_rng(23)
+    for trial in range(6):
+        Kf = r.integers(-8, 9, (P, D)).astype(np.float64)
+        rel = r.integers(0, 5, D).astype(np.float32)
+        diff = np.ptp(Kf.reshape(P // GK, GK, D), axis=1).sum(axis=0)
+        score = diff * rel
+        for k in (8, 16, 32):
+            boosted, idx = ora.select_channels_rel(F16, _bits(F16, Kf), rel, k)
+            assert boosted.sum() == k
+            assert score[boosted].min() >= score[~boosted].max()
+            # ties at the boundary resolve to the lower channels
+            edge = score[boosted].min()
+            tied = np.flatnonzero(score == edge)
+            taken = [c for c in tied if boosted[c]]
+            assert taken == sorted(tied)[:len(taken)]
+
+
+def pin_query_relevance(ora):
+    """Sum over the query heads sharing a KV head of |q|: one head only gives
+    |q| itself; heads (j + 1) / 4 * sign give 2.5 for g = 4."""
+    r = np.random.default_rng(24)
+    for dt in (F16, BF16):
+        q = r.standard_normal((2, 4, D))
+        rel = ora.query_relevance(dt, _bits(dt, q), 4)            # g = 1
+        assert np.array_equal(rel, np.abs(_val(dt, _bits(dt, q))).astype(np.float32))
+        sign = r.choice([-1.0, 1.0], (2, 8, D))
+        qq = np.stack([(j % 4 + 1) / 4.0 * sign[:, j] for j in range(8)], axis=1)
+        rel = ora.query_relevance(dt, _bits(dt, qq), 2)           # g = 4
+        assert rel.shape == (2, 2, D) and (rel == 2.5).all()
+
+
+def pin_query_page_reduces_to_magnitude(ora):
+    """Relevance 1 on the magnitude ranking's channels and 0 elsewhere: the
+    query-aware page is byte for byte the magnitude-ranked page (only the
+    selection differs between the two)."""
+    r = np.random.default_rng(25)
+    for dt, k in ((F16, 16), (BF16, 32)):
+        K = _bits(dt, r.standard_normal((P, D)) * np.exp(r.uniform(-1, 2, D)))
+        V = _bits(dt, r.standard_normal((P, D)))
+        _, idx = ora.select_channels(K, k)
+        rel = np.zeros(D, np.float32)
+        rel[idx] = 1.0
+        a, _, _ = ora.quantize_page(dt, k, K, V)
+        b, _, _ = ora.quantize_page(dt, k, K, V, rel=rel)
+        assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
 # pages: layout, planes, round trip
 # ---------------------------------------------------------------------------
 def pin_page_bytes(ora):

@@ -23,6 +23,9 @@ PLANTS = {
     10: "channels ranked by minimum magnitude",
     11: "Value groups taken along tokens",
     13: "scale divided by L + 1",
+    14: "query-aware score ignores the relevance",
+    15: "query-aware difficulty = largest group range instead of their sum",
+    16: "relevance = largest |q| of the group's heads instead of the sum",
 }
 
 
