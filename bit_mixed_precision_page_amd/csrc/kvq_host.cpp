@@ -19,6 +19,7 @@ struct kvq_cache {
     int32_t n_pages;
     int32_t n_res;
     int32_t splits_override;  // 0 = automatic
+    const float *rel;         // query-aware channel relevance [B][Hkv][D], or null
     hipEvent_t ev_before, ev_after;
 };
 
@@ -33,6 +34,7 @@ struct kvq_pool {
     std::vector<int32_t> n_pages, n_res;
     std::vector<std::vector<int32_t>> blocks;
     std::vector<int32_t> free_list;  // back() is handed out next
+    const float *rel;                // query-aware channel relevance [B][Hkv][D], or null
     hipEvent_t ev_before, ev_after;
 };
 
@@ -222,7 +224,7 @@ int pool_flush_full(kvq_pool *p, hipStream_t st, int32_t *n) {
     const uint16_t *kw = reinterpret_cast<const uint16_t *>(p->mem + G.res_base);
     hipError_t e = kvq::launch_pool_pages(G, p->mem, pool_table(p), kw, kw + (size_t)kvq::R * kvq::D,
                                           (size_t)2 * kvq::R * kvq::D,
-                                          (size_t)G.Hkv * 2 * kvq::R * kvq::D, pp, st);
+                                          (size_t)G.Hkv * 2 * kvq::R * kvq::D, pp, p->rel, st);
     if (e != hipSuccess) return KVQ_EHIP;
     for (int e2 = 0; e2 < pp.n; e2++) {
         const int b = pp.src[e2];
@@ -269,6 +271,7 @@ int kvq_cache_create(const kvq_config *cfg, void *dev_mem, size_t bytes, kvq_cac
     c->n_pages = 0;
     c->n_res = 0;
     c->splits_override = 0;
+    c->rel = nullptr;
     c->ev_before = nullptr;
     c->ev_after = nullptr;
     *out = c;
@@ -291,7 +294,7 @@ int kvq_quantize_page(kvq_cache *c, const void *k, const void *v, int32_t n_page
     if ((int64_t)c->n_pages + n_pages > c->G.max_pages) return KVQ_ECAPACITY;
     hipError_t e = kvq::launch_quantize_pages(
         c->G, c->mem, static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v),
-        (size_t)n_pages * kvq::P * kvq::D, c->n_pages, n_pages,
+        (size_t)n_pages * kvq::P * kvq::D, c->n_pages, n_pages, c->rel,
         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return KVQ_EHIP;
     c->n_pages += n_pages;
@@ -306,7 +309,7 @@ int kvq_append_token(kvq_cache *c, const void *k, const void *v, void *stream,
     if (flush && c->n_pages >= c->G.max_pages) return KVQ_ECAPACITY;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (flush) {
-        hipError_t e = kvq::launch_flush_window(c->G, c->mem, c->n_pages, st);
+        hipError_t e = kvq::launch_flush_window(c->G, c->mem, c->n_pages, c->rel, st);
         if (e != hipSuccess) return KVQ_EHIP;
         c->n_pages += 1;
         c->n_res = 0;
@@ -350,7 +353,7 @@ int kvq_append_decode(kvq_cache *c, const void *k, const void *v, const void *q,
     if (flush && c->n_pages >= c->G.max_pages) return KVQ_ECAPACITY;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (flush) {
-        hipError_t e = kvq::launch_flush_window(c->G, c->mem, c->n_pages, st);
+        hipError_t e = kvq::launch_flush_window(c->G, c->mem, c->n_pages, c->rel, st);
         if (e != hipSuccess) return KVQ_EHIP;
         c->n_pages += 1;
         c->n_res = 0;
@@ -425,6 +428,27 @@ int kvq_quantize_groups(int32_t dtype, int32_t L, const void *x, int32_t n_group
         static_cast<hipStream_t>(stream)));
 }
 
+int kvq_set_channel_relevance(kvq_cache *c, const float *rel) {
+    if (!c) return KVQ_EINVAL;
+    if (rel && !aligned16(rel)) return KVQ_EALIGN;
+    c->rel = rel;
+    return KVQ_OK;
+}
+
+int kvq_query_relevance(int32_t dtype, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                        const void *q, float *rel, void *stream) {
+    if (dtype != KVQ_F16 && dtype != KVQ_BF16) return KVQ_EINVAL;
+    if (batch < 0 || num_kv_heads < 1 || num_q_heads < num_kv_heads ||
+        num_q_heads % num_kv_heads || (int64_t)batch * num_kv_heads * kvq::D > (1 << 30))
+        return KVQ_EINVAL;
+    if (batch == 0) return KVQ_OK;
+    if (!q || !rel) return KVQ_EINVAL;
+    if (!aligned16(q) || !aligned16(rel)) return KVQ_EALIGN;
+    return hip_status(kvq::launch_query_relevance(dtype, static_cast<const uint16_t *>(q), rel,
+                                                  batch, num_q_heads, num_kv_heads,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 int kvq_set_kernel_events(kvq_cache *c, void *before, void *after) {
     if (!c) return KVQ_EINVAL;
     if ((before == nullptr) != (after == nullptr)) return KVQ_EINVAL;
@@ -466,6 +490,7 @@ int kvq_pool_create(const kvq_config *cfg, int32_t n_blocks, void *dev_mem, size
         p->blocks.assign(G.B, std::vector<int32_t>());
         p->free_list.resize(n_blocks);
         for (int32_t i = 0; i < n_blocks; i++) p->free_list[i] = n_blocks - 1 - i;
+        p->rel = nullptr;
         p->ev_before = nullptr;
         p->ev_after = nullptr;
     } catch (...) {
@@ -510,7 +535,7 @@ int kvq_pool_prefill(kvq_pool *p, int32_t seq, const void *k, const void *v, int
         }
         hipError_t e = kvq::launch_pool_pages(G, p->mem, pool_table(p), ks, vs,
                                               (size_t)n_tokens * kvq::D,
-                                              (size_t)kvq::P * kvq::D, pp, st);
+                                              (size_t)kvq::P * kvq::D, pp, p->rel, st);
         if (e != hipSuccess) return KVQ_EHIP;
     }
     hipError_t e = kvq::launch_pool_window_fill(G, p->mem, ks, vs, seq, n_tokens,
@@ -646,6 +671,13 @@ int kvq_pool_window_offset(const kvq_pool *p, int32_t seq, int32_t h, size_t *k_
 int kvq_pool_table_offset(const kvq_pool *p, size_t *off) {
     if (!p || !off) return KVQ_EINVAL;
     *off = p->table_off;
+    return KVQ_OK;
+}
+
+int kvq_pool_set_channel_relevance(kvq_pool *p, const float *rel) {
+    if (!p) return KVQ_EINVAL;
+    if (rel && !aligned16(rel)) return KVQ_EALIGN;
+    p->rel = rel;
     return KVQ_OK;
 }
 

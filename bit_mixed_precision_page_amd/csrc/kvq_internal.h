@@ -59,12 +59,18 @@ __host__ __device__ inline size_t res_v_off(const Geometry &G, int unit) {
 // Launchers (defined in the .hip files).  All asynchronous on `stream`.
 // Quantize `n_new` pages per unit: the source of page p of unit u starts at
 // element src + u * src_unit_stride + p * P * D of k_src / v_src ([P][D] rows
-// of D contiguous elements); destinations are pages first_page + p.
+// of D contiguous elements); destinations are pages first_page + p.  rel:
+// [B][Hkv][D] channel relevance (query-aware ranking) or null (magnitude).
 hipError_t launch_quantize_pages(const Geometry &G, uint8_t *cache, const uint16_t *k_src,
                                  const uint16_t *v_src, size_t src_unit_stride,
-                                 int first_page, int n_new, hipStream_t stream);
+                                 int first_page, int n_new, const float *rel,
+                                 hipStream_t stream);
 // Same, with each unit's window as the source (one page per unit).
-hipError_t launch_flush_window(const Geometry &G, uint8_t *cache, int page, hipStream_t stream);
+hipError_t launch_flush_window(const Geometry &G, uint8_t *cache, int page, const float *rel,
+                               hipStream_t stream);
+// rel [B][Hkv][D] = sum over each KV head's query heads of |q| (q [B][Hq][D]).
+hipError_t launch_query_relevance(int dtype, const uint16_t *q, float *rel, int B, int Hq,
+                                  int Hkv, hipStream_t stream);
 // Copy one token per unit into window slot `slot`.
 hipError_t launch_append(const Geometry &G, uint8_t *cache, const uint16_t *k,
                          const uint16_t *v, int slot, hipStream_t stream);
@@ -129,7 +135,8 @@ struct PoolPlan {
 // res_base = byte offset of the windows ([B][Hkv][K | V][R][D]).
 hipError_t launch_pool_pages(const Geometry &G, uint8_t *pool, int32_t *table,
                              const uint16_t *k_src, const uint16_t *v_src, size_t src_h_stride,
-                             size_t src_e_stride, const PoolPages &pp, hipStream_t stream);
+                             size_t src_e_stride, const PoolPages &pp, const float *rel,
+                             hipStream_t stream);
 hipError_t launch_pool_append(const Geometry &G, uint8_t *mem, const uint16_t *k,
                               const uint16_t *v, const PoolSlots &ps, hipStream_t stream);
 hipError_t launch_pool_window_fill(const Geometry &G, uint8_t *mem, const uint16_t *k,

@@ -6,7 +6,9 @@
 //     fraction at higher precision; notes.yuuk.io "KV cache quantization",
 //     open questions: the heuristic is magnitude based): score = max |K| over
 //     the page as sign-cleared bits, ties to the lower channel, top k by an
-//     exact rank count;
+//     exact rank count.  With a relevance vector (MixKVQ abstract: the
+//     channel's quantization difficulty and its relevance to the query) the
+//     score is |(sum of the channel's four Key-group ranges) * relevance|;
 //   * Keys per channel over 32-token groups, Values per token over
 //     32-channel groups, asymmetric min/max (KIVI explainer, section 3);
 //     boosted channels with 4 bits split into a lo and a hi 2-bit plane;
@@ -67,15 +69,17 @@ __device__ __forceinline__ uint32_t quant_code(float x, float zf, float inv, int
     return (uint32_t)r;
 }
 
-// One page: K and V rows [P][D] at ks / vs, the packed page written to pg.
+// One page: K and V rows [P][D] at ks / vs, the packed page written to pg;
+// rel: [D] channel relevance (query-aware ranking) or null (magnitude).
 template <int DT>
 __device__ __forceinline__ void quantize_page_body(uint8_t *__restrict__ pg,
                                                    const uint16_t *__restrict__ ks,
-                                                   const uint16_t *__restrict__ vs, int k) {
+                                                   const uint16_t *__restrict__ vs, int k,
+                                                   const float *__restrict__ rel) {
     __shared__ __align__(16) uint16_t tile[P * kRowPad];
     __shared__ __align__(16) uint8_t codes[P * D];
-    __shared__ uint32_t amax[2][D];
-    __shared__ uint32_t keys[D];
+    __shared__ uint32_t amax[2][D];  // |K| bits, or fp32 bits of two group ranges
+    __shared__ uint64_t keys[D];
     __shared__ uint8_t boosted[D];
     __shared__ uint8_t idx[D];
     __shared__ uint64_t mask0;
@@ -119,14 +123,29 @@ __device__ __forceinline__ void quantize_page_body(uint8_t *__restrict__ pg,
         glo[gg] = lo;
         ghi[gg] = hi;
     }
-    amax[half][c] = am;
+    if (rel) {
+        // ranges of this thread's groups 2 half and 2 half + 1, summed pairwise
+        amax[half][c] = __float_as_uint(
+            __fadd_rn(__fsub_rn(ghi[0], glo[0]), __fsub_rn(ghi[1], glo[1])));
+    } else {
+        amax[half][c] = am;
+    }
     __syncthreads();
-    if (tid < D) keys[tid] = (max(amax[0][tid], amax[1][tid]) << 8) | (uint32_t)(255 - tid);
+    if (tid < D) {
+        uint64_t sc;
+        if (rel) {
+            const float diff = __fadd_rn(__uint_as_float(amax[0][tid]), __uint_as_float(amax[1][tid]));
+            sc = __float_as_uint(__fmul_rn(diff, rel[tid])) & 0x7fffffffu;
+        } else {
+            sc = max(amax[0][tid], amax[1][tid]);
+        }
+        keys[tid] = (sc << 8) | (uint64_t)(255 - tid);
+    }
     __syncthreads();
 
     // 3. Top-k by rank count; ascending list through wave ballots.
     if (tid < D) {
-        uint32_t my = keys[tid];
+        const uint64_t my = keys[tid];
         int rank = 0;
         for (int j = 0; j < D; j++) rank += keys[j] > my ? 1 : 0;
         bool b = rank < k;
@@ -244,31 +263,49 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void quantize_pages_kernel(
     uint8_t *__restrict__ cache, const uint16_t *__restrict__ k_src,
     const uint16_t *__restrict__ v_src, size_t src_unit_stride, int first_page, int n_new,
-    int max_pages, uint32_t page_bytes, int k) {
+    int max_pages, uint32_t page_bytes, int k, const float *__restrict__ rel) {
     const int p = blockIdx.x;
     const int unit = blockIdx.y;
     uint8_t *pg = cache + ((size_t)unit * max_pages + first_page + p) * page_bytes;
     const uint16_t *ks = k_src + (size_t)unit * src_unit_stride + (size_t)p * P * D;
     const uint16_t *vs = v_src + (size_t)unit * src_unit_stride + (size_t)p * P * D;
-    quantize_page_body<DT>(pg, ks, vs, k);
+    quantize_page_body<DT>(pg, ks, vs, k, rel ? rel + (size_t)unit * D : nullptr);
 }
 
 // Block pool: entry blockIdx.x of the list, KV head blockIdx.y.  The page
 // goes to pool block pp.block[e] (the block holds the Hkv pages of one
 // 128-token span); its source rows start at element
 // pp.src[e] * src_e_stride + h * src_h_stride; the KV-head-0 workgroup
-// records the block in the block table.
+// records the block in the block table (entry tslot = seq * max_pages + page,
+// which also names the relevance row of the sequence).
 template <int DT>
 __global__ __launch_bounds__(kThreads) void pool_pages_kernel(
     uint8_t *__restrict__ pool, int32_t *__restrict__ table, const uint16_t *__restrict__ k_src,
     const uint16_t *__restrict__ v_src, size_t src_h_stride, size_t src_e_stride, int Hkv,
-    uint32_t page_bytes, int k, const PoolPages pp) {
+    int max_pages, uint32_t page_bytes, int k, const float *__restrict__ rel,
+    const PoolPages pp) {
     const int e = blockIdx.x, h = blockIdx.y;
     const int blk = pp.block[e];
     if (h == 0 && threadIdx.x == 0) table[pp.tslot[e]] = blk;
     uint8_t *pg = pool + ((size_t)blk * Hkv + h) * page_bytes;
     const size_t so = (size_t)pp.src[e] * src_e_stride + (size_t)h * src_h_stride;
-    quantize_page_body<DT>(pg, k_src + so, v_src + so, k);
+    const int seq = pp.tslot[e] / max_pages;
+    quantize_page_body<DT>(pg, k_src + so, v_src + so, k,
+                           rel ? rel + ((size_t)seq * Hkv + h) * D : nullptr);
+}
+
+// rel[b][h][c] = sum over the g query heads h g + j (j ascending) of
+// |q[b][h g + j][c]| in fp32: the relevance of one query to each Key channel.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void query_relevance_kernel(
+    const uint16_t *__restrict__ q, float *__restrict__ rel, int B, int Hq, int Hkv) {
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= B * Hkv * D) return;
+    const int c = i % D, bh = i / D, b = bh / Hkv, h = bh % Hkv, g = Hq / Hkv;
+    float acc = 0.0f;
+    for (int j = 0; j < g; j++)
+        acc = __fadd_rn(acc, fabsf(dec<DT>(q[((size_t)b * Hq + h * g + j) * D + c])));
+    rel[i] = acc;
 }
 
 // Block pool: copy one token per (sequence, KV head) into window slot
@@ -353,24 +390,39 @@ __global__ __launch_bounds__(kThreads) void quantize_groups_kernel(
 
 hipError_t launch_quantize_pages(const Geometry &G, uint8_t *cache, const uint16_t *k_src,
                                  const uint16_t *v_src, size_t src_unit_stride,
-                                 int first_page, int n_new, hipStream_t stream) {
+                                 int first_page, int n_new, const float *rel,
+                                 hipStream_t stream) {
     if (n_new <= 0) return hipSuccess;
     dim3 grid(n_new, G.B * G.Hkv);
     if (G.dtype == F16)
         hipLaunchKernelGGL(quantize_pages_kernel<F16>, grid, dim3(kThreads), 0, stream, cache,
                            k_src, v_src, src_unit_stride, first_page, n_new, G.max_pages,
-                           G.page_bytes, G.k);
+                           G.page_bytes, G.k, rel);
     else
         hipLaunchKernelGGL(quantize_pages_kernel<BF16>, grid, dim3(kThreads), 0, stream, cache,
                            k_src, v_src, src_unit_stride, first_page, n_new, G.max_pages,
-                           G.page_bytes, G.k);
+                           G.page_bytes, G.k, rel);
     return hipGetLastError();
 }
 
-hipError_t launch_flush_window(const Geometry &G, uint8_t *cache, int page, hipStream_t stream) {
+hipError_t launch_flush_window(const Geometry &G, uint8_t *cache, int page, const float *rel,
+                               hipStream_t stream) {
     const uint16_t *kw = reinterpret_cast<const uint16_t *>(cache + G.res_base);
     const uint16_t *vw = kw + (size_t)R * D;
-    return launch_quantize_pages(G, cache, kw, vw, (size_t)2 * R * D, page, 1, stream);
+    return launch_quantize_pages(G, cache, kw, vw, (size_t)2 * R * D, page, 1, rel, stream);
+}
+
+hipError_t launch_query_relevance(int dtype, const uint16_t *q, float *rel, int B, int Hq,
+                                  int Hkv, hipStream_t stream) {
+    const int n = B * Hkv * D;
+    dim3 grid((n + kThreads - 1) / kThreads);
+    if (dtype == F16)
+        hipLaunchKernelGGL(query_relevance_kernel<F16>, grid, dim3(kThreads), 0, stream, q, rel,
+                           B, Hq, Hkv);
+    else
+        hipLaunchKernelGGL(query_relevance_kernel<BF16>, grid, dim3(kThreads), 0, stream, q, rel,
+                           B, Hq, Hkv);
+    return hipGetLastError();
 }
 
 hipError_t launch_append(const Geometry &G, uint8_t *cache, const uint16_t *k,
@@ -389,15 +441,18 @@ hipError_t launch_append(const Geometry &G, uint8_t *cache, const uint16_t *k,
 
 hipError_t launch_pool_pages(const Geometry &G, uint8_t *pool, int32_t *table,
                              const uint16_t *k_src, const uint16_t *v_src, size_t src_h_stride,
-                             size_t src_e_stride, const PoolPages &pp, hipStream_t stream) {
+                             size_t src_e_stride, const PoolPages &pp, const float *rel,
+                             hipStream_t stream) {
     if (pp.n <= 0) return hipSuccess;
     dim3 grid(pp.n, G.Hkv);
     if (G.dtype == F16)
         hipLaunchKernelGGL(pool_pages_kernel<F16>, grid, dim3(kThreads), 0, stream, pool, table,
-                           k_src, v_src, src_h_stride, src_e_stride, G.Hkv, G.page_bytes, G.k, pp);
+                           k_src, v_src, src_h_stride, src_e_stride, G.Hkv, G.max_pages,
+                           G.page_bytes, G.k, rel, pp);
     else
         hipLaunchKernelGGL(pool_pages_kernel<BF16>, grid, dim3(kThreads), 0, stream, pool, table,
-                           k_src, v_src, src_h_stride, src_e_stride, G.Hkv, G.page_bytes, G.k, pp);
+                           k_src, v_src, src_h_stride, src_e_stride, G.Hkv, G.max_pages,
+                           G.page_bytes, G.k, rel, pp);
     return hipGetLastError();
 }
 

@@ -29,7 +29,8 @@ EXPORTS = ["kvq_cache_bytes", "kvq_page_bytes", "kvq_cache_create", "kvq_cache_d
            "kvq_pool_append", "kvq_pool_decode_workspace_bytes", "kvq_pool_decode_attention",
            "kvq_pool_append_decode", "kvq_pool_release", "kvq_pool_get_seq",
            "kvq_pool_block_of", "kvq_pool_free_blocks", "kvq_pool_page_offset",
-           "kvq_pool_window_offset", "kvq_pool_table_offset", "kvq_pool_set_kernel_events"]
+           "kvq_pool_window_offset", "kvq_pool_table_offset", "kvq_pool_set_kernel_events",
+           "kvq_set_channel_relevance", "kvq_query_relevance", "kvq_pool_set_channel_relevance"]
 
 
 class KvqError(RuntimeError):
@@ -96,6 +97,9 @@ _SIG = {
     "kvq_pool_window_offset": [_vp, _i32, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)],
     "kvq_pool_table_offset": [_vp, ctypes.POINTER(_sz)],
     "kvq_pool_set_kernel_events": [_vp, _vp, _vp],
+    "kvq_set_channel_relevance": [_vp, _vp],
+    "kvq_query_relevance": [_i32, _i32, _i32, _i32, _vp, _vp, _vp],
+    "kvq_pool_set_channel_relevance": [_vp, _vp],
 }
 for _name, _args in _SIG.items():
     _f = getattr(_L, _name)
@@ -226,6 +230,20 @@ def kvq_strerror(code):
     return _L.kvq_strerror(code).decode()
 
 
+def kvq_set_channel_relevance(handle, rel):
+    _check(_L.kvq_set_channel_relevance(handle, _ptr(rel)), "kvq_set_channel_relevance")
+
+
+def kvq_query_relevance(dtype, batch, num_q_heads, num_kv_heads, q, rel, stream=None):
+    _check(_L.kvq_query_relevance(dtype, batch, num_q_heads, num_kv_heads, _ptr(q), _ptr(rel),
+                                  _stream(stream)), "kvq_query_relevance")
+
+
+def kvq_pool_set_channel_relevance(handle, rel):
+    _check(_L.kvq_pool_set_channel_relevance(handle, _ptr(rel)),
+           "kvq_pool_set_channel_relevance")
+
+
 # -- block pool (variable-length batches) ---------------------------------------
 def kvq_pool_bytes(cfg, n_blocks):
     n = _sz()
@@ -348,6 +366,11 @@ class Cache:
     def append_decode(self, k, v, q, out, stream=None):
         return kvq_append_decode(self.handle, k, v, q, out, self.ws, self.ws_bytes, stream)
 
+    def set_relevance(self, rel):
+        """rel: [B][Hkv][128] float32 device tensor (kept alive by the caller), or None."""
+        self._rel = rel
+        kvq_set_channel_relevance(self.handle, rel)
+
     @property
     def state(self):
         return kvq_get_state(self.handle)
@@ -405,6 +428,11 @@ class Pool:
 
     def release(self, seq):
         kvq_pool_release(self.handle, seq)
+
+    def set_relevance(self, rel):
+        """rel: [batch][Hkv][128] float32 device tensor (kept alive by the caller), or None."""
+        self._rel = rel
+        kvq_pool_set_channel_relevance(self.handle, rel)
 
     def seq(self, seq):
         """(live, n_pages, n_res) of one slot."""

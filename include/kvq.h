@@ -178,6 +178,26 @@ int kvq_residual_offset(const kvq_cache *cache, int32_t b, int32_t h, size_t *k_
 int kvq_quantize_groups(int32_t dtype, int32_t L, const void *x, int32_t n_groups,
                         int32_t group_len, void *s, void *z, void *codes, void *stream);
 
+/* Query-aware Key channel ranking (MixKVQ abstract, fugumt, arXiv
+   2512.19206: a Key channel's need for precision follows its quantization
+   difficulty and its relevance to the query).  rel: device [batch][Hkv][128]
+   float32 (16-byte aligned, finite, >= 0), read by every later page
+   quantization of this cache when its kernel runs (bulk pages and window
+   flushes; the caller may rewrite it between calls, stream-ordered).  Page
+   channel score = |(sum over the page's four Key groups of (max - min) of
+   the channel) * rel[c]| in fp32 (group ranges added pairwise: (g0 + g1) +
+   (g2 + g3)), the k largest boosted, ties to the lower channel.  rel = NULL
+   restores the magnitude ranking.  The page layout and the decode path are
+   unchanged.  Errors: KVQ_EINVAL, KVQ_EALIGN. */
+int kvq_set_channel_relevance(kvq_cache *cache, const float *rel);
+
+/* Relevance of one query batch: rel[b][h][c] = sum over the g = Hq / Hkv query
+   heads h g + j (j ascending) of |q[b][h g + j][c]|, in fp32.  q: device
+   [batch][Hq][128] dtype; rel: device [batch][Hkv][128] float32.  Errors:
+   KVQ_EINVAL, KVQ_EALIGN. */
+int kvq_query_relevance(int32_t dtype, int32_t batch, int32_t num_q_heads,
+                        int32_t num_kv_heads, const void *q, float *rel, void *stream);
+
 /* Optional timing hooks: when set (non-NULL hipEvent_t values), decode
    attention records `before` on its stream just before its split kernel and
    `after` just after it.  NULL, NULL clears them. */
@@ -271,6 +291,10 @@ int kvq_pool_page_offset(const kvq_pool *pool, int32_t block, int32_t h, size_t 
 int kvq_pool_window_offset(const kvq_pool *pool, int32_t seq, int32_t h, size_t *k_off,
                            size_t *v_off);
 int kvq_pool_table_offset(const kvq_pool *pool, size_t *off);
+
+/* Query-aware ranking for the pool's later pages (prefill and flushes), as
+   kvq_set_channel_relevance; rel: device [batch][Hkv][128] float32. */
+int kvq_pool_set_channel_relevance(kvq_pool *pool, const float *rel);
 
 /* Timing hooks of the pool's split kernel (as kvq_set_kernel_events). */
 int kvq_pool_set_kernel_events(kvq_pool *pool, void *before, void *after);
