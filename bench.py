@@ -49,6 +49,9 @@ def parse():
                          "kvq_append_decode, same results)")
     ap.add_argument("--event-fence", action="store_true",
                     help="events with the default system-scope fence (slower markers)")
+    ap.add_argument("--query-aware", action="store_true",
+                    help="rank Key channels by group range x query relevance (relevance of "
+                         "the first decode query) instead of magnitude")
     return ap.parse_args()
 
 
@@ -299,8 +302,14 @@ def stream_main(a, w, torch, gen, kvq):
     del K, V
     cfg = kvq.config(w.B, w.Hq, w.Hkv, w.boost, w.max_pages, w.dtype)
     scratch = kvq.Cache(cfg, device=dev)
-    scratch.quantize_page(Kd, Vd, bulk)
     base = kvq.Cache(cfg, device=dev)
+    rel = None
+    if a.query_aware:
+        rel = torch.empty(w.B, w.Hkv, 128, dtype=torch.float32, device=dev)
+        kvq.kvq_query_relevance(w.dtype, w.B, w.Hq, w.Hkv, to_dev(gen.query(w, step=1)), rel)
+        scratch.set_relevance(rel)
+        base.set_relevance(rel)
+    scratch.quantize_page(Kd, Vd, bulk)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -319,6 +328,8 @@ def stream_main(a, w, torch, gen, kvq):
         c = kvq.Cache(cfg, device=dev)
         c.mem.copy_(base.mem)
         kvq.kvq_set_state(c.handle, bulk, 0)
+        if rel is not None:
+            c.set_relevance(rel)
         caches.append(c)
     qs, kts, vts = [], [], []
     for s in range(1, w.decode_steps + 1):
@@ -361,6 +372,7 @@ def stream_main(a, w, torch, gen, kvq):
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": 128, "ctx": bulk * PAGE, "decode_steps": w.decode_steps,
                    "boost_channels": w.boost, "layers_rotated": layers,
+                   "channel_ranking": "query-aware" if a.query_aware else "magnitude",
                    "step": "append + attention, " + ("two calls" if a.unfused else "fused")},
         "tokens_per_s": round(w.B / (total_ms / w.decode_steps / layers / 1e3), 1),
         "step_us": {"p10": round(float(np.percentile(step_ms, 10)) * 1e3, 2),

@@ -21,6 +21,8 @@ namespace kvq {
 namespace {
 
 constexpr int kThreads = 256;
+// 16 bytes as a native vector, so that arrays of them stay in registers
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 constexpr int kRowPad = 136;  // LDS row stride in u16 (272 B) to spread banks
 
 template <int DT>
@@ -88,17 +90,17 @@ __device__ __forceinline__ void quantize_page_body(uint8_t *__restrict__ pg,
     const PageLayout Ly = page_layout(k);
 
     // 1. Issue every load of the K and V tiles (16 B per thread per step).
-    uint4 kr[8], vr[8];
+    u4_t kr[8], vr[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         int i = tid + kThreads * j;  // 16-byte chunk: row i / 16, 8 channels (i % 16)
-        kr[j] = reinterpret_cast<const uint4 *>(ks)[i];
-        vr[j] = reinterpret_cast<const uint4 *>(vs)[i];
+        kr[j] = reinterpret_cast<const u4_t *>(ks)[i];
+        vr[j] = reinterpret_cast<const u4_t *>(vs)[i];
     }
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         int i = tid + kThreads * j;
-        *reinterpret_cast<uint4 *>(&tile[(i >> 4) * kRowPad + (i & 15) * 8]) = kr[j];
+        *reinterpret_cast<u4_t *>(&tile[(i >> 4) * kRowPad + (i & 15) * 8]) = kr[j];
     }
     __syncthreads();
 
@@ -212,7 +214,7 @@ __device__ __forceinline__ void quantize_page_body(uint8_t *__restrict__ pg,
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         int i = tid + kThreads * j;
-        *reinterpret_cast<uint4 *>(&tile[(i >> 4) * kRowPad + (i & 15) * 8]) = vr[j];
+        *reinterpret_cast<u4_t *>(&tile[(i >> 4) * kRowPad + (i & 15) * 8]) = vr[j];
     }
     __syncthreads();
     {
