@@ -61,30 +61,64 @@ __device__ __forceinline__ void group_params(float lo, float hi, int L, uint16_t
     inv = sf == 0.0f ? 0.0f : __fdiv_rn(1.0f, sf);
 }
 
+// code = clamp(rint((x - z) * inv), 0, L).  No branch for s == 0: then
+// inv == 0 and x - z is finite and >= 0 (z is the group minimum, the range is
+// finite), so the product is +-0 and the code 0, as the definition gives.
 __device__ __forceinline__ uint32_t quant_code(float x, float zf, float inv, int L) {
-    if (inv == 0.0f) return 0u;  // s == 0: every code is 0
     float d = __fsub_rn(x, zf);
     float t = __fmul_rn(d, inv);
-    float r = rintf(t);
-    r = r < 0.0f ? 0.0f : r;
-    r = r > (float)L ? (float)L : r;
+    float r = __builtin_amdgcn_fmed3f(rintf(t), 0.0f, (float)L);
     return (uint32_t)r;
+}
+
+// Decode the two stored values packed in one 32-bit word (lower address first).
+template <int DT>
+__device__ __forceinline__ float dec_lo(uint32_t w) { return dec<DT>((uint16_t)(w & 0xffffu)); }
+template <int DT>
+__device__ __forceinline__ float dec_hi(uint32_t w) { return dec<DT>((uint16_t)(w >> 16)); }
+
+// Running min / max.  The maximum keeps the first of equal values, so a zero
+// maximum keeps the sign it had first (as the element-by-element definition
+// does: the sign reaches the stored scale through max - min).  The minimum's
+// zero sign never matters (a zero minimum is stored as +0, and the query-aware
+// score takes |.| of its ranges), so it uses the plain min instruction.
+__device__ __forceinline__ void minmax(float x, float &lo, float &hi) {
+    lo = __builtin_fminf(x, lo);
+    hi = x > hi ? x : hi;
 }
 
 // One page: K and V rows [P][D] at ks / vs, the packed page written to pg;
 // rel: [D] channel relevance (query-aware ranking) or null (magnitude).
+//
+// Work split of the 256 threads (4 waves):
+//   Key statistics and codes by columns: wave g owns Key group g (32
+//     tokens), lane p the channel pair (2p, 2p + 1); its 64 values stay in
+//     registers from the statistics to the codes.
+//   Channel ranking: every thread counts the larger keys in one half.
+//   K lo plane: code pairs become nibbles, lane pairs bytes, staged in LDS in
+//     the page's own layout and copied out with 16-byte stores.
+//   K hi plane: thread (token, half) recomputes the 4-bit codes of its half of
+//     the boosted list and packs their upper bits.
+//   Value statistics and codes by rows: thread (token, half) owns 64 channels
+//     (two Value groups); codes are staged per (channel mod 16, token) and
+//     read back in the page's V_codes order.
 template <int DT>
 __device__ __forceinline__ void quantize_page_body(uint8_t *__restrict__ pg,
                                                    const uint16_t *__restrict__ ks,
                                                    const uint16_t *__restrict__ vs, int k,
                                                    const float *__restrict__ rel) {
-    __shared__ __align__(16) uint16_t tile[P * kRowPad];
-    __shared__ __align__(16) uint8_t codes[P * D];
-    __shared__ uint32_t amax[2][D];  // |K| bits, or fp32 bits of two group ranges
-    __shared__ uint64_t keys[D];
+    constexpr int kRow32 = kRowPad / 2;    // tile row stride in 32-bit words
+    constexpr int kVpkRow = 2 * P + 8;     // bytes per staged V row (padded: spreads banks)
+    __shared__ __align__(16) uint16_t tile[P * kRowPad];  // K tile, later the V tile
+    __shared__ __align__(16) float kst[2][P / GK][D];     // Key group min / max per channel
+    __shared__ __align__(16) uint8_t stage[16 * kVpkRow]; // K lo plane, later V code bytes
+    __shared__ __align__(16) float2 hpar[P / GK][D];      // (zf, inv) of boosted channels, by list slot
+    __shared__ __align__(16) uint64_t keys[D];
+    __shared__ __align__(16) int rankp[2][D];
     __shared__ uint8_t boosted[D];
-    __shared__ uint8_t idx[D];
-    __shared__ uint64_t mask0;
+    __shared__ __align__(16) uint8_t idx[D];
+    __shared__ int8_t jpos[D];
+    __shared__ int nbelow;
 
     const int tid = threadIdx.x;
     const PageLayout Ly = page_layout(k);
@@ -104,113 +138,131 @@ __device__ __forceinline__ void quantize_page_body(uint8_t *__restrict__ pg,
     }
     __syncthreads();
 
-    // 2. Key column statistics: thread (c, half) covers groups 2 half, 2 half + 1.
-    const int c = tid & (D - 1);
-    const int half = tid >> 7;
-    float glo[2], ghi[2];
-    uint32_t am = 0;
+    // 2. Key statistics: wave g = Key group g, lane p = channels 2p, 2p + 1.
+    const int p = tid & 63, g = tid >> 6;
+    uint32_t kw[GK];
+    const uint32_t *tile32 = reinterpret_cast<const uint32_t *>(tile);
 #pragma unroll
-    for (int gg = 0; gg < 2; gg++) {
-        int g = 2 * half + gg;
-        uint16_t h0 = tile[(g * GK) * kRowPad + c];
-        float lo = dec<DT>(h0), hi = lo;
-        am = max(am, (uint32_t)(h0 & 0x7fffu));
-        for (int t = 1; t < GK; t++) {
-            uint16_t h = tile[(g * GK + t) * kRowPad + c];
-            float x = dec<DT>(h);
-            lo = x < lo ? x : lo;
-            hi = x > hi ? x : hi;
-            am = max(am, (uint32_t)(h & 0x7fffu));
-        }
-        glo[gg] = lo;
-        ghi[gg] = hi;
+    for (int t = 0; t < GK; t++) kw[t] = tile32[(g * GK + t) * kRow32 + p];
+    float lo0 = dec_lo<DT>(kw[0]), hi0 = lo0, lo1 = dec_hi<DT>(kw[0]), hi1 = lo1;
+#pragma unroll
+    for (int t = 1; t < GK; t++) {
+        minmax(dec_lo<DT>(kw[t]), lo0, hi0);
+        minmax(dec_hi<DT>(kw[t]), lo1, hi1);
     }
-    if (rel) {
-        // ranges of this thread's groups 2 half and 2 half + 1, summed pairwise
-        amax[half][c] = __float_as_uint(
-            __fadd_rn(__fsub_rn(ghi[0], glo[0]), __fsub_rn(ghi[1], glo[1])));
-    } else {
-        amax[half][c] = am;
-    }
+    *reinterpret_cast<float2 *>(&kst[0][g][2 * p]) = make_float2(lo0, lo1);
+    *reinterpret_cast<float2 *>(&kst[1][g][2 * p]) = make_float2(hi0, hi1);
     __syncthreads();
+
+    // 3. Ranking keys: magnitude (largest |K| over the page, as fp32 bits of
+    // the group extremes) or |(summed group ranges) * relevance|; ties go to
+    // the lower channel.
     if (tid < D) {
+        const int c = tid;
         uint64_t sc;
         if (rel) {
-            const float diff = __fadd_rn(__uint_as_float(amax[0][tid]), __uint_as_float(amax[1][tid]));
-            sc = __float_as_uint(__fmul_rn(diff, rel[tid])) & 0x7fffffffu;
-        } else {
-            sc = max(amax[0][tid], amax[1][tid]);
-        }
-        keys[tid] = (sc << 8) | (uint64_t)(255 - tid);
-    }
-    __syncthreads();
-
-    // 3. Top-k by rank count; ascending list through wave ballots.
-    if (tid < D) {
-        const uint64_t my = keys[tid];
-        int rank = 0;
-        for (int j = 0; j < D; j++) rank += keys[j] > my ? 1 : 0;
-        bool b = rank < k;
-        boosted[tid] = b ? 1 : 0;
-        uint64_t m = __ballot(b);  // waves 0 and 1 are fully active here
-        if (tid == 0) mask0 = m;
-    }
-    __syncthreads();
-    if (tid < D) {
-        uint64_t m = __ballot(boosted[tid] != 0);
-        int lane = tid & 63;
-        int pos = __popcll(m & ((1ull << lane) - 1ull)) + (tid >= 64 ? __popcll(mask0) : 0);
-        if (boosted[tid]) idx[pos] = (uint8_t)tid;
-    }
-    __syncthreads();
-
-    // 4. Key codes and metadata.
+            float r[P / GK];
 #pragma unroll
-    for (int gg = 0; gg < 2; gg++) {
-        int g = 2 * half + gg;
-        int L = boosted[c] ? 15 : 3;
-        uint16_t sb, zb;
-        float zf, inv;
-        group_params<DT>(glo[gg], ghi[gg], L, sb, zb, zf, inv);
-        reinterpret_cast<uint16_t *>(pg + Ly.ks)[g * D + c] = sb;
-        reinterpret_cast<uint16_t *>(pg + Ly.kz)[g * D + c] = zb;
+            for (int gg = 0; gg < P / GK; gg++) r[gg] = __fsub_rn(kst[1][gg][c], kst[0][gg][c]);
+            const float diff = __fadd_rn(__fadd_rn(r[0], r[1]), __fadd_rn(r[2], r[3]));
+            sc = __float_as_uint(__fmul_rn(diff, rel[c])) & 0x7fffffffu;
+        } else {
+            uint32_t am = 0;
+#pragma unroll
+            for (int gg = 0; gg < P / GK; gg++)
+                am = max(am, max(__float_as_uint(kst[0][gg][c]) & 0x7fffffffu,
+                                 __float_as_uint(kst[1][gg][c]) & 0x7fffffffu));
+            sc = am;
+        }
+        keys[c] = (sc << 8) | (uint64_t)(255 - c);
+    }
+    __syncthreads();
+
+    // 4. Top-k by rank count (each thread counts one half of the keys), then
+    // the ascending list through wave ballots.
+    {
+        const int c = tid & (D - 1), part = tid >> 7;
+        const uint64_t my = keys[c];
+        int cnt = 0;
+        const u4_t *kv = reinterpret_cast<const u4_t *>(keys + 64 * part);
+#pragma unroll 8
+        for (int j = 0; j < 32; j++) {
+            const u4_t two = kv[j];
+            const uint64_t a = (uint64_t)two[0] | ((uint64_t)two[1] << 32);
+            const uint64_t b = (uint64_t)two[2] | ((uint64_t)two[3] << 32);
+            cnt += (a > my ? 1 : 0) + (b > my ? 1 : 0);
+        }
+        rankp[part][c] = cnt;
+    }
+    __syncthreads();
+    if (tid < D) {  // waves 0 and 1, fully active
+        const bool b = rankp[0][tid] + rankp[1][tid] < k;
+        boosted[tid] = b ? 1 : 0;
+        const uint64_t m = __ballot(b);
+        if (tid == 0) nbelow = __popcll(m);  // boosted channels below 64
+        const int pos = __popcll(m & ((1ull << (tid & 63)) - 1ull));
+        jpos[tid] = b ? (int8_t)pos : (int8_t)-1;  // wave 1 adds nbelow below
+    }
+    __syncthreads();
+    if (tid < D) {
+        const int pos = jpos[tid] + (tid >= 64 ? nbelow : 0);
+        if (jpos[tid] >= 0) {
+            idx[pos] = (uint8_t)tid;
+            jpos[tid] = (int8_t)pos;
+        }
+    }
+    __syncthreads();
+
+    // 5. Key metadata and codes (wave g, channels 2p, 2p + 1).
+    {
+        const int c0 = 2 * p;
+        const bool b0 = boosted[c0] != 0, b1 = boosted[c0 + 1] != 0;
+        const int L0 = b0 ? 15 : 3, L1 = b1 ? 15 : 3;
+        uint16_t sb0, zb0, sb1, zb1;
+        float zf0, inv0, zf1, inv1;
+        group_params<DT>(lo0, hi0, L0, sb0, zb0, zf0, inv0);
+        group_params<DT>(lo1, hi1, L1, sb1, zb1, zf1, inv1);
+        reinterpret_cast<uint32_t *>(pg + Ly.ks)[(g * D + c0) >> 1] = (uint32_t)sb0 | ((uint32_t)sb1 << 16);
+        reinterpret_cast<uint32_t *>(pg + Ly.kz)[(g * D + c0) >> 1] = (uint32_t)zb0 | ((uint32_t)zb1 << 16);
+        if (b0) hpar[g][jpos[c0]] = make_float2(zf0, inv0);
+        if (b1) hpar[g][jpos[c0 + 1]] = make_float2(zf1, inv1);
+        // lo plane: nibble (channels 2p, 2p + 1) per token, lane pairs make a
+        // byte (channels 4 (p / 2) .. + 3), staged as rows of 32 bytes
+#pragma unroll
         for (int t = 0; t < GK; t++) {
-            float x = dec<DT>(tile[(g * GK + t) * kRowPad + c]);
-            codes[(g * GK + t) * D + c] = (uint8_t)quant_code(x, zf, inv, L);
+            const uint32_t q0 = quant_code(dec_lo<DT>(kw[t]), zf0, inv0, L0);
+            const uint32_t q1 = quant_code(dec_hi<DT>(kw[t]), zf1, inv1, L1);
+            const uint32_t nib = (q0 & 3u) | ((q1 & 3u) << 2);
+            const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)nib, 0xB1, 0xF, 0xF, false);
+            const uint32_t byte = (p & 1) ? (other | (nib << 4)) : (nib | (other << 4));
+            stage[(g * GK + t) * 32 + (p >> 1)] = (uint8_t)byte;
         }
     }
     if (tid < k / 16)
         reinterpret_cast<uint4 *>(pg + Ly.kidx)[tid] = reinterpret_cast<const uint4 *>(idx)[tid];
     __syncthreads();
+    *reinterpret_cast<u4_t *>(pg + Ly.klo + 16 * tid) = reinterpret_cast<const u4_t *>(stage)[tid];
 
-    // 5. Pack the lo plane (16 B per thread) and the hi plane (k/4 B per token).
-    {
-        int t = tid >> 1, c0 = (tid & 1) * 64;
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            uint32_t acc = 0;
-            const uint8_t *src = &codes[t * D + c0 + 16 * q];
-#pragma unroll
-            for (int e = 0; e < 16; e++) acc |= ((uint32_t)src[e] & 3u) << (2 * e);
-            w[q] = acc;
-        }
-        *reinterpret_cast<uint4 *>(pg + Ly.klo + t * 32 + (tid & 1) * 16) =
-            make_uint4(w[0], w[1], w[2], w[3]);
-    }
-    if (tid < P && k > 0) {
-        int t = tid;
-        uint32_t *dst = reinterpret_cast<uint32_t *>(pg + Ly.khi + t * (k / 4));
+    // 6. K hi plane: thread (token t, half) covers list slots
+    // [half k / 2, half k / 2 + k / 2), eight per 16-bit word.
+    if (k > 0) {
+        const int t = tid >> 1, half = tid & 1, kg = t / GK;
+        uint16_t *dst = reinterpret_cast<uint16_t *>(pg + Ly.khi + t * (k / 4) + half * (k / 8));
         for (int q = 0; q < k / 16; q++) {
             uint32_t acc = 0;
-            for (int e = 0; e < 16; e++)
-                acc |= ((uint32_t)codes[t * D + idx[16 * q + e]] >> 2) << (2 * e);
-            dst[q] = acc;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const int j = half * (k / 2) + 8 * q + e;
+                const float2 pr = hpar[kg][j];
+                const float x = dec<DT>(tile[t * kRowPad + idx[j]]);
+                acc |= (quant_code(x, pr.x, pr.y, 15) >> 2) << (2 * e);
+            }
+            dst[q] = (uint16_t)acc;
         }
     }
     __syncthreads();
 
-    // 6. Values: tile <- V, then per (token, 32-channel group) statistics.
+    // 7. Values: tile <- V; thread (token t, half) reads its 64 channels.
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         int i = tid + kThreads * j;
@@ -218,45 +270,56 @@ __device__ __forceinline__ void quantize_page_body(uint8_t *__restrict__ pg,
     }
     __syncthreads();
     {
-        int t = tid >> 1;
+        const int t = tid >> 1, h2 = tid & 1;
+        uint32_t vw[32];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const u4_t x = *reinterpret_cast<const u4_t *>(&tile[t * kRowPad + 64 * h2 + 8 * i]);
+            vw[4 * i] = x[0];
+            vw[4 * i + 1] = x[1];
+            vw[4 * i + 2] = x[2];
+            vw[4 * i + 3] = x[3];
+        }
+        uint32_t code[64];
 #pragma unroll
         for (int gg = 0; gg < 2; gg++) {
-            int h = 2 * (tid & 1) + gg;
-            const uint16_t *row = &tile[t * kRowPad + h * GV];
-            float lo = dec<DT>(row[0]), hi = lo;
-            for (int e = 1; e < GV; e++) {
-                float x = dec<DT>(row[e]);
-                lo = x < lo ? x : lo;
-                hi = x > hi ? x : hi;
+            const uint32_t *w = vw + 16 * gg;  // channels 64 h2 + 32 gg + [0, 32)
+            float lo = dec_lo<DT>(w[0]), hi = lo;
+            minmax(dec_hi<DT>(w[0]), lo, hi);
+#pragma unroll
+            for (int e = 1; e < 16; e++) {
+                minmax(dec_lo<DT>(w[e]), lo, hi);
+                minmax(dec_hi<DT>(w[e]), lo, hi);
             }
             uint16_t sb, zb;
             float zf, inv;
             group_params<DT>(lo, hi, 3, sb, zb, zf, inv);
-            reinterpret_cast<uint16_t *>(pg + Ly.vs)[h * P + t] = sb;
-            reinterpret_cast<uint16_t *>(pg + Ly.vz)[h * P + t] = zb;
-            for (int e = 0; e < GV; e++)
-                codes[t * D + h * GV + e] = (uint8_t)quant_code(dec<DT>(row[e]), zf, inv, 3);
+            const int hh = 2 * h2 + gg;
+            reinterpret_cast<uint16_t *>(pg + Ly.vs)[hh * P + t] = sb;
+            reinterpret_cast<uint16_t *>(pg + Ly.vz)[hh * P + t] = zb;
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                code[32 * gg + 2 * e] = quant_code(dec_lo<DT>(w[e]), zf, inv, 3);
+                code[32 * gg + 2 * e + 1] = quant_code(dec_hi<DT>(w[e]), zf, inv, 3);
+            }
         }
+        // byte (channel class cl = c % 16, token t, half h2): the codes of
+        // channels 64 h2 + 16 m + cl, m = 0..3, at bits 2 m
+#pragma unroll
+        for (int cl = 0; cl < 16; cl++)
+            stage[cl * kVpkRow + 2 * t + h2] =
+                (uint8_t)(code[cl] | (code[16 + cl] << 2) | (code[32 + cl] << 4) | (code[48 + cl] << 6));
     }
     __syncthreads();
 
-    // 7. Pack Value codes: thread = one 16-byte block (step s, lane 16 G + cl).
+    // 8. V_codes: thread = one 16-byte block (32-token step s, lane 16 G + cl):
+    // words hold tokens (4G, 4G + 1), (4G + 2, 4G + 3), (16 + 4G, ..), (.., 16 + 4G + 3).
     {
-        int s = tid >> 6, lane = tid & 63, G = lane >> 4, cl = lane & 15;
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            int t0 = 32 * s + (q < 2 ? 4 * G + 2 * q : 16 + 4 * G + 2 * (q - 2));
-            uint32_t acc = 0;
-#pragma unroll
-            for (int n = 0; n < 8; n++) {
-                acc |= (uint32_t)codes[t0 * D + 16 * n + cl] << (2 * n);
-                acc |= (uint32_t)codes[(t0 + 1) * D + 16 * n + cl] << (16 + 2 * n);
-            }
-            w[q] = acc;
-        }
-        *reinterpret_cast<uint4 *>(pg + Ly.vc + 1024 * s + 16 * lane) =
-            make_uint4(w[0], w[1], w[2], w[3]);
+        const int s = tid >> 6, lane = tid & 63, G = lane >> 4, cl = lane & 15;
+        const uint8_t *row = stage + cl * kVpkRow + 2 * (32 * s + 4 * G);
+        const uint2 a = *reinterpret_cast<const uint2 *>(row);
+        const uint2 b = *reinterpret_cast<const uint2 *>(row + 32);
+        *reinterpret_cast<uint4 *>(pg + Ly.vc + 1024 * s + 16 * lane) = make_uint4(a.x, a.y, b.x, b.y);
     }
 }
 
