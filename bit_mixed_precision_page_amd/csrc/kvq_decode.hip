@@ -32,12 +32,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
                                  gps, max_splits, qscale, unit, split, nullptr);
 }
 
-// One workgroup of four waves per (sequence, query head).
+// D / (32 CPL) workgroups per output row.
+template <int PER, int CPL>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *__restrict__ ws_ml,
                                                                   const float *__restrict__ ws_acc,
                                                                   float *__restrict__ out, int n,
                                                                   int max_splits) {
-    combine_body(ws_ml, ws_acc, out, n, max_splits, blockIdx.x);
+    constexpr int kSlices = D / (32 * CPL);
+    combine_body<PER, CPL>(ws_ml, ws_acc, out, n, max_splits, blockIdx.x / kSlices,
+                           blockIdx.x % kSlices);
+}
+
+template <int PER, int CPL>
+hipError_t launch_combine(int rows, const float *ml, const float *acc, float *out, int n,
+                          int max_splits, hipStream_t st) {
+    hipLaunchKernelGGL((combine_kernel<PER, CPL>), dim3(rows * (D / (32 * CPL))),
+                       dim3(kCombineThreads), 0, st, ml, acc, out, n, max_splits);
+    return hipGetLastError();
 }
 
 // Resident workgroups of this instantiation on the whole device (occupancy API),
@@ -147,9 +158,13 @@ hipError_t launch_decode(const Geometry &G, uint8_t *cache, const uint16_t *q,
     if (e != hipSuccess) return e;
     if (ev_after && (e = hipEventRecord(ev_after, st)) != hipSuccess) return e;
     if (pl.total_splits > kMaxCombine) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(combine_kernel, dim3(G.B * G.Hq), dim3(kCombineThreads), 0, st, ml, acc, out,
-                       pl.total_splits, pl.max_splits);
-    return hipGetLastError();
+    const int rows = G.B * G.Hq;
+    const CombineShape cs = combine_shape(rows, pl.total_splits);
+    if (cs.cpl == 4)
+        return cs.per == 8 ? launch_combine<8, 4>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st)
+                           : launch_combine<kCombinePerMax, 4>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st);
+    return cs.per == 8 ? launch_combine<8, 1>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st)
+                       : launch_combine<kCombinePerMax, 1>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st);
 }
 
 }  // namespace kvq

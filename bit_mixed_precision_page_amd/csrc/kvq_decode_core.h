@@ -779,68 +779,88 @@ __device__ __forceinline__ void split_body(
     }
 }
 
-// One workgroup of four waves per (sequence, query head): the split weights
-// exp2(m_s - M) are computed once into LDS, each wave sums a quarter of the
-// splits for all 128 channels with four loads in flight per lane, and LDS
-// adds the four partial sums (the partials are read once, latency hidden).
-// Output row bq merges n partials (n == 0: a sequence without tokens, the
-// row is zero).
+// Split combine.  A workgroup covers one output row (sequence, query head)
+// or a slice of it: 32 lanes x CPL channels, so D / (32 CPL) workgroups per
+// row (many rows: CPL = 4, one workgroup per row; few rows with many splits:
+// CPL = 1, four).  Every load is issued first: thread (stripe, lane) reads
+// its channels from splits stripe, stripe + 8, ... (at most PER of them) into
+// registers, and the split statistics (m, l) two per thread; then the
+// maximum, the weights exp2(m_s - M) into LDS, the weighted sums of the eight
+// stripes and one LDS reduction.  Row bq merges n partials (n == 0: a
+// sequence without tokens, the row is zero).
 constexpr int kCombineThreads = 256;
+constexpr int kCombineStripes = kCombineThreads / 32;
+constexpr int kCombinePerMax = (kMaxCombine + kCombineStripes - 1) / kCombineStripes;
+static_assert(2 * kCombineThreads >= kMaxCombine, "two split statistics per thread");
+template <int CPL>
+struct CombineVec;
+template <>
+struct CombineVec<1> { typedef float T; };
+template <>
+struct CombineVec<4> { typedef f4_t T; };
+template <int PER, int CPL>
 __device__ __forceinline__ void combine_body(const float *__restrict__ ws_ml,
                                              const float *__restrict__ ws_acc,
                                              float *__restrict__ out, int n, int max_splits,
-                                             size_t bq) {
+                                             size_t bq, int slice) {
+    typedef typename CombineVec<CPL>::T vec;
     __shared__ float wsh[kMaxCombine];
     __shared__ float red[4], dred[4];
-    __shared__ float2 part[4][64];
+    __shared__ vec part[kCombineStripes][32];
     const int t = threadIdx.x, wv = t >> 6, ln = t & 63;
+    const int c = t & 31, stripe = t >> 5;
+    vec *o = reinterpret_cast<vec *>(out + bq * D + 32 * CPL * slice) + c;
     if (n == 0) {
-        if (t < 64) reinterpret_cast<float2 *>(out + bq * D)[ln] = make_float2(0.0f, 0.0f);
+        if (t < 32) *o = vec{};
         return;
     }
     const float *ml = ws_ml + bq * max_splits * 2;
-    float m = -INFINITY;
-    for (int s = t; s < n; s += kCombineThreads) m = fmaxf(m, ml[2 * s]);
-    m = wave_max(m);
+    const vec *a = reinterpret_cast<const vec *>(ws_acc + bq * max_splits * D + 32 * CPL * slice) + c;
+    vec x[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int sp = stripe + kCombineStripes * i;
+        x[i] = sp < n ? a[(size_t)sp * (D / CPL)] : vec{};
+    }
+    const int s1 = t + kCombineThreads;
+    const float m0 = t < n ? ml[2 * t] : -INFINITY, l0 = t < n ? ml[2 * t + 1] : 0.0f;
+    const float m1 = s1 < n ? ml[2 * s1] : -INFINITY, l1 = s1 < n ? ml[2 * s1 + 1] : 0.0f;
+    const float m = wave_max(fmaxf(m0, m1));
     if (ln == 0) red[wv] = m;
     __syncthreads();
     const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float den = 0.0f;
-    for (int s = t; s < n; s += kCombineThreads) {
-        const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-        wsh[s] = w;
-        den = fmaf(w, ml[2 * s + 1], den);
-    }
-    den = wave_sum(den);
+    const float w0 = t < n ? __builtin_amdgcn_exp2f(m0 - M) : 0.0f;
+    const float w1 = s1 < n ? __builtin_amdgcn_exp2f(m1 - M) : 0.0f;
+    if (t < n) wsh[t] = w0;
+    if (s1 < n) wsh[s1] = w1;
+    const float den = wave_sum(fmaf(w0, l0, w1 * l1));
     if (ln == 0) dred[wv] = den;
     __syncthreads();
-    const float2 *a = reinterpret_cast<const float2 *>(ws_acc + bq * max_splits * D) + ln;
-    float2 acc = make_float2(0.0f, 0.0f);
-    int s = wv;
-    for (; s + 12 < n; s += 16) {
-        const float2 x0 = a[(s + 0) * (D / 2)], x1 = a[(s + 4) * (D / 2)];
-        const float2 x2 = a[(s + 8) * (D / 2)], x3 = a[(s + 12) * (D / 2)];
-        const float w0 = wsh[s], w1 = wsh[s + 4], w2 = wsh[s + 8], w3 = wsh[s + 12];
-        acc.x = fmaf(w0, x0.x, fmaf(w1, x1.x, fmaf(w2, x2.x, fmaf(w3, x3.x, acc.x))));
-        acc.y = fmaf(w0, x0.y, fmaf(w1, x1.y, fmaf(w2, x2.y, fmaf(w3, x3.y, acc.y))));
-    }
-    for (; s < n; s += 4) {
-        const float2 x = a[s * (D / 2)];
-        acc.x = fmaf(wsh[s], x.x, acc.x);
-        acc.y = fmaf(wsh[s], x.y, acc.y);
-    }
-    part[wv][ln] = acc;
-    __syncthreads();
-    if (wv == 0) {
-        float2 r = part[0][ln];
+    vec acc{};
 #pragma unroll
-        for (int i = 1; i < 4; i++) {
-            r.x += part[i][ln].x;
-            r.y += part[i][ln].y;
-        }
-        const float inv = 1.0f / (dred[0] + dred[1] + dred[2] + dred[3]);
-        reinterpret_cast<float2 *>(out + bq * D)[ln] = make_float2(r.x * inv, r.y * inv);
+    for (int i = 0; i < PER; i++) {
+        const int sp = stripe + kCombineStripes * i;
+        if (sp < n) acc += wsh[sp] * x[i];
     }
+    part[stripe][c] = acc;
+    __syncthreads();
+    if (t < 32) {
+        vec r = part[0][t];
+#pragma unroll
+        for (int i = 1; i < kCombineStripes; i++) r += part[i][t];
+        *o = r / ((dred[0] + dred[1]) + (dred[2] + dred[3]));
+    }
+}
+
+// Combine kernel shape for rows x splits: (PER, CPL) and workgroups per row.
+struct CombineShape {
+    int per, cpl;
+};
+inline CombineShape combine_shape(int rows, int max_n) {
+    CombineShape c;
+    c.cpl = rows >= 256 ? 4 : 1;
+    c.per = max_n <= 8 * kCombineStripes ? 8 : kCombinePerMax;
+    return c;
 }
 
 }  // namespace

@@ -3,6 +3,8 @@
 // The per-launch plan (split counts and lengths per sequence) is a kernel
 // argument; the work of a split is the same code as for the dense cache
 // (kvq_decode_core.h).
+#include <algorithm>
+
 #include "kvq_decode_core.h"
 
 namespace kvq {
@@ -51,14 +53,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
                                 pl.gps, pl.max_splits, qscale, b * Hkv + h, split, table);
 }
 
-// Row bq = (sequence, query head) merges that sequence's S_b + W_b partials.
+// Row bq = (sequence, query head) merges that sequence's S_b + W_b partials;
+// D / (32 CPL) workgroups per row.
+template <int PER, int CPL>
 __global__ __launch_bounds__(kCombineThreads) void pool_combine_kernel(
     const float *__restrict__ ws_ml, const float *__restrict__ ws_acc, float *__restrict__ out,
     int Hq, int Hkv, const PoolPlan pl) {
-    const int b = blockIdx.x / Hq;
+    constexpr int kSlices = D / (32 * CPL);
+    const int bq = blockIdx.x / kSlices;
+    const int b = bq / Hq;
     const int n = (int)(pl.page_pref[b + 1] - pl.page_pref[b] + pl.win_pref[b + 1] -
                         pl.win_pref[b]) / Hkv;
-    combine_body(ws_ml, ws_acc, out, n, pl.max_splits, blockIdx.x);
+    combine_body<PER, CPL>(ws_ml, ws_acc, out, n, pl.max_splits, bq, blockIdx.x % kSlices);
+}
+
+template <int PER, int CPL>
+hipError_t launch_pool_combine(const Geometry &G, const float *ml, const float *acc, float *out,
+                               const PoolPlan &pl, hipStream_t st) {
+    hipLaunchKernelGGL((pool_combine_kernel<PER, CPL>), dim3(G.B * G.Hq * (D / (32 * CPL))),
+                       dim3(kCombineThreads), 0, st, ml, acc, out, G.Hq, G.Hkv, pl);
+    return hipGetLastError();
 }
 
 template <int DT, int G, int KH>
@@ -159,9 +173,16 @@ hipError_t launch_pool_decode(const Geometry &G, uint8_t *mem, const int32_t *ta
                        : plaunch1<BF16>(G, mem, table, kn, vn, q, ml, acc, pl, st);
     if (e != hipSuccess) return e;
     if (ev_after && (e = hipEventRecord(ev_after, st)) != hipSuccess) return e;
-    hipLaunchKernelGGL(pool_combine_kernel, dim3(G.B * G.Hq), dim3(kCombineThreads), 0, st, ml,
-                       acc, out, G.Hq, G.Hkv, pl);
-    return hipGetLastError();
+    int max_n = 0;
+    for (int b = 0; b < pl.n_seq; b++)
+        max_n = std::max(max_n, (int)(pl.page_pref[b + 1] - pl.page_pref[b] + pl.win_pref[b + 1] -
+                                      pl.win_pref[b]) / G.Hkv);
+    const CombineShape cs = combine_shape(G.B * G.Hq, max_n);
+    if (cs.cpl == 4)
+        return cs.per == 8 ? launch_pool_combine<8, 4>(G, ml, acc, out, pl, st)
+                           : launch_pool_combine<kCombinePerMax, 4>(G, ml, acc, out, pl, st);
+    return cs.per == 8 ? launch_pool_combine<8, 1>(G, ml, acc, out, pl, st)
+                       : launch_pool_combine<kCombinePerMax, 1>(G, ml, acc, out, pl, st);
 }
 
 }  // namespace kvq
