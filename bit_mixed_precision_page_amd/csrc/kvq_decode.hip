@@ -9,6 +9,16 @@ namespace {
 // 1-D grid: every page split of every (sequence, KV head) first, then the
 // window splits, so the hardware places the long page waves evenly before
 // the short window waves fill the remaining slots.
+//
+// dstate != null: a step whose counters live in device memory (dstate =
+// {pages, window tokens, finished-workgroup count, error}), so that its
+// launches have the same arguments at every step and can be replayed from a
+// captured graph.  The kernel derives the step's state (a full window was
+// flushed by the preceding quantize launch; the new token takes the next
+// window slot), covers the pages with page_splits splits of
+// ceil(4 pages / page_splits) groups (empty splits and window splits past the
+// last token write empty partials) and the last workgroup to finish stores
+// the new counters.
 template <int DT, int G, int KH>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target(G, KH)))) void decode_split_kernel(
     const uint8_t *__restrict__ cache, uint8_t *__restrict__ window_w,
@@ -16,7 +26,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
     const uint16_t *__restrict__ q, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, int Hkv, int max_pages, uint32_t page_bytes, int k,
     size_t res_base, int n_pages, int n_res, int page_splits, int gps, int win_splits, int max_splits,
-    float qscale) {
+    float qscale, int32_t *__restrict__ dstate) {
+    bool room = true;
+    if (dstate) {
+        const int np = dstate[0], nr = dstate[1];
+        const bool full = nr == R;
+        room = !full || np < max_pages;
+        n_pages = full && room ? np + 1 : np;
+        n_res = full ? (room ? 1 : R) : nr + 1;
+        slot = room ? n_res - 1 : -1;
+        gps = max(1, (4 * n_pages + page_splits - 1) / page_splits);
+    }
     const int n_units = gridDim.x / (page_splits + win_splits);
     int unit, split;
     if ((int)blockIdx.x < page_splits * n_units) {
@@ -30,6 +50,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
     split_body<DT, G, KH, false>(cache, window_w, knew, vnew, slot, q, ws_ml, ws_acc, Hkv,
                                  max_pages, page_bytes, k, res_base, n_pages, n_res, page_splits,
                                  gps, max_splits, qscale, unit, split, nullptr);
+    if (dstate && threadIdx.x == 0) {
+        // every other workgroup has finished (and read dstate at its start)
+        // when the count reaches the grid size
+        if (atomicAdd(reinterpret_cast<unsigned *>(dstate + 2), 1u) == gridDim.x - 1) {
+            dstate[0] = n_pages;
+            dstate[1] = n_res;
+            dstate[2] = 0;
+            if (!room) dstate[3] = 1;
+        }
+    }
+}
+
+// Device counters for graph-replayed steps.
+__global__ void state_init_kernel(int32_t *dstate, int n_pages, int n_res) {
+    dstate[0] = n_pages;
+    dstate[1] = n_res;
+    dstate[2] = 0;
+    dstate[3] = 0;
 }
 
 // D / (32 CPL) workgroups per output row.
@@ -80,7 +118,7 @@ hipError_t launch3(const Geometry &Gm, uint8_t *cache, const uint16_t *kn, const
                        acc, Gm.Hkv, Gm.max_pages, Gm.page_bytes, Gm.k, Gm.res_base,
                        pl.n_pages, pl.n_res, pl.page_splits, pl.groups_per_split,
                        pl.total_splits - pl.page_splits,
-                       pl.max_splits, Gm.scale * kLog2e);
+                       pl.max_splits, Gm.scale * kLog2e, pl.dstate);
     return hipGetLastError();
 }
 
@@ -142,6 +180,11 @@ int decode_slots(const Geometry &G) {
 size_t decode_workspace_bytes(const Geometry &G, int max_splits) {
     size_t rows = (size_t)G.B * G.Hq * max_splits;
     return rows * 2 * sizeof(float) + rows * D * sizeof(float);
+}
+
+hipError_t launch_state_init(int32_t *dstate, int n_pages, int n_res, hipStream_t st) {
+    hipLaunchKernelGGL(state_init_kernel, dim3(1), dim3(1), 0, st, dstate, n_pages, n_res);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode(const Geometry &G, uint8_t *cache, const uint16_t *q,

@@ -742,15 +742,19 @@ __device__ __forceinline__ void split_body(
     auto rs_of = [&](int gi) {
         return page_rsrc(page_ptr(min(gi, g1 - 1) >> 2), gi < g1 ? page_bytes : 0u);
     };
-    GroupRegs<KHE> ga, gb;
-    load_group<KH>(ga, rs_of(g0), O, g0 & 3);
-    for (int gi = g0;;) {
-        load_group<KH>(gb, rs_of(gi + 1), O, (gi + 1) & 3);
-        process(ga);
-        if (++gi >= g1) break;
-        load_group<KH>(ga, rs_of(gi + 1), O, (gi + 1) & 3);
-        process(gb);
-        if (++gi >= g1) break;
+    // (an empty range only occurs in a graph-replayed step: the split then
+    // writes an empty partial, m = -inf and l = 0)
+    if (g0 < g1) {
+        GroupRegs<KHE> ga, gb;
+        load_group<KH>(ga, rs_of(g0), O, g0 & 3);
+        for (int gi = g0;;) {
+            load_group<KH>(gb, rs_of(gi + 1), O, (gi + 1) & 3);
+            process(ga);
+            if (++gi >= g1) break;
+            load_group<KH>(ga, rs_of(gi + 1), O, (gi + 1) & 3);
+            process(gb);
+            if (++gi >= g1) break;
+        }
     }
 
     // --- partials: lane (r, R) owns head head_of(R, s), channels 16 n + r ---

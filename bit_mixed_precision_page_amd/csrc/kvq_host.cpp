@@ -371,6 +371,49 @@ int kvq_append_decode(kvq_cache *c, const void *k, const void *v, const void *q,
     return KVQ_OK;
 }
 
+int kvq_device_state_init(kvq_cache *c, int32_t *dev_state, void *stream) {
+    if (!c || !dev_state) return KVQ_EINVAL;
+    if (!aligned16(dev_state)) return KVQ_EALIGN;
+    return hip_status(kvq::launch_state_init(dev_state, c->n_pages, c->n_res,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int kvq_append_decode_device(kvq_cache *c, const void *k, const void *v, const void *q,
+                             float *out, void *workspace, size_t ws_bytes, int32_t *dev_state,
+                             void *stream) {
+    if (!c || !k || !v || !q || !out || !workspace || !dev_state) return KVQ_EINVAL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(out) ||
+        !aligned16(workspace) || !aligned16(dev_state))
+        return KVQ_EALIGN;
+    if (ws_bytes < kvq::decode_workspace_bytes(c->G, max_splits_of(c->G)))
+        return KVQ_EWORKSPACE;
+    // Page splits fixed for every replay: the override, or one round of
+    // resident waves sized for the host counters at this call (at least one,
+    // at most one per group of one more page than the cache holds now).
+    const int cap = std::min(kMaxSplits, 4 * std::min(c->G.max_pages, c->n_pages + 1));
+    int S;
+    if (c->splits_override > 0) {
+        S = c->splits_override;
+    } else {
+        const int units = c->G.B * c->G.Hkv;
+        const int per_unit = kvq::decode_slots(c->G) / units - kvq::R / 32;
+        S = per_unit >= 1 ? per_unit : (4 * (c->n_pages + 1) + kRoundGroups - 1) / kRoundGroups;
+    }
+    kvq::DecodePlan pl{};
+    pl.page_splits = std::max(1, std::min(S, cap));
+    pl.groups_per_split = 1;  // derived on the device from the counters
+    pl.total_splits = pl.page_splits + kvq::R / 32;
+    pl.max_splits = max_splits_of(c->G);
+    pl.dstate = dev_state;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = kvq::launch_flush_window_device(c->G, c->mem, dev_state, c->rel, st);
+    if (e != hipSuccess) return KVQ_EHIP;
+    return hip_status(kvq::launch_decode(c->G, c->mem, static_cast<const uint16_t *>(q), out,
+                                         workspace, pl, static_cast<const uint16_t *>(k),
+                                         static_cast<const uint16_t *>(v), 0, c->ev_before,
+                                         c->ev_after, st));
+}
+
 int kvq_set_decode_splits(kvq_cache *c, int32_t splits) {
     if (!c || splits < 0) return KVQ_EINVAL;
     c->splits_override = splits;

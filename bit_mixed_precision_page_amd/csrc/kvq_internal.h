@@ -68,6 +68,12 @@ hipError_t launch_quantize_pages(const Geometry &G, uint8_t *cache, const uint16
 // Same, with each unit's window as the source (one page per unit).
 hipError_t launch_flush_window(const Geometry &G, uint8_t *cache, int page, const float *rel,
                                hipStream_t stream);
+// Same, reading the counters from device memory ({pages, window tokens, ..}):
+// does nothing unless the window is full and a page is free.
+hipError_t launch_flush_window_device(const Geometry &G, uint8_t *cache, const int32_t *dstate,
+                                      const float *rel, hipStream_t stream);
+// dstate <- {n_pages, n_res, 0, 0}
+hipError_t launch_state_init(int32_t *dstate, int n_pages, int n_res, hipStream_t stream);
 // rel [B][Hkv][D] = sum over each KV head's query heads of |q| (q [B][Hq][D]).
 hipError_t launch_query_relevance(int dtype, const uint16_t *q, float *rel, int B, int Hq,
                                   int Hkv, hipStream_t stream);
@@ -85,6 +91,8 @@ struct DecodePlan {
     int groups_per_split;
     int total_splits;     // page_splits + ceil(n_res / 32) window splits
     int max_splits;       // workspace stride (splits per (b, hq))
+    int32_t *dstate;      // non-null: counters in device memory (graph-replayable step);
+                          // then total_splits = page_splits + R / 32
 };
 size_t decode_workspace_bytes(const Geometry &G, int max_splits);
 // Workgroups of the decode kernel the device holds at once (2048 without a device).

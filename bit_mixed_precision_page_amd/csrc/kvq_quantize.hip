@@ -323,12 +323,19 @@ __device__ __forceinline__ void quantize_page_body(uint8_t *__restrict__ pg,
     }
 }
 
-// Dense cache: page first_page + blockIdx.x of unit blockIdx.y.
+// Dense cache: page first_page + blockIdx.x of unit blockIdx.y (with dstate:
+// the window flush of a graph-replayed step, page dstate[0] when the window
+// holds dstate[1] == R tokens, nothing otherwise).
 template <int DT>
 __global__ __launch_bounds__(kThreads) void quantize_pages_kernel(
     uint8_t *__restrict__ cache, const uint16_t *__restrict__ k_src,
     const uint16_t *__restrict__ v_src, size_t src_unit_stride, int first_page, int n_new,
-    int max_pages, uint32_t page_bytes, int k, const float *__restrict__ rel) {
+    int max_pages, uint32_t page_bytes, int k, const float *__restrict__ rel,
+    const int32_t *__restrict__ dstate) {
+    if (dstate) {  // window flush of a graph-replayed step: only when it is due
+        if (dstate[1] != R || dstate[0] >= max_pages) return;
+        first_page = dstate[0];
+    }
     const int p = blockIdx.x;
     const int unit = blockIdx.y;
     uint8_t *pg = cache + ((size_t)unit * max_pages + first_page + p) * page_bytes;
@@ -462,11 +469,27 @@ hipError_t launch_quantize_pages(const Geometry &G, uint8_t *cache, const uint16
     if (G.dtype == F16)
         hipLaunchKernelGGL(quantize_pages_kernel<F16>, grid, dim3(kThreads), 0, stream, cache,
                            k_src, v_src, src_unit_stride, first_page, n_new, G.max_pages,
-                           G.page_bytes, G.k, rel);
+                           G.page_bytes, G.k, rel, nullptr);
     else
         hipLaunchKernelGGL(quantize_pages_kernel<BF16>, grid, dim3(kThreads), 0, stream, cache,
                            k_src, v_src, src_unit_stride, first_page, n_new, G.max_pages,
-                           G.page_bytes, G.k, rel);
+                           G.page_bytes, G.k, rel, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_flush_window_device(const Geometry &G, uint8_t *cache, const int32_t *dstate,
+                                      const float *rel, hipStream_t stream) {
+    const uint16_t *kw = reinterpret_cast<const uint16_t *>(cache + G.res_base);
+    const uint16_t *vw = kw + (size_t)R * D;
+    dim3 grid(1, G.B * G.Hkv);
+    if (G.dtype == F16)
+        hipLaunchKernelGGL(quantize_pages_kernel<F16>, grid, dim3(kThreads), 0, stream, cache, kw,
+                           vw, (size_t)2 * R * D, 0, 1, G.max_pages, G.page_bytes, G.k, rel,
+                           dstate);
+    else
+        hipLaunchKernelGGL(quantize_pages_kernel<BF16>, grid, dim3(kThreads), 0, stream, cache, kw,
+                           vw, (size_t)2 * R * D, 0, 1, G.max_pages, G.page_bytes, G.k, rel,
+                           dstate);
     return hipGetLastError();
 }
 

@@ -30,7 +30,8 @@ EXPORTS = ["kvq_cache_bytes", "kvq_page_bytes", "kvq_cache_create", "kvq_cache_d
            "kvq_pool_append_decode", "kvq_pool_release", "kvq_pool_get_seq",
            "kvq_pool_block_of", "kvq_pool_free_blocks", "kvq_pool_page_offset",
            "kvq_pool_window_offset", "kvq_pool_table_offset", "kvq_pool_set_kernel_events",
-           "kvq_set_channel_relevance", "kvq_query_relevance", "kvq_pool_set_channel_relevance"]
+           "kvq_set_channel_relevance", "kvq_query_relevance", "kvq_pool_set_channel_relevance",
+           "kvq_device_state_init", "kvq_append_decode_device"]
 
 
 class KvqError(RuntimeError):
@@ -100,6 +101,8 @@ _SIG = {
     "kvq_set_channel_relevance": [_vp, _vp],
     "kvq_query_relevance": [_i32, _i32, _i32, _i32, _vp, _vp, _vp],
     "kvq_pool_set_channel_relevance": [_vp, _vp],
+    "kvq_device_state_init": [_vp, _vp, _vp],
+    "kvq_append_decode_device": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp],
 }
 for _name, _args in _SIG.items():
     _f = getattr(_L, _name)
@@ -182,6 +185,17 @@ def kvq_append_decode(handle, k, v, q, out, workspace, ws_bytes, stream=None):
     _check(_L.kvq_append_decode(handle, _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(workspace),
                                 ws_bytes, _stream(stream), ctypes.byref(f)), "kvq_append_decode")
     return bool(f.value)
+
+
+def kvq_device_state_init(handle, dev_state, stream=None):
+    _check(_L.kvq_device_state_init(handle, _ptr(dev_state), _stream(stream)),
+           "kvq_device_state_init")
+
+
+def kvq_append_decode_device(handle, k, v, q, out, workspace, ws_bytes, dev_state, stream=None):
+    _check(_L.kvq_append_decode_device(handle, _ptr(k), _ptr(v), _ptr(q), _ptr(out),
+                                       _ptr(workspace), ws_bytes, _ptr(dev_state),
+                                       _stream(stream)), "kvq_append_decode_device")
 
 
 def kvq_set_decode_splits(handle, splits):
@@ -370,6 +384,16 @@ class Cache:
         """rel: [B][Hkv][128] float32 device tensor (kept alive by the caller), or None."""
         self._rel = rel
         kvq_set_channel_relevance(self.handle, rel)
+
+    def device_state(self, stream=None):
+        """A new int32[4] device state holding the current counters."""
+        st = torch.zeros(4, dtype=torch.int32, device=self.mem.device)
+        kvq_device_state_init(self.handle, st, stream)
+        return st
+
+    def append_decode_device(self, k, v, q, out, dev_state, stream=None):
+        kvq_append_decode_device(self.handle, k, v, q, out, self.ws, self.ws_bytes, dev_state,
+                                 stream)
 
     @property
     def state(self):

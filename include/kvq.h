@@ -148,6 +148,29 @@ int kvq_decode_attention(kvq_cache *cache, const void *q, float *out, void *work
 int kvq_append_decode(kvq_cache *cache, const void *k, const void *v, const void *q, float *out,
                       void *workspace, size_t ws_bytes, void *stream, int32_t *flushed);
 
+/* Graph-replayable decode step (same launches, same arguments, every step).
+   dev_state: device int32[4] = {pages, window tokens, internal counter (0),
+   error flag}, 16-byte aligned, owned by the caller.
+   kvq_device_state_init writes the handle's host counters into dev_state (a
+   kernel launch, so it may itself be captured).
+   kvq_append_decode_device is kvq_append_decode with the counters read from
+   and advanced in dev_state by the kernels themselves: a window flush launch
+   that acts only when the window is full, then the attention launches, whose
+   last finishing workgroup stores the new counters.  Its page split count is
+   fixed at the call (kvq_set_decode_splits, else one round of resident waves
+   for the host counters at that moment), so the launches it records into a
+   HIP graph stay valid for any later state.  The host counters of the handle
+   are NOT advanced: read dev_state back and call kvq_set_state before using
+   the other entry points again.  When a flush would need a page beyond
+   max_pages the kernels leave the cache unchanged, the step skips the new
+   token, and dev_state[3] becomes 1.  Results equal kvq_append_decode's up to
+   the rounding of a different split count.
+   Errors: KVQ_EINVAL, KVQ_EALIGN, KVQ_EWORKSPACE (argument checks only). */
+int kvq_device_state_init(kvq_cache *cache, int32_t *dev_state, void *stream);
+int kvq_append_decode_device(kvq_cache *cache, const void *k, const void *v, const void *q,
+                             float *out, void *workspace, size_t ws_bytes, int32_t *dev_state,
+                             void *stream);
+
 /* Number of page splits per (sequence, KV head) decode attention uses; a
    split covers consecutive 32-token page groups.  splits = 0 restores the
    automatic choice (one round of resident waves); otherwise it is clamped to

@@ -1,0 +1,121 @@
+"""Graph-replayed decode step (kvq_append_decode_device) through the C ABI.
+
+The step's counters live in device memory, so one captured HIP graph serves
+every later step.  Every replay is checked against eager calls on a twin cache
+fed the same tokens (page and window bytes bit-exact, attention within the
+split-count rounding bound) and against the CPU oracle (attention within
+max-abs 1e-3), with eager copies and synchronizations between the replays.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from bit_mixed_precision_page_amd import inputs as gen
+from gpu_util import Pair, dev, host
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+SPLIT_TOL = 1e-4  # different split counts change only the fp32 summation order
+W = gen.WORKLOADS
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _compare(graph, ref, out, st, step):
+    n_pages, n_res = ref.gpu.state
+    assert tuple(host(st)[:2]) == (n_pages, n_res), f"step {step}: device counters"
+    assert host(st)[2] == 0 and host(st)[3] == 0
+    assert (graph.pages()[:, :, :n_pages] == ref.pages()[:, :, :n_pages]).all(), \
+        f"step {step}: page bytes differ"
+    kg, vg = graph.windows()
+    kr, vr = ref.windows()
+    assert (kg[:, :, :n_res] == kr[:, :, :n_res]).all()
+    assert (vg[:, :, :n_res] == vr[:, :, :n_res]).all()
+
+
+def test_graph_replay_equals_eager_steps():
+    w = W["llama3_8b_decode"]
+    B = 2
+    graph = Pair(w, B=B, bulk_pages=2, window=124, max_pages=5, with_oracle=False)
+    ref = Pair(w, B=B, bulk_pages=2, window=124, max_pages=5)
+    st = graph.gpu.device_state()
+    torch.cuda.synchronize()
+    assert tuple(host(st)) == (2, 124, 0, 0)
+
+    def ref_step(step, kt, vt, q):
+        ref.append(kt, vt)
+        return ref.attention(q)
+
+    # step 0: the device-counter entry point called eagerly
+    kt, vt = gen.step_kv(w, 700)
+    kt, vt = kt[:B], vt[:B]
+    q = ref.query(0)
+    out = torch.empty(B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    graph.gpu.append_decode_device(dev(kt), dev(vt), dev(q), out, st)
+    torch.cuda.synchronize()
+    want = ref_step(0, kt, vt, q)
+    assert np.abs(host(out) - want).max() <= SPLIT_TOL
+    _compare(graph, ref, out, st, 0)
+
+    # capture one step; its inputs live in static buffers refilled before each replay
+    ks = torch.empty(B, w.Hkv, 128, dtype=torch.int16, device="cuda")
+    vs = torch.empty_like(ks)
+    qs = torch.empty(B, w.Hq, 128, dtype=torch.int16, device="cuda")
+    os_ = torch.empty(B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        graph.gpu.append_decode_device(ks, vs, qs, os_, st)
+    torch.cuda.synchronize()
+    assert tuple(host(st)[:2]) == (2, 125), "capture must not run the step"
+
+    for step in range(1, 9):  # window 126 .. 128, flush at step 4, then 1 .. 5
+        kt, vt = gen.step_kv(w, 700 + step)
+        kt, vt = kt[:B], vt[:B]
+        q = ref.query(step)
+        ks.copy_(dev(kt))
+        vs.copy_(dev(vt))
+        qs.copy_(dev(q))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = host(os_)
+        want = ref_step(step, kt, vt, q)
+        assert ref.flushes[-1] == (step == 4)
+        _compare(graph, ref, os_, st, step)
+        d_ref = np.abs(got - want).max()
+        d_ora = np.abs(got - ref.ora.attention(q)).max()
+        say(f"    replay {step}: state {tuple(int(x) for x in host(st)[:2])}, "
+            f"|graph - eager| = {d_ref:.2e}, "
+            f"|graph - oracle| = {d_ora:.2e}")
+        assert np.isfinite(got).all()
+        assert d_ref <= SPLIT_TOL
+        assert d_ora <= TOL
+
+
+def test_graph_step_full_cache_sets_flag():
+    """A full window with no free page: the step leaves the cache unchanged,
+    skips the token, raises the flag, and attends over the unchanged cache."""
+    w = W["llama3_8b_decode"]
+    B = 2
+    pair = Pair(w, B=B, bulk_pages=2, window=128, max_pages=2)
+    pages0 = pair.pages().copy()
+    kw0, vw0 = (a.copy() for a in pair.windows())
+    st = pair.gpu.device_state()
+    kt, vt = gen.step_kv(w, 900)
+    q = pair.query(9)
+    out = torch.empty(B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    pair.gpu.append_decode_device(dev(kt[:B]), dev(vt[:B]), dev(q), out, st)
+    torch.cuda.synchronize()
+    assert tuple(host(st)) == (2, 128, 0, 1)
+    assert (pair.pages()[:, :, :2] == pages0[:, :, :2]).all()
+    kw, vw = pair.windows()
+    assert (kw == kw0).all() and (vw == vw0).all()
+    err = np.abs(host(out) - pair.ora.attention(q)).max()
+    say(f"    full cache: flag set, max |gpu - oracle| = {err:.2e}")
+    assert err <= TOL
