@@ -6,9 +6,10 @@
 namespace kvq {
 namespace {
 
-// 1-D grid: every page split of every (sequence, KV head) first, then the
-// window splits, so the hardware places the long page waves evenly before
-// the short window waves fill the remaining slots.
+// 1-D grid of kDecodeWaves-wave workgroups: every page split of every
+// (sequence, KV head) first, then the window splits, so the hardware places
+// the long page workgroups evenly and the short window workgroups run as
+// they drain.
 //
 // dstate != null: a step whose counters live in device memory (dstate =
 // {pages, window tokens, finished-workgroup count, error}), so that its
@@ -16,11 +17,12 @@ namespace {
 // captured graph.  The kernel derives the step's state (a full window was
 // flushed by the preceding quantize launch; the new token takes the next
 // window slot), covers the pages with page_splits splits of
-// ceil(4 pages / page_splits) groups (empty splits and window splits past the
+// ceil(4 pages / (page_splits kDecodeWaves)) groups per wave (empty runs and
+// window waves past the
 // last token write empty partials) and the last workgroup to finish stores
 // the new counters.
 template <int DT, int G, int KH>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target(G, KH)))) void decode_split_kernel(
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(waves_target(G, KH)))) void decode_split_kernel(
     const uint8_t *__restrict__ cache, uint8_t *__restrict__ window_w,
     const uint16_t *__restrict__ knew, const uint16_t *__restrict__ vnew, int slot,
     const uint16_t *__restrict__ q, float *__restrict__ ws_ml,
@@ -35,7 +37,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
         n_pages = full && room ? np + 1 : np;
         n_res = full ? (room ? 1 : R) : nr + 1;
         slot = room ? n_res - 1 : -1;
-        gps = max(1, (4 * n_pages + page_splits - 1) / page_splits);
+        gps = max(1, (4 * n_pages + page_splits * kDecodeWaves - 1) / (page_splits * kDecodeWaves));
     }
     const int n_units = gridDim.x / (page_splits + win_splits);
     int unit, split;
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
         unit = l / win_splits;
         split = page_splits + l % win_splits;
     }
-    split_body<DT, G, KH, false>(cache, window_w, knew, vnew, slot, q, ws_ml, ws_acc, Hkv,
+    split_body<DT, G, KH, false, kDecodeWaves>(cache, window_w, knew, vnew, slot, q, ws_ml, ws_acc, Hkv,
                                  max_pages, page_bytes, k, res_base, n_pages, n_res, page_splits,
                                  gps, max_splits, qscale, unit, split, nullptr);
     if (dstate && threadIdx.x == 0) {
@@ -89,7 +91,7 @@ hipError_t launch_combine(int rows, const float *ml, const float *acc, float *ou
     return hipGetLastError();
 }
 
-// Resident workgroups of this instantiation on the whole device (occupancy API),
+// Resident waves of this instantiation on the whole device (occupancy API),
 // cached; 2048 when no device answers (host-only use).
 template <int DT, int G, int KH>
 int slots3() {
@@ -98,13 +100,13 @@ int slots3() {
     int per_cu = 0, dev = 0;
     hipDeviceProp_t prop;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<DT, G, KH>,
-                                                     64, 0) != hipSuccess ||
+                                                     64 * kDecodeWaves, 0) != hipSuccess ||
         hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
         per_cu <= 0) {
         (void)hipGetLastError();
         return 2048;
     }
-    cached = per_cu * prop.multiProcessorCount;
+    cached = per_cu * kDecodeWaves * prop.multiProcessorCount;
     return cached;
 }
 
@@ -113,7 +115,7 @@ hipError_t launch3(const Geometry &Gm, uint8_t *cache, const uint16_t *kn, const
                    int slot, const uint16_t *q, float *ml, float *acc, const DecodePlan &pl,
                    hipStream_t st) {
     dim3 grid(pl.total_splits * Gm.Hkv * Gm.B);
-    hipLaunchKernelGGL((decode_split_kernel<DT, G, KH>), grid, dim3(64), 0, st, cache, cache,
+    hipLaunchKernelGGL((decode_split_kernel<DT, G, KH>), grid, dim3(64 * kDecodeWaves), 0, st, cache, cache,
                        kn, vn, slot, q, ml,
                        acc, Gm.Hkv, Gm.max_pages, Gm.page_bytes, Gm.k, Gm.res_base,
                        pl.n_pages, pl.n_res, pl.page_splits, pl.groups_per_split,

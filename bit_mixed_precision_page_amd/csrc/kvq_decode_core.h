@@ -270,12 +270,26 @@ constexpr int waves_target(int G, int KH) {
 }
 
 
-// One split of one (sequence, KV head) unit: window split when split >=
-// page_splits, else groups [split * gps, split * gps + gps) of the unit's
-// pages.  With POOL the pages of sequence b live at pool blocks
-// table[b * max_pages + page] (block = the Hkv pages of one 128-token span),
-// otherwise at unit * max_pages + page of a dense array.
-template <int DT, int G, int KH, bool POOL>
+// Bytes of the per-wave LDS region of split_body.
+template <int G, int KH>
+constexpr int split_lds_bytes() {
+    constexpr int HQ = (G + 3) / 4, KHE = KH > 0 ? KH : 1, D_ = 128;
+    constexpr int page = G * D_ * 2 + HQ * 4 * 32 * 16 + HQ * KHE * 2 * 16 * 16 + 384 * 4 + D_ * 2 +
+                         HQ * 4 * 32 * 4;
+    constexpr int win = G * D_ * 4 + 32 * G * 4;
+    return page > win ? page : win;
+}
+
+// One split of one (sequence, KV head) unit, computed by a workgroup of NW
+// waves: window split when split >= page_splits (wave w of window split j
+// takes window tokens [32 (NW j + w), +32)), else wave w takes groups
+// [(NW split + w) gps, +gps) of the unit's pages.  With NW > 1 the waves'
+// partials (m, l, acc) are merged in LDS and the workgroup writes one
+// partial; with NW == 1 the wave writes its own.  With POOL the pages of
+// sequence b live at pool blocks table[b * max_pages + page] (block = the
+// Hkv pages of one 128-token span), otherwise at unit * max_pages + page of a
+// dense array.
+template <int DT, int G, int KH, bool POOL, int NW = 1>
 __device__ __forceinline__ void split_body(
     const uint8_t *__restrict__ cache, uint8_t *__restrict__ window_w,
     const uint16_t *__restrict__ knew, const uint16_t *__restrict__ vnew, int slot,
@@ -294,21 +308,76 @@ __device__ __forceinline__ void split_body(
     constexpr int O_ST = O_WH + HQ * KHE * 2 * 16 * 16;   // f32 [384] K scale 2^E | V scale | V zero
     constexpr int O_KZ = O_ST + 384 * 4;                  // u16 [D] K zero of the group
     constexpr int O_PX = O_KZ + D * 2;                    // f32 [HQ][4][32] softmax weights
-    constexpr int PAGE_LDS = O_PX + HQ * 4 * 32 * 4;
-    constexpr int WIN_LDS = G * D * 4 + 32 * G * 4;
-    __shared__ __align__(16) uint8_t lds[PAGE_LDS > WIN_LDS ? PAGE_LDS : WIN_LDS];
+    constexpr int LDSB = split_lds_bytes<G, KH>();
+    static_assert(LDSB >= O_PX + HQ * 4 * 32 * 4, "page LDS");
+    static_assert(NW == 1 || LDSB >= G * (D + 2) * 4, "merge area of a wave");
+    __shared__ __align__(16) uint8_t lds_all[NW][LDSB];
+    // wave index, wave-uniform (page descriptors derived from it stay scalar)
+    const int wv = NW > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
+    uint8_t *lds = lds_all[wv];
 
     const int h = unit % Hkv, b = unit / Hkv;
     const int Hq = Hkv * G;
-    const int lane = threadIdx.x, r = lane & 15, kb = lane >> 4;
+    const int lane = threadIdx.x & 63, r = lane & 15, kb = lane >> 4;
     const uint16_t *qg = q + ((size_t)b * Hq + h * G) * D;
+    // partial of this wave: global memory (NW == 1) or its LDS region, laid
+    // out [head][acc 0..127, m, l] (NW > 1), merged below
+    float *mine = reinterpret_cast<float *>(lds);
+    auto put_acc = [&](int hh, int c, float v) {
+        if constexpr (NW == 1) {
+            const size_t bq = (size_t)b * Hq + h * G + hh;
+            ws_acc[(bq * max_splits + split) * D + c] = v;
+        } else {
+            mine[hh * (D + 2) + c] = v;
+        }
+    };
+    auto put_ml = [&](int hh, float m, float l) {
+        if constexpr (NW == 1) {
+            const size_t bq = (size_t)b * Hq + h * G + hh;
+            ws_ml[(bq * max_splits + split) * 2 + 0] = m;
+            ws_ml[(bq * max_splits + split) * 2 + 1] = l;
+        } else {
+            mine[hh * (D + 2) + D] = m;
+            mine[hh * (D + 2) + D + 1] = l;
+        }
+    };
+    auto merge = [&]() {
+        if constexpr (NW > 1) {
+            __syncthreads();  // every wave's partial is in its LDS region
+            for (int i = threadIdx.x; i < G * D; i += 64 * NW) {
+                const int hh = i / D, c = i % D;
+                float mw[NW], M = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < NW; w++) {
+                    mw[w] = reinterpret_cast<const float *>(lds_all[w])[hh * (D + 2) + D];
+                    M = fmaxf(M, mw[w]);
+                }
+                float a = 0.0f, l = 0.0f;
+                if (M > -INFINITY) {
+#pragma unroll
+                    for (int w = 0; w < NW; w++) {
+                        const float *pw = reinterpret_cast<const float *>(lds_all[w]) + hh * (D + 2);
+                        const float f = __builtin_amdgcn_exp2f(mw[w] - M);
+                        a = fmaf(f, pw[c], a);
+                        l = fmaf(f, pw[D + 1], l);
+                    }
+                }
+                const size_t bq = (size_t)b * Hq + h * G + hh;
+                ws_acc[(bq * max_splits + split) * D + c] = a;
+                if (c == 0) {
+                    ws_ml[(bq * max_splits + split) * 2 + 0] = M;
+                    ws_ml[(bq * max_splits + split) * 2 + 1] = l;
+                }
+            }
+        }
+    };
 
     if (split >= page_splits) {
         // ---------------- window split: 32 exact tokens on the VALU ----------------
         // Every global load of the split (the token's K row, the V values of
         // this lane's two channels for all 32 tokens, q) is issued before any
         // arithmetic, so the split pays one memory latency.
-        const int w = split - page_splits;
+        const int w = (split - page_splits) * NW + wv;
         const int t0 = 32 * w;
         const int nt = min(32, n_res - t0);
         const uint16_t *kw = reinterpret_cast<const uint16_t *>(cache + res_base +
@@ -420,21 +489,18 @@ __device__ __forceinline__ void split_body(
                 acc[hh][1] = fmaf(p, v1, acc[hh][1]);
             }
         }
+        wave_sync();  // this wave's reads of its LDS region are done
 #pragma unroll
         for (int hh = 0; hh < G; hh++) {
-            size_t bq = (size_t)b * Hq + h * G + hh;
-            *reinterpret_cast<float2 *>(&ws_acc[(bq * max_splits + split) * D + 2 * lane]) =
-                make_float2(acc[hh][0], acc[hh][1]);
+            put_acc(hh, 2 * lane, acc[hh][0]);
+            put_acc(hh, 2 * lane + 1, acc[hh][1]);
         }
 #pragma unroll
         for (int j = 0; j < NHW; j++) {
             int hh = hs + 2 * j;
-            if (hh < G && tl == 0) {
-                size_t bq = (size_t)b * Hq + h * G + hh;
-                ws_ml[(bq * max_splits + split) * 2 + 0] = mrow[j];
-                ws_ml[(bq * max_splits + split) * 2 + 1] = lrow[j];
-            }
+            if (hh < G && tl == 0) put_ml(hh, mrow[j], lrow[j]);
         }
+        merge();
         return;
     }
 
@@ -727,7 +793,7 @@ __device__ __forceinline__ void split_body(
     };
 
     // groups [g0, g1) of this unit (four per page), two register sets in turn
-    const int g0 = split * gps;
+    const int g0 = (split * NW + wv) * gps;
     const int g1 = min(4 * n_pages, g0 + gps);
     const uint8_t *ubase = cache + (size_t)unit * max_pages * page_bytes;
     auto page_ptr = [&](int p) {
@@ -769,18 +835,15 @@ __device__ __forceinline__ void split_body(
 #pragma unroll
         for (int cg = 0; cg < 4; cg++) zg[cg] = shfl(z, 4 * kb + cg);
         const int hh = head_of<G>(kb, s);
+        if (s == 0 && NW > 1) wave_sync();  // this wave's reads of its LDS region are done
         if (G >= 4 || kb < G) {
-            const size_t bq = (size_t)b * Hq + h * G + hh;
-            float *dst = ws_acc + (bq * max_splits + split) * D;
 #pragma unroll
             for (int n = 0; n < 8; n++)
-                dst[16 * n + r] = acc[s][n] * ldexpf(1.0f, 24 - 2 * code_sig(n)) + zg[n >> 1];
-            if (r == 0) {
-                ws_ml[(bq * max_splits + split) * 2 + 0] = m_run[s] - (float)Eu;
-                ws_ml[(bq * max_splits + split) * 2 + 1] = l;
-            }
+                put_acc(hh, 16 * n + r, acc[s][n] * ldexpf(1.0f, 24 - 2 * code_sig(n)) + zg[n >> 1]);
+            if (r == 0) put_ml(hh, m_run[s] - (float)Eu, l);
         }
     }
+    merge();
 }
 
 // Split combine.  A workgroup covers one output row (sequence, query head)

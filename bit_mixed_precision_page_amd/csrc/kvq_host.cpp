@@ -95,26 +95,30 @@ kvq::DecodePlan plan_of(const kvq_cache *c) {
     pl.n_res = c->n_res;
     pl.max_splits = max_splits_of(c->G);
     if (c->n_pages > 0) {
-        int S;
+        constexpr int NW = kvq::kDecodeWaves;
+        const int groups = 4 * c->n_pages;
+        int S;  // page splits (workgroups of NW waves, one run of groups each)
         if (c->splits_override > 0) {
             S = c->splits_override;
         } else {
-            // One round of resident single-wave workgroups (occupancy of this
-            // kernel instance x compute units), shared with the window
-            // splits, with equal groups per split.  When the units alone fill
-            // more than a round, splits of about kRoundGroups groups run in
-            // several rounds and the hardware's dispatch balances them.
-            int units = c->G.B * c->G.Hkv;
-            int win = (c->n_res + 31) / 32;
-            int per_unit = kvq::decode_slots(c->G) / units - win;
-            S = per_unit >= 1 ? per_unit : (4 * c->n_pages + kRoundGroups - 1) / kRoundGroups;
+            // One round of resident waves (occupancy of this kernel instance
+            // x compute units) of page runs with equal groups per run; the
+            // short window splits follow as the page workgroups drain (a
+            // measured 2-3 % faster than sharing the round with them, and the
+            // split count does not depend on the window length).  When the
+            // units alone fill more than a round, runs of about kRoundGroups
+            // groups fill several rounds and the hardware's dispatch balances
+            // them.
+            const int units = c->G.B * c->G.Hkv;
+            const int per_unit = kvq::decode_slots(c->G) / units;
+            S = per_unit >= NW ? per_unit / NW
+                               : (groups + kRoundGroups * NW - 1) / (kRoundGroups * NW);
         }
-        const int groups = 4 * c->n_pages;
-        S = std::max(1, std::min(S, std::min(groups, kMaxSplits)));
-        pl.groups_per_split = (groups + S - 1) / S;
-        pl.page_splits = (groups + pl.groups_per_split - 1) / pl.groups_per_split;
+        S = std::max(1, std::min(S, std::min((groups + NW - 1) / NW, kMaxSplits)));
+        pl.groups_per_split = (groups + S * NW - 1) / (S * NW);  // per wave
+        pl.page_splits = (groups + pl.groups_per_split * NW - 1) / (pl.groups_per_split * NW);
     }
-    pl.total_splits = pl.page_splits + (c->n_res + 31) / 32;
+    pl.total_splits = pl.page_splits + (c->n_res + 32 * kvq::kDecodeWaves - 1) / (32 * kvq::kDecodeWaves);
     return pl;
 }
 
@@ -157,20 +161,20 @@ kvq::PoolPlan pool_plan(const kvq_pool *p, const int *slot_of) {
     pl.n_seq = G.B;
     pl.max_splits = max_splits_of(G);
     int64_t unit_groups = 0;
-    int units_with_pages = 0, max_groups = 0, win_wgs = 0;
+    int units_with_pages = 0, max_groups = 0;
     for (int b = 0; b < G.B; b++) {
         if (!p->live[b]) continue;
         unit_groups += (int64_t)4 * p->n_pages[b] * G.Hkv;
         units_with_pages += p->n_pages[b] > 0 ? G.Hkv : 0;
         max_groups = std::max(max_groups, 4 * p->n_pages[b]);
-        win_wgs += G.Hkv * ((p->n_res[b] + 31) / 32);
     }
-    // One round of resident waves shared with the window splits, equal
-    // groups per split across all sequences; several rounds of about
-    // kRoundGroups groups when the units alone fill more than a round.
+    // One round of resident waves of page splits (the window splits follow
+    // as they drain), equal groups per split across all sequences; several
+    // rounds of about kRoundGroups groups when the units alone fill more than
+    // a round.
     int gps = 1;
     if (units_with_pages > 0) {
-        const int target = kvq::pool_decode_slots(G) - win_wgs;
+        const int target = kvq::pool_decode_slots(G);
         if (target >= units_with_pages)
             gps = (int)std::max<int64_t>(1, (unit_groups + target - 1) / target);
         else
@@ -389,20 +393,22 @@ int kvq_append_decode_device(kvq_cache *c, const void *k, const void *v, const v
         return KVQ_EWORKSPACE;
     // Page splits fixed for every replay: the override, or one round of
     // resident waves sized for the host counters at this call (at least one,
-    // at most one per group of one more page than the cache holds now).
-    const int cap = std::min(kMaxSplits, 4 * std::min(c->G.max_pages, c->n_pages + 1));
+    // at most one wave per group of one more page than the cache holds now).
+    constexpr int NW = kvq::kDecodeWaves;
+    const int cap = std::min(kMaxSplits, (4 * std::min(c->G.max_pages, c->n_pages + 1) + NW - 1) / NW);
     int S;
     if (c->splits_override > 0) {
         S = c->splits_override;
     } else {
         const int units = c->G.B * c->G.Hkv;
-        const int per_unit = kvq::decode_slots(c->G) / units - kvq::R / 32;
-        S = per_unit >= 1 ? per_unit : (4 * (c->n_pages + 1) + kRoundGroups - 1) / kRoundGroups;
+        const int per_unit = kvq::decode_slots(c->G) / units;
+        S = per_unit >= NW ? per_unit / NW
+                           : (4 * (c->n_pages + 1) + kRoundGroups * NW - 1) / (kRoundGroups * NW);
     }
     kvq::DecodePlan pl{};
     pl.page_splits = std::max(1, std::min(S, cap));
     pl.groups_per_split = 1;  // derived on the device from the counters
-    pl.total_splits = pl.page_splits + kvq::R / 32;
+    pl.total_splits = pl.page_splits + (kvq::R + 32 * NW - 1) / (32 * NW);
     pl.max_splits = max_splits_of(c->G);
     pl.dstate = dev_state;
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -95,7 +95,11 @@ struct DecodePlan {
                           // then total_splits = page_splits + R / 32
 };
 size_t decode_workspace_bytes(const Geometry &G, int max_splits);
-// Workgroups of the decode kernel the device holds at once (2048 without a device).
+// Waves per workgroup of the dense decode kernel: each wave streams its own
+// run of groups (or 32 window tokens) and the workgroup merges the waves'
+// partials in LDS, so one split = kDecodeWaves runs.
+constexpr int kDecodeWaves = 4;
+// Waves of the decode kernel the device holds at once (2048 without a device).
 int decode_slots(const Geometry &G);
 // knew, vnew ([B][Hkv][D]) and slot >= 0: the newest window token (slot) is
 // read from knew / vnew and written into the window by the kernel itself (a

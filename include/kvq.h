@@ -171,11 +171,14 @@ int kvq_append_decode_device(kvq_cache *cache, const void *k, const void *v, con
                              float *out, void *workspace, size_t ws_bytes, int32_t *dev_state,
                              void *stream);
 
-/* Number of page splits per (sequence, KV head) decode attention uses; a
-   split covers consecutive 32-token page groups.  splits = 0 restores the
-   automatic choice (one round of resident waves); otherwise it is clamped to
-   [1, min(4 n_pages, 256)] at each call.  Results do not depend on it beyond
-   rounding. */
+/* Number of page splits per (sequence, KV head) decode attention uses.  A
+   split is one workgroup of four waves; each wave covers a run of
+   ceil(4 n_pages / (4 splits)) consecutive 32-token page groups and the
+   workgroup merges the four partial results, so the split count in effect is
+   ceil(4 n_pages / (4 run)).  splits = 0 restores the automatic choice (one
+   round of resident waves); otherwise it is clamped to
+   [1, min(ceil(4 n_pages / 4), 256)] at each call.  Results do not depend on
+   it beyond rounding. */
 int kvq_set_decode_splits(kvq_cache *cache, int32_t splits);
 
 /* The page split count the next kvq_decode_attention call will use. */

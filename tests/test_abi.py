@@ -166,14 +166,15 @@ def test_decode_split_choice(kvq):
     h, c = _handle(kvq, max_pages=64)
     kvq.kvq_set_state(h, 63, 128)
     auto = kvq.kvq_get_decode_splits(h)
-    groups = 4 * 63  # splits cover 32-token page groups
-    assert 1 <= auto <= min(groups, 256)
-    for s, want in [(1, 1), (7, 7), (63, 63), (100, 100), (1000, 252)]:
+    groups = 4 * 63  # runs of 32-token page groups, four runs (waves) per split
+    NW = 4
+    assert 1 <= auto <= min(-(-groups // NW), 256)
+    for s, want in [(1, 1), (7, 7), (20, 20), (63, 63), (100, 63), (1000, 63)]:
         kvq.kvq_set_decode_splits(h, s)
         got = kvq.kvq_get_decode_splits(h)
-        # groups per split = ceil(252 / s); splits = ceil(252 / groups per split)
-        gps = -(-groups // want)
-        assert got == -(-groups // gps)
+        # groups per run = ceil(252 / (4 s)); splits = ceil(252 / (4 run))
+        run = -(-groups // (NW * want))
+        assert got == -(-groups // (NW * run))
     kvq.kvq_set_decode_splits(h, 0)
     assert kvq.kvq_get_decode_splits(h) == auto
     kvq.kvq_cache_destroy(h)
