@@ -83,6 +83,50 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *_
                            blockIdx.x % kSlices);
 }
 
+// Few splits per row: one wave per output row (sequence, query head).  Each
+// lane issues every load of its row at once -- the n split statistics
+// (the same address in every lane, one request per wave) and its two
+// channels of each partial -- so a row costs one memory round trip, with no
+// LDS and no barrier.
+template <int NMAX>
+__global__ __launch_bounds__(256) void combine_wave_kernel(const float *__restrict__ ws_ml,
+                                                           const float *__restrict__ ws_acc,
+                                                           float *__restrict__ out, int rows, int n,
+                                                           int max_splits) {
+    const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const float2 *ml = reinterpret_cast<const float2 *>(ws_ml + (size_t)row * max_splits * 2);
+    const float *a = ws_acc + (size_t)row * max_splits * D + 2 * lane;
+    float2 st[NMAX], x[NMAX];
+#pragma unroll
+    for (int s = 0; s < NMAX; s++) {
+        st[s] = s < n ? ml[s] : make_float2(-INFINITY, 0.0f);
+        x[s] = s < n ? *reinterpret_cast<const float2 *>(a + (size_t)s * D) : make_float2(0.0f, 0.0f);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NMAX; s++) M = fmaxf(M, st[s].x);
+    float den = 0.0f, ax = 0.0f, ay = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NMAX; s++) {
+        const float w = s < n ? __builtin_amdgcn_exp2f(st[s].x - M) : 0.0f;
+        den = fmaf(w, st[s].y, den);
+        ax = fmaf(w, x[s].x, ax);
+        ay = fmaf(w, x[s].y, ay);
+    }
+    *reinterpret_cast<float2 *>(out + (size_t)row * D + 2 * lane) =
+        den > 0.0f ? make_float2(ax / den, ay / den) : make_float2(0.0f, 0.0f);
+}
+
+template <int NMAX>
+hipError_t launch_combine_wave(int rows, const float *ml, const float *acc, float *out, int n,
+                               int max_splits, hipStream_t st) {
+    hipLaunchKernelGGL((combine_wave_kernel<NMAX>), dim3((rows + 3) / 4), dim3(256), 0, st, ml, acc,
+                       out, rows, n, max_splits);
+    return hipGetLastError();
+}
+
 template <int PER, int CPL>
 hipError_t launch_combine(int rows, const float *ml, const float *acc, float *out, int n,
                           int max_splits, hipStream_t st) {
@@ -204,6 +248,10 @@ hipError_t launch_decode(const Geometry &G, uint8_t *cache, const uint16_t *q,
     if (ev_after && (e = hipEventRecord(ev_after, st)) != hipSuccess) return e;
     if (pl.total_splits > kMaxCombine) return hipErrorInvalidValue;
     const int rows = G.B * G.Hq;
+    if (pl.total_splits <= 16)
+        return launch_combine_wave<16>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st);
+    if (pl.total_splits <= 32)
+        return launch_combine_wave<32>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st);
     const CombineShape cs = combine_shape(rows, pl.total_splits);
     if (cs.cpl == 4)
         return cs.per == 8 ? launch_combine<8, 4>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st)
