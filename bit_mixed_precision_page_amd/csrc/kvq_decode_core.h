@@ -22,8 +22,10 @@
 //      duplicate work.  Boosted channels (Kitty abstract: two uniform 2-bit
 //      planes per mixed-precision Key page) add a contraction of the hi plane
 //      against 4 w of the listed channels.  The zero-point term q . z per
-//      group and head is a VALU dot product: each lane holds q' of eight
-//      channels for its row's head, and a row sum over 16 lanes finishes it.
+//      group and head is a VALU dot product: each lane holds the raw q of
+//      eight channels for its row's head and takes four packed two-element
+//      dot products with the raw Key zeros (exact products, fp32 sums); a row
+//      sum over 16 lanes finishes it.
 //  PV  (16 rows = 4 heads x 4 Value groups) x (32 tokens x 16 channels): the
 //      A operand is p * s_v (softmax weight times the token's Value scale for
 //      the group), split hi/lo; p reaches that layout through a 512-byte LDS
@@ -92,6 +94,17 @@ __device__ __forceinline__ f4_t mfma_dt(u4_t a, u4_t b, f4_t c) {
 }
 
 typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 hf2_t __attribute__((ext_vector_type(2)));
+// c + a.lo b.lo + a.hi b.hi for two packed dtype pairs (products exact in fp32)
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    if constexpr (DT == F16)
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(hf2_t, a), __builtin_bit_cast(hf2_t, b), c, false);
+    else
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2_t, a), __builtin_bit_cast(bf2_t, b), c,
+                                                false);
+}
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 // fp16 pair of (a, b), round to nearest even (one v_cvt_pk_f16_f32).
 __device__ __forceinline__ uint32_t pack_rne(float a, float b) {
@@ -274,8 +287,8 @@ constexpr int waves_target(int G, int KH) {
 template <int G, int KH>
 constexpr int split_lds_bytes() {
     constexpr int HQ = (G + 3) / 4, KHE = KH > 0 ? KH : 1, D_ = 128;
-    constexpr int page = G * D_ * 2 + HQ * 4 * 32 * 16 + HQ * KHE * 2 * 16 * 16 + 384 * 4 + D_ * 2 +
-                         HQ * 4 * 32 * 4;
+    constexpr int page = G * D_ * 2 + HQ * 4 * 32 * 16 + HQ * KHE * 2 * 16 * 16 + 416 * 4 + D_ * 2 +
+                         HQ * 4 * 32 * 4 + (KH > 0 ? G * D_ * 4 : 0);
     constexpr int win = G * D_ * 4 + 32 * G * 4;
     return page > win ? page : win;
 }
@@ -305,11 +318,14 @@ __device__ __forceinline__ void split_body(
     constexpr int O_Q = 0;                                // u16 [G][D] raw q
     constexpr int O_WL = O_Q + G * D * 2;                 // u4 [HQ][4 m][2 x][4 R][4 kb] lo-plane weights
     constexpr int O_WH = O_WL + HQ * 4 * 32 * 16;         // u32 [HQ][KHE][2 x][4 R][4 kb][4] hi plane
-    constexpr int O_ST = O_WH + HQ * KHE * 2 * 16 * 16;   // f32 [384] K scale 2^E | V scale | V zero
-    constexpr int O_KZ = O_ST + 384 * 4;                  // u16 [D] K zero of the group
+    // f32 [416] K scale 2^E [128] | V scale [4 groups][36] | V zero [4][36]
+    // (rows padded to 36: the PV-side reads of four groups hit four banks)
+    constexpr int O_ST = O_WH + HQ * KHE * 2 * 16 * 16;
+    constexpr int O_KZ = O_ST + 416 * 4;                  // u16 [D] K zero of the group
     constexpr int O_PX = O_KZ + D * 2;                    // f32 [HQ][4][32] softmax weights
+    constexpr int O_QF = O_PX + HQ * 4 * 32 * 4;          // f32 [G][D] q' (boosted-channel gathers)
     constexpr int LDSB = split_lds_bytes<G, KH>();
-    static_assert(LDSB >= O_PX + HQ * 4 * 32 * 4, "page LDS");
+    static_assert(LDSB >= O_QF + (KH > 0 ? G * D * 4 : 0), "page LDS");
     static_assert(NW == 1 || LDSB >= G * (D + 2) * 4, "merge area of a wave");
     __shared__ __align__(16) uint8_t lds_all[NW][LDSB];
     // wave index, wave-uniform (page descriptors derived from it stay scalar)
@@ -511,8 +527,17 @@ __device__ __forceinline__ void split_body(
     uint16_t *kz = reinterpret_cast<uint16_t *>(lds + O_KZ);
     float *px = reinterpret_cast<float *>(lds + O_PX);
 
-    for (int ch = lane; ch < G * (D / 8); ch += 64)
-        *reinterpret_cast<uint4 *>(qr + 8 * ch) = *reinterpret_cast<const uint4 *>(qg + 8 * ch);
+    float *qf = reinterpret_cast<float *>(lds + O_QF);
+    for (int ch = lane; ch < G * (D / 8); ch += 64) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(qg + 8 * ch);
+        *reinterpret_cast<uint4 *>(qr + 8 * ch) = v;
+        if constexpr (KH > 0) {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                qf[8 * ch + e] = dec<DT>((uint16_t)(w[e >> 1] >> (16 * (e & 1)))) * qscale;
+        }
+    }
     wave_sync();
     auto qv = [&](int hh, int c) { return dec<DT>(qr[hh * D + c]) * qscale; };
 
@@ -539,18 +564,28 @@ __device__ __forceinline__ void split_body(
                                        : 1.0f / (float)(1 << (2 * code_sig(e >> 1)));
             qpp[s][e] = qv(hh, pcb + (e >> 1) + 8 * (e & 1)) * sig;
         }
-    // q' of channels 8 r + [0, 8) for the head of row kb: the zero-point term
-    float qz[HQ][8];
+    // raw q pairs of channels 8 r + [0, 8) for the head of row kb: the
+    // zero-point term
+    uint32_t qz[HQ][4];
 #pragma unroll
-    for (int s = 0; s < HQ; s++)
+    for (int s = 0; s < HQ; s++) {
+        const u4_t v = *reinterpret_cast<const u4_t *>(qr + head_of<G>(kb, s) * D + 8 * r);
 #pragma unroll
-        for (int e = 0; e < 8; e++) qz[s][e] = qv(head_of<G>(kb, s), 8 * r + e);
+        for (int i = 0; i < 4; i++) qz[s][i] = v[i];
+    }
 
     // Hi-plane producer role: k block hkb, row block hR, operand dword hq; its
     // boosted slots are j0 = 32 ms + 16 (hkb / 2) + 4 (hkb % 2) + hq and j0 + 8,
     // at mantissa bits 2 sig_hi with sig_hi = 2 + (hq & 1).
     const int hkb = lane >> 4, hR = (lane >> 2) & 3, hq = lane & 3;
     const float fh = (hq & 1) ? 4.0f / 64.0f : 4.0f / 16.0f;
+    // ... times 0 for slots past the k listed channels (their index bytes are 0)
+    float fhs[KHE][2];
+#pragma unroll
+    for (int ms = 0; ms < KHE; ms++)
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+            fhs[ms][t] = 32 * ms + 16 * (hkb >> 1) + 4 * (hkb & 1) + hq + 8 * t < k ? fh : 0.0f;
 
     LaneOffs<KHE> O;
     O.klo = (int)Ly.klo + r * 32 + 8 * kb;
@@ -571,7 +606,8 @@ __device__ __forceinline__ void split_body(
         }
     }
     // staging destinations of this lane's metadata chunk
-    const int st_o = lane < 16 ? 8 * lane : 128 + 8 * (lane - 32);
+    const int st_o = lane < 16 ? 8 * lane
+                               : 128 + 144 * ((lane - 32) >> 4) + 36 * ((lane >> 2) & 3) + 8 * (lane & 3);
     const bool st_f32 = lane < 16 || lane >= 32;
 
     float acc[HQ][8];  // lane (r, R): head head_of(R, s), channel 16 n + r
@@ -594,12 +630,10 @@ __device__ __forceinline__ void split_body(
         for (int ms = 0; ms < KH; ms++)
 #pragma unroll
             for (int t = 0; t < 2; t++) {
-                const int j = 32 * ms + 16 * (hkb >> 1) + 4 * (hkb & 1) + hq + 8 * t;
                 const int c = (int)(Gr.ib[ms][t] & 127u);
                 hc[ms][t] = c;
 #pragma unroll
-                for (int s = 0; s < HQ; s++)
-                    qh[s][ms][t] = j < k ? qv(head_of<G>(hR, s), c) * fh : 0.0f;
+                for (int s = 0; s < HQ; s++) qh[s][ms][t] = qf[head_of<G>(hR, s) * D + c] * fhs[ms][t];
             }
         // ---- metadata: exponents from the largest scales (integer max of the
         // bits: scales are never negative), then fp32 copies into LDS ----
@@ -675,19 +709,17 @@ __device__ __forceinline__ void split_body(
                     wh[64] = lo;
                 }
             }
-            // ---- zero-point term per head: q' . K zero, eight channels per lane ----
+            // ---- zero-point term per head: q . K zero (pairwise dot products
+            // of the raw values, exact products), eight channels per lane ----
             float bias[HQ];
             {
                 const u4_t zr = *reinterpret_cast<const u4_t *>(kz + 8 * r);
-                float zf[8];
-#pragma unroll
-                for (int e = 0; e < 8; e++) zf[e] = dec<DT>((uint16_t)(zr[e >> 1] >> (16 * (e & 1))));
 #pragma unroll
                 for (int s = 0; s < HQ; s++) {
                     float t = 0.0f;
 #pragma unroll
-                    for (int e = 0; e < 8; e++) t = fmaf(qz[s][e], zf[e], t);
-                    bias[s] = row_sum(t);
+                    for (int i = 0; i < 4; i++) t = dot2<DT>(qz[s][i], zr[i], t);
+                    bias[s] = row_sum(t) * qscale;
                 }
             }
             wave_sync();
@@ -757,10 +789,10 @@ __device__ __forceinline__ void split_body(
         u4_t ahi[HQ], alo[HQ];
         {
             const int cg = r & 3;
-            const float4 va = *reinterpret_cast<const float4 *>(st + 128 + 32 * cg + 4 * kb);
-            const float4 vb = *reinterpret_cast<const float4 *>(st + 128 + 32 * cg + 16 + 4 * kb);
-            const float4 za = *reinterpret_cast<const float4 *>(st + 256 + 32 * cg + 4 * kb);
-            const float4 zb = *reinterpret_cast<const float4 *>(st + 256 + 32 * cg + 16 + 4 * kb);
+            const float4 va = *reinterpret_cast<const float4 *>(st + 128 + 36 * cg + 4 * kb);
+            const float4 vb = *reinterpret_cast<const float4 *>(st + 128 + 36 * cg + 16 + 4 * kb);
+            const float4 za = *reinterpret_cast<const float4 *>(st + 272 + 36 * cg + 4 * kb);
+            const float4 zb = *reinterpret_cast<const float4 *>(st + 272 + 36 * cg + 16 + 4 * kb);
             const float v8[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
             const float z8[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
 #pragma unroll
