@@ -283,12 +283,17 @@ constexpr int waves_target(int G, int KH) {
 }
 
 
+// Index swizzle of the lo-plane weight table (16-byte entries): bit 1 is
+// flipped by bits 3 and 4, so the eight lanes an LDS access serves at a time
+// hit eight different bank groups on both the producing and the MFMA side.
+__device__ __forceinline__ int wl_swz(int i) { return i ^ ((((i >> 3) ^ (i >> 4)) & 1) << 1); }
+
 // Bytes of the per-wave LDS region of split_body.
 template <int G, int KH>
 constexpr int split_lds_bytes() {
     constexpr int HQ = (G + 3) / 4, KHE = KH > 0 ? KH : 1, D_ = 128;
     constexpr int page = G * D_ * 2 + HQ * 4 * 32 * 16 + HQ * KHE * 2 * 16 * 16 + 416 * 4 + D_ * 2 +
-                         HQ * 4 * 32 * 4 + (KH > 0 ? G * D_ * 4 : 0);
+                         HQ * 4 * 48 * 4 + (KH > 0 ? G * D_ * 4 : 0);
     constexpr int win = G * D_ * 4 + 32 * G * 4;
     return page > win ? page : win;
 }
@@ -322,8 +327,8 @@ __device__ __forceinline__ void split_body(
     // (rows padded to 36: the PV-side reads of four groups hit four banks)
     constexpr int O_ST = O_WH + HQ * KHE * 2 * 16 * 16;
     constexpr int O_KZ = O_ST + 416 * 4;                  // u16 [D] K zero of the group
-    constexpr int O_PX = O_KZ + D * 2;                    // f32 [HQ][4][32] softmax weights
-    constexpr int O_QF = O_PX + HQ * 4 * 32 * 4;          // f32 [G][D] q' (boosted-channel gathers)
+    constexpr int O_PX = O_KZ + D * 2;                    // f32 [HQ][4][48] softmax weights (rows padded)
+    constexpr int O_QF = O_PX + HQ * 4 * 48 * 4;          // f32 [G][D] q' (boosted-channel gathers)
     constexpr int LDSB = split_lds_bytes<G, KH>();
     static_assert(LDSB >= O_QF + (KH > 0 ? G * D * 4 : 0), "page LDS");
     static_assert(NW == 1 || LDSB >= G * (D + 2) * 4, "merge area of a wave");
@@ -690,9 +695,10 @@ __device__ __forceinline__ void split_body(
 #pragma unroll
                     for (int i = 0; i < 4; i++)
                         split2(qpp[s][2 * i] * s0[i], qpp[s][2 * i + 1] * s1[i], hi[i], lo[i]);
-                    u4_t *wl = reinterpret_cast<u4_t *>(lds + O_WL) + (s * 4 + pm) * 32 + 4 * pR + pkb;
-                    wl[0] = u4_t{hi[0], hi[1], hi[2], hi[3]};
-                    wl[16] = u4_t{lo[0], lo[1], lo[2], lo[3]};
+                    u4_t *wl = reinterpret_cast<u4_t *>(lds + O_WL);
+                    const int wi = (s * 4 + pm) * 32 + 4 * pR + pkb;
+                    wl[wl_swz(wi)] = u4_t{hi[0], hi[1], hi[2], hi[3]};
+                    wl[wl_swz(wi + 16)] = u4_t{lo[0], lo[1], lo[2], lo[3]};
                 }
             }
             // ---- hi-plane weights of this group ----
@@ -729,8 +735,8 @@ __device__ __forceinline__ void split_body(
 #pragma unroll
             for (int qs = 0; qs < NQS; qs++) {
                 const int slot = min(2 * qs + ((r >> 1) & 1), HQ - 1);
-                const u4_t *wl = reinterpret_cast<const u4_t *>(lds + O_WL) + slot * 128 +
-                                 16 * (r & 1) + 4 * (r >> 2) + kb;
+                const u4_t *wl = reinterpret_cast<const u4_t *>(lds + O_WL) +
+                                 wl_swz(slot * 128 + 16 * (r & 1) + 4 * (r >> 2) + kb);
                 f4_t c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0};
 #pragma unroll
                 for (int m = 0; m < 4; m++) {
@@ -778,8 +784,8 @@ __device__ __forceinline__ void split_body(
                     const float p0 = __builtin_amdgcn_exp2f(sc0 - mo);
                     const float p1 = __builtin_amdgcn_exp2f(sc1 - mo);
                     l_part[s] += p0 + p1;
-                    px[(s * 4 + kb) * 32 + r] = p0;
-                    px[(s * 4 + kb) * 32 + 16 + r] = p1;
+                    px[(s * 4 + kb) * 48 + r] = p0;
+                    px[(s * 4 + kb) * 48 + 16 + r] = p1;
                 }
             }
             wave_sync();
@@ -797,9 +803,9 @@ __device__ __forceinline__ void split_body(
             const float z8[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
 #pragma unroll
             for (int s = 0; s < HQ; s++) {
-                const float4 pa = *reinterpret_cast<const float4 *>(px + (s * 4 + (r >> 2)) * 32 + 4 * kb);
+                const float4 pa = *reinterpret_cast<const float4 *>(px + (s * 4 + (r >> 2)) * 48 + 4 * kb);
                 const float4 pb =
-                    *reinterpret_cast<const float4 *>(px + (s * 4 + (r >> 2)) * 32 + 16 + 4 * kb);
+                    *reinterpret_cast<const float4 *>(px + (s * 4 + (r >> 2)) * 48 + 16 + 4 * kb);
                 const float p8[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
                 uint32_t hi[4], lo[4];
 #pragma unroll
