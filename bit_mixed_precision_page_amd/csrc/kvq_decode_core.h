@@ -527,6 +527,47 @@ __device__ __forceinline__ void split_body(
 
     // ---------------------------- page split ----------------------------
     const PageLayout Ly = page_layout(k);
+    // hi-plane producer role: k block hkb, row block hR, operand dword hq
+    const int hkb = lane >> 4, hR = (lane >> 2) & 3, hq = lane & 3;
+    LaneOffs<KHE> O;
+    O.klo = (int)Ly.klo + r * 32 + 8 * kb;
+    O.vc = (int)Ly.vc + 16 * lane;
+    O.meta = lane < 32 ? (int)Ly.ks + 1024 * (lane >> 4) + 16 * (lane & 15)
+                       : (int)Ly.vs + 1024 * ((lane - 32) >> 4) + 256 * ((lane >> 2) & 3) +
+                             16 * (lane & 3);
+    O.mstride = lane < 32 ? 256 : 64;
+    O.khi_tile = 4 * k;
+#pragma unroll
+    for (int ms = 0; ms < KHE; ms++) {
+        const int dw = min(2 * ms + (kb >> 1), max(k / 16 - 1, 0));
+        O.khi[ms] = (int)Ly.khi + r * (k / 4) + 4 * dw;
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const int j = 32 * ms + 16 * (hkb >> 1) + 4 * (hkb & 1) + hq + 8 * t;
+            O.idx[ms][t] = (int)Ly.kidx + min(j, max(k - 1, 0));
+        }
+    }
+    // groups [g0, g1) of this unit (four per page), two register sets in turn
+    const int g0 = (split * NW + wv) * gps;
+    const int g1 = min(4 * n_pages, g0 + gps);
+    const uint8_t *ubase = cache + (size_t)unit * max_pages * page_bytes;
+    auto page_ptr = [&](int p) {
+        if constexpr (POOL)
+            return cache + ((size_t)table[(size_t)b * max_pages + p] * Hkv + h) * page_bytes;
+        else
+            return ubase + (size_t)p * page_bytes;
+    };
+    // The prefetch past the split's last group goes through an empty
+    // descriptor: every offset is out of range, so it reads zeros without
+    // touching memory and the number of loads in flight stays static.
+    auto rs_of = [&](int gi) {
+        return page_rsrc(page_ptr(min(gi, g1 - 1) >> 2), gi < g1 ? page_bytes : 0u);
+    };
+    // The first group's loads go out before the query is staged, so their
+    // latency overlaps the set-up below.
+    GroupRegs<KHE> ga;
+    if (g0 < g1) load_group<KH>(ga, rs_of(g0), O, g0 & 3);
+
     uint16_t *qr = reinterpret_cast<uint16_t *>(lds + O_Q);
     float *st = reinterpret_cast<float *>(lds + O_ST);
     uint16_t *kz = reinterpret_cast<uint16_t *>(lds + O_KZ);
@@ -579,10 +620,9 @@ __device__ __forceinline__ void split_body(
         for (int i = 0; i < 4; i++) qz[s][i] = v[i];
     }
 
-    // Hi-plane producer role: k block hkb, row block hR, operand dword hq; its
-    // boosted slots are j0 = 32 ms + 16 (hkb / 2) + 4 (hkb % 2) + hq and j0 + 8,
-    // at mantissa bits 2 sig_hi with sig_hi = 2 + (hq & 1).
-    const int hkb = lane >> 4, hR = (lane >> 2) & 3, hq = lane & 3;
+    // Hi-plane producer role (hkb, hR, hq, defined above): its boosted slots
+    // are j0 = 32 ms + 16 (hkb / 2) + 4 (hkb % 2) + hq and j0 + 8, at mantissa
+    // bits 2 sig_hi with sig_hi = 2 + (hq & 1).
     const float fh = (hq & 1) ? 4.0f / 64.0f : 4.0f / 16.0f;
     // ... times 0 for slots past the k listed channels (their index bytes are 0)
     float fhs[KHE][2];
@@ -592,24 +632,6 @@ __device__ __forceinline__ void split_body(
         for (int t = 0; t < 2; t++)
             fhs[ms][t] = 32 * ms + 16 * (hkb >> 1) + 4 * (hkb & 1) + hq + 8 * t < k ? fh : 0.0f;
 
-    LaneOffs<KHE> O;
-    O.klo = (int)Ly.klo + r * 32 + 8 * kb;
-    O.vc = (int)Ly.vc + 16 * lane;
-    O.meta = lane < 32 ? (int)Ly.ks + 1024 * (lane >> 4) + 16 * (lane & 15)
-                       : (int)Ly.vs + 1024 * ((lane - 32) >> 4) + 256 * ((lane >> 2) & 3) +
-                             16 * (lane & 3);
-    O.mstride = lane < 32 ? 256 : 64;
-    O.khi_tile = 4 * k;
-#pragma unroll
-    for (int ms = 0; ms < KHE; ms++) {
-        const int dw = min(2 * ms + (kb >> 1), max(k / 16 - 1, 0));
-        O.khi[ms] = (int)Ly.khi + r * (k / 4) + 4 * dw;
-#pragma unroll
-        for (int t = 0; t < 2; t++) {
-            const int j = 32 * ms + 16 * (hkb >> 1) + 4 * (hkb & 1) + hq + 8 * t;
-            O.idx[ms][t] = (int)Ly.kidx + min(j, max(k - 1, 0));
-        }
-    }
     // staging destinations of this lane's metadata chunk
     const int st_o = lane < 16 ? 8 * lane
                                : 128 + 144 * ((lane - 32) >> 4) + 36 * ((lane >> 2) & 3) + 8 * (lane & 3);
@@ -830,27 +852,10 @@ __device__ __forceinline__ void split_body(
         }
     };
 
-    // groups [g0, g1) of this unit (four per page), two register sets in turn
-    const int g0 = (split * NW + wv) * gps;
-    const int g1 = min(4 * n_pages, g0 + gps);
-    const uint8_t *ubase = cache + (size_t)unit * max_pages * page_bytes;
-    auto page_ptr = [&](int p) {
-        if constexpr (POOL)
-            return cache + ((size_t)table[(size_t)b * max_pages + p] * Hkv + h) * page_bytes;
-        else
-            return ubase + (size_t)p * page_bytes;
-    };
-    // The prefetch past the split's last group goes through an empty
-    // descriptor: every offset is out of range, so it reads zeros without
-    // touching memory and the number of loads in flight stays static.
-    auto rs_of = [&](int gi) {
-        return page_rsrc(page_ptr(min(gi, g1 - 1) >> 2), gi < g1 ? page_bytes : 0u);
-    };
     // (an empty range only occurs in a graph-replayed step: the split then
     // writes an empty partial, m = -inf and l = 0)
     if (g0 < g1) {
-        GroupRegs<KHE> ga, gb;
-        load_group<KH>(ga, rs_of(g0), O, g0 & 3);
+        GroupRegs<KHE> gb;
         for (int gi = g0;;) {
             load_group<KH>(gb, rs_of(gi + 1), O, (gi + 1) & 3);
             process(ga);
