@@ -279,7 +279,7 @@ __device__ __forceinline__ void load_group(GroupRegs<KHE> &Gr, __amdgpu_buffer_r
 // Waves per SIMD the register allocation aims at (more registers per wave
 // beyond that would spill).
 constexpr int waves_target(int G, int KH) {
-    return G <= 4 ? (KH == 0 || (KH == 1 && G > 1) ? 4 : KH <= 3 ? 3 : 2) : G == 8 ? (KH <= 3 ? 2 : 1) : 1;
+    return G <= 4 ? (KH == 0 || (KH == 1 && G > 1) ? 4 : KH <= 3 ? 3 : 2) : G == 8 ? (KH <= 1 ? 3 : KH <= 3 ? 2 : 1) : 1;
 }
 
 
@@ -293,7 +293,7 @@ template <int G, int KH>
 constexpr int split_lds_bytes() {
     constexpr int HQ = (G + 3) / 4, KHE = KH > 0 ? KH : 1, D_ = 128;
     constexpr int page = G * D_ * 2 + HQ * 4 * 32 * 16 + HQ * KHE * 2 * 16 * 16 + 416 * 4 + D_ * 2 +
-                         HQ * 4 * 48 * 4 + (KH > 0 ? G * D_ * 4 : 0);
+                         HQ * 4 * 48 * 4 + (KH > 0 && G <= 4 ? G * D_ * 4 : 0);
     constexpr int win = G * D_ * 4 + 32 * G * 4;
     return page > win ? page : win;
 }
@@ -330,7 +330,10 @@ __device__ __forceinline__ void split_body(
     constexpr int O_PX = O_KZ + D * 2;                    // f32 [HQ][4][48] softmax weights (rows padded)
     constexpr int O_QF = O_PX + HQ * 4 * 48 * 4;          // f32 [G][D] q' (boosted-channel gathers)
     constexpr int LDSB = split_lds_bytes<G, KH>();
-    static_assert(LDSB >= O_QF + (KH > 0 ? G * D * 4 : 0), "page LDS");
+    // fp32 q' table for the boosted-channel gathers: only where the LDS it
+    // takes does not cost occupancy (G <= 4); larger groups decode raw q
+    constexpr bool QF = KH > 0 && G <= 4;
+    static_assert(LDSB >= O_QF + (QF ? G * D * 4 : 0), "page LDS");
     static_assert(NW == 1 || LDSB >= G * (D + 2) * 4, "merge area of a wave");
     __shared__ __align__(16) uint8_t lds_all[NW][LDSB];
     // wave index, wave-uniform (page descriptors derived from it stay scalar)
@@ -577,7 +580,7 @@ __device__ __forceinline__ void split_body(
     for (int ch = lane; ch < G * (D / 8); ch += 64) {
         const uint4 v = *reinterpret_cast<const uint4 *>(qg + 8 * ch);
         *reinterpret_cast<uint4 *>(qr + 8 * ch) = v;
-        if constexpr (KH > 0) {
+        if constexpr (QF) {
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 8; e++)
@@ -660,7 +663,9 @@ __device__ __forceinline__ void split_body(
                 const int c = (int)(Gr.ib[ms][t] & 127u);
                 hc[ms][t] = c;
 #pragma unroll
-                for (int s = 0; s < HQ; s++) qh[s][ms][t] = qf[head_of<G>(hR, s) * D + c] * fhs[ms][t];
+                for (int s = 0; s < HQ; s++)
+                    qh[s][ms][t] = (QF ? qf[head_of<G>(hR, s) * D + c] : qv(head_of<G>(hR, s), c)) *
+                                   fhs[ms][t];
             }
         // ---- metadata: exponents from the largest scales (integer max of the
         // bits: scales are never negative), then fp32 copies into LDS ----
