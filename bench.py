@@ -331,6 +331,9 @@ def stream_main(a, w, torch, gen, kvq):
         if rel is not None:
             c.set_relevance(rel)
         caches.append(c)
+    if a.splits:
+        for c in caches:
+            kvq.kvq_set_decode_splits(c.handle, a.splits)
     qs, kts, vts = [], [], []
     for s in range(1, w.decode_steps + 1):
         qs.append(to_dev(gen.query(w, step=s)))
