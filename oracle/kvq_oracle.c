@@ -60,6 +60,19 @@
  *      head); score = |fp32(difficulty * rel)|; ties go to the lower channel.
  *      The relevance of a query is the sum over the query heads that share
  *      the KV head of |q_c|, in fp32, heads in ascending order.
+ *  R20 prefill attention (MiniKV summary, "proposed method": the prefill
+ *      processes the whole input; a two-stage selective flash-attention
+ *      yields the attention output and the cumulative attention scores in
+ *      linear memory) is causal: query position i attends to key positions
+ *      j <= i; query head hq reads KV head hq / (Hq / Hkv); scale as R8.
+ *  R21 cumulative score of key position j for KV head h: the sum, over the
+ *      query heads of h and over the query positions i >= j, of the softmax
+ *      probability P[i][j] (the accumulated attention the heavy-hitter
+ *      selection ranks by).
+ *  R22 token selection (same section: heavy hitters and a recent window are
+ *      kept, 25 % of the budget each by default): the last `recent`
+ *      positions are kept; of the others, the `heavy` positions of largest
+ *      score, ties to the lower position; the kept list is ascending.
  */
 #include <math.h>
 #include <stdint.h>
@@ -543,4 +556,100 @@ int ora_num_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/* ------------------------------------------------------------------------
+ * R20, R21: causal prefill attention of one sequence, in double precision.
+ * q: [Hq][T][D], k, v: [Hkv][T][D] stored values; out: [Hq][T][D] doubles;
+ * score: [Hkv][T] doubles (cumulative attention per key position).
+ * ---------------------------------------------------------------------- */
+int ora_prefill_attention(int dt, int T, int Hq, int Hkv, const uint16_t *q,
+                          const uint16_t *k, const uint16_t *v, double scale,
+                          double *out, double *score) {
+    if (T <= 0 || Hkv <= 0 || Hq % Hkv) return -1;
+    int g = Hq / Hkv;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < Hkv; h++) {
+        double *Kh = (double *)malloc(sizeof(double) * (size_t)T * D);
+        double *Vh = (double *)malloc(sizeof(double) * (size_t)T * D);
+        double *w = (double *)malloc(sizeof(double) * (size_t)T);
+        if (!Kh || !Vh || !w) {
+            err = -2;
+            free(Kh); free(Vh); free(w);
+            continue;
+        }
+        for (size_t x = 0; x < (size_t)T * D; x++) {
+            Kh[x] = ora_decode(dt, k[(size_t)h * T * D + x]);
+            Vh[x] = ora_decode(dt, v[(size_t)h * T * D + x]);
+        }
+        for (int j = 0; j < T; j++) score[(size_t)h * T + j] = 0.0;
+        for (int a = 0; a < g; a++) {
+            int hq = h * g + a;
+            for (int i = 0; i < T; i++) {
+                const uint16_t *qi = q + ((size_t)hq * T + i) * D;
+                double qd[D];
+                for (int c = 0; c < D; c++) qd[c] = ora_decode(dt, qi[c]);
+                int last = ORA_PLANT == 17 ? T - 1 : i; /* causal mask dropped */
+                double m = -INFINITY;
+                for (int j = 0; j <= last; j++) {
+                    double d = 0.0;
+                    for (int c = 0; c < D; c++) d += qd[c] * Kh[(size_t)j * D + c];
+                    w[j] = scale * d;
+                    if (w[j] > m) m = w[j];
+                }
+                double l = 0.0;
+                for (int j = 0; j <= last; j++) {
+                    w[j] = exp(w[j] - m);
+                    l += w[j];
+                }
+                double o[D];
+                for (int c = 0; c < D; c++) o[c] = 0.0;
+                for (int j = 0; j <= last; j++) {
+                    double pr = w[j] / l;
+                    score[(size_t)h * T + j] += ORA_PLANT == 18 ? w[j] : pr; /* unnormalized */
+                    for (int c = 0; c < D; c++) o[c] += pr * Vh[(size_t)j * D + c];
+                }
+                for (int c = 0; c < D; c++) out[((size_t)hq * T + i) * D + c] = o[c];
+            }
+        }
+        free(Kh);
+        free(Vh);
+        free(w);
+    }
+    return err;
+}
+
+/* R22: heavy hitters + recent window.  Sorting (a library step) orders the
+   candidate positions by score, higher first, the lower position first among
+   equal scores. */
+static const double *sel_score;
+static int sel_cmp(const void *a, const void *b) {
+    int i = *(const int *)a, j = *(const int *)b;
+    if (sel_score[i] != sel_score[j]) return sel_score[i] > sel_score[j] ? -1 : 1;
+    return ORA_PLANT == 19 ? (i < j ? 1 : -1) : (i < j ? -1 : 1); /* ties to the lower */
+}
+
+int ora_select_tokens(int T, const double *score, int heavy, int recent, int32_t *keep) {
+    if (T < 0 || heavy < 0 || recent < 0) return -1;
+    if (recent > T) recent = T;
+    int n_old = T - recent;
+    if (heavy > n_old) heavy = n_old;
+    int *idx = (int *)malloc(sizeof(int) * (size_t)(n_old > 0 ? n_old : 1));
+    char *kept = (char *)calloc((size_t)(T > 0 ? T : 1), 1);
+    if (!idx || !kept) {
+        free(idx); free(kept);
+        return -2;
+    }
+    for (int j = 0; j < n_old; j++) idx[j] = j;
+    sel_score = score;
+    qsort(idx, (size_t)n_old, sizeof(int), sel_cmp);
+    for (int r = 0; r < heavy; r++) kept[idx[r]] = 1;
+    for (int j = n_old + (ORA_PLANT == 20 ? 1 : 0); j < T; j++) kept[j] = 1; /* recent window */
+    int n = 0;
+    for (int j = 0; j < T; j++)
+        if (kept[j]) keep[n++] = j;
+    free(idx);
+    free(kept);
+    return n;
 }

@@ -27,6 +27,7 @@ _u16p = ctypes.POINTER(ctypes.c_uint16)
 _f64p = ctypes.POINTER(ctypes.c_double)
 _f32p = ctypes.POINTER(ctypes.c_float)
 _i64p = ctypes.POINTER(ctypes.c_int64)
+_i32p = ctypes.POINTER(ctypes.c_int32)
 
 
 def _ptr(a, t):
@@ -81,6 +82,9 @@ class OracleLib:
                                             _u8p, _u8p, _u8p]
         L.ora_num_threads.restype = ctypes.c_int
         L.ora_num_threads.argtypes = []
+        L.ora_prefill_attention.argtypes = [ctypes.c_int] * 4 + [_u16p, _u16p, _u16p,
+                                                                 ctypes.c_double, _f64p, _f64p]
+        L.ora_select_tokens.argtypes = [ctypes.c_int, _f64p, ctypes.c_int, ctypes.c_int, _i32p]
         self.L = L
 
     # -- stored dtypes -----------------------------------------------------
@@ -225,6 +229,34 @@ class OracleLib:
 
     def num_threads(self):
         return int(self.L.ora_num_threads())
+
+    def prefill_attention(self, dt, q, k, v, scale):
+        """Causal prefill attention of one sequence (R20, R21): q [Hq][T][D],
+        k, v [Hkv][T][D] u16 -> (out [Hq][T][D] float64, score [Hkv][T] float64)."""
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        k = np.ascontiguousarray(k, dtype=np.uint16)
+        v = np.ascontiguousarray(v, dtype=np.uint16)
+        Hq, T, d = q.shape
+        Hkv = k.shape[0]
+        assert d == D and k.shape == (Hkv, T, D) and v.shape == k.shape
+        out = np.empty((Hq, T, D), np.float64)
+        score = np.empty((Hkv, T), np.float64)
+        rc = self.L.ora_prefill_attention(dt, T, Hq, Hkv, _ptr(q, _u16p), _ptr(k, _u16p),
+                                          _ptr(v, _u16p), float(scale), _ptr(out, _f64p),
+                                          _ptr(score, _f64p))
+        if rc:
+            raise ValueError(f"ora_prefill_attention failed ({rc})")
+        return out, score
+
+    def select_tokens(self, score, heavy, recent):
+        """R22: kept positions (ascending) of one KV head's scores [T]."""
+        score = np.ascontiguousarray(score, dtype=np.float64)
+        T = score.shape[0]
+        keep = np.empty(max(T, 1), np.int32)
+        n = self.L.ora_select_tokens(T, _ptr(score, _f64p), heavy, recent, _ptr(keep, _i32p))
+        if n < 0:
+            raise ValueError(f"ora_select_tokens failed ({n})")
+        return keep[:n].copy()
 
 
 _default = None

@@ -521,4 +521,120 @@ def pin_append_equals_bulk(ora):
     assert (stream.vres[:, :, :5] == V[:, :, 3 * P:]).all()
 
 
+# ---------------------------------------------------------------------------
+# Prefill attention with cumulative scores and token selection (MiniKV
+# summary, "proposed method": heavy hitters by cumulative attention plus a
+# recent window, both chosen at the prefill).
+
+def _prefill_inputs(r, dt, Hq, Hkv, T, kscale=1.0):
+    q = _bits(dt, r.standard_normal((Hq, T, D), dtype=np.float32))
+    k = _bits(dt, kscale * r.standard_normal((Hkv, T, D), dtype=np.float32))
+    v = _bits(dt, r.standard_normal((Hkv, T, D), dtype=np.float32))
+    return q, k, v
+
+
+def _causal_sdpa(q, k, v, g, scale):
+    """torch fp64 causal SDPA, KV heads repeated for their query heads."""
+    Q = torch.from_numpy(q)[None]
+    K = torch.from_numpy(k).repeat_interleave(g, dim=0)[None]
+    V = torch.from_numpy(v).repeat_interleave(g, dim=0)[None]
+    return torch.nn.functional.scaled_dot_product_attention(
+        Q, K, V, is_causal=True, scale=scale)[0].numpy()
+
+
+def pin_prefill_attention_sdpa(ora):
+    """Library routine: outputs = torch fp64 causal SDPA over the stored values."""
+    r = np.random.default_rng(71)
+    for dt, Hq, Hkv, T in [(BF16, 4, 2, 37), (F16, 2, 1, 5), (BF16, 8, 2, 1)]:
+        q, k, v = _prefill_inputs(r, dt, Hq, Hkv, T)
+        scale = 1.0 / np.sqrt(D)
+        out, _ = ora.prefill_attention(dt, q, k, v, scale)
+        ref = _causal_sdpa(_val(dt, q), _val(dt, k), _val(dt, v), Hq // Hkv, scale)
+        assert np.abs(out - ref).max() < 1e-12, (dt, Hq, Hkv, T)
+
+
+def pin_prefill_score_total(ora):
+    """Invariant: each query row's probabilities sum to 1, so a KV head's
+    cumulative scores sum to (query heads per KV head) x T; and scores are
+    positive."""
+    r = np.random.default_rng(72)
+    for dt, Hq, Hkv, T in [(BF16, 4, 2, 45), (F16, 3, 1, 17)]:
+        q, k, v = _prefill_inputs(r, dt, Hq, Hkv, T, kscale=2.0)
+        _, score = ora.prefill_attention(dt, q, k, v, 1.0 / np.sqrt(D))
+        g = Hq // Hkv
+        assert np.allclose(score.sum(axis=1), g * T, rtol=0, atol=1e-9), score.sum(axis=1)
+        assert (score > 0).all()
+
+
+def pin_prefill_score_uniform(ora):
+    """Closed form: with all Keys zero every causal row is uniform,
+    P[i][j] = 1/(i+1), so score[j] = g (H_T - H_j), H_n the n-th harmonic
+    number; and the output row i is the mean of the first i+1 Values."""
+    r = np.random.default_rng(73)
+    T, Hq, Hkv = 29, 4, 1
+    q, _, v = _prefill_inputs(r, BF16, Hq, Hkv, T)
+    k = np.zeros((Hkv, T, D), np.uint16)
+    out, score = ora.prefill_attention(BF16, q, k, v, 1.0 / np.sqrt(D))
+    H = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, T + 1))])
+    want = Hq * (H[T] - H[np.arange(T)])
+    assert np.abs(score[0] - want).max() < 1e-12
+    vv = _val(BF16, v)[0]
+    means = np.cumsum(vv, axis=0) / np.arange(1, T + 1)[:, None]
+    assert np.abs(out - means[None]).max() < 1e-12
+
+
+def pin_prefill_score_last_and_first(ora):
+    """Library routine: the last key is seen only by the last query row, so
+    its score is the sum over heads of that row's last softmax probability;
+    the first key's score is the sum over all rows of their first probability
+    (torch fp64 softmax of the explicit causal score rows)."""
+    r = np.random.default_rng(74)
+    T, Hq, Hkv = 23, 4, 2
+    q, k, v = _prefill_inputs(r, BF16, Hq, Hkv, T, kscale=3.0)
+    scale = 1.0 / np.sqrt(D)
+    _, score = ora.prefill_attention(BF16, q, k, v, scale)
+    Q = torch.from_numpy(_val(BF16, q))
+    K = torch.from_numpy(_val(BF16, k)).repeat_interleave(Hq // Hkv, dim=0)
+    s = scale * Q @ K.transpose(1, 2)
+    mask = torch.ones(T, T, dtype=torch.bool).tril()
+    p = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=-1).numpy()  # [Hq][T][T]
+    g = Hq // Hkv
+    for h in range(Hkv):
+        ph = p[h * g:(h + 1) * g]
+        assert abs(score[h, T - 1] - ph[:, T - 1, T - 1].sum()) < 1e-12
+        assert abs(score[h, 0] - ph[:, :, 0].sum()) < 1e-12
+
+
+def pin_select_tokens_golden(ora):
+    """Hand-worked values (tests/golden/token_selection.json)."""
+    cases = json.load(open(os.path.join(GOLDEN, "token_selection.json")))["cases"]
+    for c in cases:
+        got = ora.select_tokens(np.array(c["score"], np.float64), c["heavy"], c["recent"])
+        assert got.tolist() == c["keep"], (c, got.tolist())
+
+
+def pin_select_tokens_bruteforce(ora):
+    """Brute force over every heavy subset on small inputs with forced ties:
+    the kept heavy set maximizes the score sum, and among the sets with that
+    sum it is the one whose sorted positions come first; the recent window is
+    always kept; the list is ascending."""
+    r = np.random.default_rng(75)
+    for trial in range(60):
+        T = int(r.integers(1, 10))
+        recent = int(r.integers(0, 4))
+        heavy = int(r.integers(0, 5))
+        score = r.integers(0, 4, T).astype(np.float64) / 4.0  # many ties
+        got = ora.select_tokens(score, heavy, recent).tolist()
+        rec = min(recent, T)
+        old = T - rec
+        h = min(heavy, old)
+        best = None
+        for sub in itertools.combinations(range(old), h):
+            key = (-sum(score[list(sub)]), sub)
+            if best is None or key < best:
+                best = key
+        want = sorted(list(best[1]) + list(range(old, T)))
+        assert got == want, (score.tolist(), heavy, recent, got, want)
+
+
 PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

@@ -26,6 +26,10 @@ PLANTS = {
     14: "query-aware score ignores the relevance",
     15: "query-aware difficulty = largest group range instead of their sum",
     16: "relevance = largest |q| of the group's heads instead of the sum",
+    17: "prefill attention without the causal mask",
+    18: "cumulative scores summed before the softmax normalization",
+    19: "token selection ties to the higher position",
+    20: "recent window one position short",
 }
 
 
