@@ -15,10 +15,12 @@ OUT = os.path.join(HERE, "libkvq.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kvq_host.cpp", "kvq_quantize.hip", "kvq_decode.hip", "kvq_pool.hip"]
+SOURCES = ["kvq_host.cpp", "kvq_quantize.hip", "kvq_decode.hip", "kvq_pool.hip",
+           "kvq_prefill.hip"]
 # The decode kernels never produce or test NaNs; without NaN semantics
 # fmaxf needs no quieting of its operands and fuses with cross-lane DPP moves.
-PER_FILE = {"kvq_decode.hip": ["-fno-honor-nans"], "kvq_pool.hip": ["-fno-honor-nans"]}
+PER_FILE = {"kvq_decode.hip": ["-fno-honor-nans"], "kvq_pool.hip": ["-fno-honor-nans"],
+            "kvq_prefill.hip": ["-fno-honor-nans"]}
 FLAGS = [
     "-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math", "-ffp-contract=fast",

@@ -242,6 +242,21 @@ int pool_flush_full(kvq_pool *p, hipStream_t st, int32_t *n) {
 
 }  // namespace
 
+// ------------------------------------------------------------- prefill ----
+namespace {
+constexpr int64_t kPrefillMaxT = 1 << 20;  // positions of one prefill
+
+size_t prefill_stats_bytes(int32_t T, int32_t Hq) { return align256((size_t)Hq * T * 8); }
+size_t prefill_ws_bytes(int32_t T, int32_t Hq, int32_t Hkv) {
+    const size_t T32 = ((size_t)T + 31) / 32 * 32;
+    return prefill_stats_bytes(T, Hq) + (size_t)Hkv * kvq::D * T32 * 2;
+}
+int prefill_shape_ok(int32_t T, int32_t Hq, int32_t Hkv) {
+    return T >= 1 && T <= kPrefillMaxT && Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 &&
+           Hq / Hkv <= 16 && (int64_t)Hq * T * kvq::D <= (int64_t)1 << 31;
+}
+}  // namespace
+
 extern "C" {
 
 int kvq_cache_bytes(const kvq_config *cfg, size_t *bytes) {
@@ -482,6 +497,57 @@ int kvq_set_channel_relevance(kvq_cache *c, const float *rel) {
     if (rel && !aligned16(rel)) return KVQ_EALIGN;
     c->rel = rel;
     return KVQ_OK;
+}
+
+
+int kvq_prefill_workspace_bytes(int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                                size_t *bytes) {
+    if (!bytes || !prefill_shape_ok(T, num_q_heads, num_kv_heads)) return KVQ_EINVAL;
+    *bytes = prefill_ws_bytes(T, num_q_heads, num_kv_heads);
+    return KVQ_OK;
+}
+
+int kvq_prefill_select(int32_t dtype, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                       float softmax_scale, const void *q, const void *k, const void *v,
+                       int32_t heavy, int32_t recent, float *out, float *score, int32_t *keep,
+                       void *k_sel, void *v_sel, void *workspace, size_t ws_bytes, void *stream,
+                       int32_t *n_keep) {
+    if (dtype != KVQ_F16 && dtype != KVQ_BF16) return KVQ_EINVAL;
+    if (!prefill_shape_ok(T, num_q_heads, num_kv_heads) || heavy < 0 || recent < 0)
+        return KVQ_EINVAL;
+    if (!q || !k || !v || !out || !score || !workspace || !n_keep) return KVQ_EINVAL;
+    if (!k_sel != !v_sel) return KVQ_EINVAL;
+    const int32_t rec = std::min(recent, T);
+    const int32_t hv = std::min(heavy, T - rec);
+    const int32_t nk = hv + rec;
+    if (nk > 0 && !keep) return KVQ_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(score) ||
+        !aligned16(workspace) || (keep && !aligned16(keep)) || (k_sel && !aligned16(k_sel)) ||
+        (v_sel && !aligned16(v_sel)))
+        return KVQ_EALIGN;
+    if (ws_bytes < prefill_ws_bytes(T, num_q_heads, num_kv_heads)) return KVQ_EWORKSPACE;
+    kvq::PrefillArgs a{};
+    a.T = T;
+    a.T32 = (T + 31) / 32 * 32;
+    a.Hq = num_q_heads;
+    a.Hkv = num_kv_heads;
+    a.heavy = heavy;
+    a.recent = recent;
+    a.n_keep = nk;
+    a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)kvq::D);
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    a.stats = reinterpret_cast<float2 *>(ws);
+    a.vt = reinterpret_cast<uint16_t *>(ws + prefill_stats_bytes(T, num_q_heads));
+    a.out = out;
+    a.score = score;
+    a.keep = keep;
+    a.k_sel = static_cast<uint16_t *>(k_sel);
+    a.v_sel = static_cast<uint16_t *>(v_sel);
+    *n_keep = nk;
+    return hip_status(kvq::launch_prefill(dtype, a, static_cast<hipStream_t>(stream)));
 }
 
 int kvq_query_relevance(int32_t dtype, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

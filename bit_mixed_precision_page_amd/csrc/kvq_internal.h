@@ -95,6 +95,20 @@ struct DecodePlan {
                           // then total_splits = page_splits + R / 32
 };
 size_t decode_workspace_bytes(const Geometry &G, int max_splits);
+
+// Prefill of one sequence: causal attention with cumulative attention scores,
+// heavy-hitter + recent token selection and the gather of the kept rows.
+struct PrefillArgs {
+    int T, T32, Hq, Hkv, heavy, recent, n_keep;
+    float scale;
+    const uint16_t *q, *k, *v;  // [Hq][T][D], [Hkv][T][D], [Hkv][T][D]
+    uint16_t *vt;               // workspace: [Hkv][D][T32] transposed Values
+    float2 *stats;              // workspace: [Hq][T] (row max in log2 units, 1 / row sum)
+    float *out, *score;         // [Hq][T][D], [Hkv][T]
+    int32_t *keep;              // [Hkv][n_keep]
+    uint16_t *k_sel, *v_sel;    // [Hkv][n_keep][D], or null
+};
+hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream);
 // Waves per workgroup of the dense decode kernel: each wave streams its own
 // run of groups (or 32 window tokens) and the workgroup merges the waves'
 // partials in LDS, so one split = kDecodeWaves runs.

@@ -1,0 +1,353 @@
+// kvq_prefill.hip -- prefill attention of one sequence with cumulative
+// attention scores, and heavy-hitter + recent token selection (gfx950).
+//
+// MiniKV summary (f-binder), "proposed method": the prefill processes the
+// whole input and chooses the KV states to keep from cumulative attention
+// scores -- the heavy hitters plus a recent window, 25 % of the budget each by
+// default -- and a two-stage selective flash-attention yields the attention
+// output and the cumulative scores in linear memory.  Readings: the attention
+// is causal; the score of key position j is the sum, over the query heads of
+// its KV head and the query rows i >= j, of the softmax probability P[i][j];
+// the last `recent` positions are kept, plus the `heavy` positions of largest
+// score among the others (ties to the lower position), listed ascending.
+//
+// Stage 0  Values transposed to [Hkv][D][T32] (T32 = T rounded up to 32, zero
+//          tail), so a lane's P.V operand is 16 contiguous bytes.
+// Stage 1  flash attention: one wave per 16 query rows of one query head, 32
+//          keys per step.  S = Q K^T on the matrix cores (the dtype inputs are
+//          exact, fp32 accumulation); online softmax in the log2 domain; P
+//          through a 2 KB LDS transpose into the operand layout, split into a
+//          dtype hi and lo part (~16 bits for bf16, ~22 for fp16); P V with 2
+//          MFMAs per 16-channel tile, accumulated in the MFMA results.
+//          Writes out (fp32) and per row (max, 1 / sum).
+// Stage 2  cumulative scores: one wave per 16 keys of one KV head runs over
+//          every query head of the group and every 16-row query block at or
+//          after its keys: S again, P = 2^(s - m_i) / l_i from the stage-1
+//          row statistics, column sums in registers.  A wave owns its keys,
+//          so the sums are deterministic.
+// Stage 3  selection, one workgroup per KV head: the heavy-th largest score
+//          by a bitwise search over the score bits (scores are >= 0, so the
+//          bits order like the values), ties at that score resolved to the
+//          lower positions by a prefix count, then an ascending compaction.
+// Stage 4  gather of the kept K and V rows.
+#include "kvq_decode_core.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kSelThreads = 256;
+
+// fp32 pair -> dtype pair, round to nearest even
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    if constexpr (DT == F16) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2_t));
+    } else {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, bf2_t));
+    }
+}
+template <int DT>
+__device__ __forceinline__ float lo16(uint32_t w) {
+    return dec<DT>((uint16_t)(w & 0xffffu));
+}
+template <int DT>
+__device__ __forceinline__ float hi16(uint32_t w) {
+    return dec<DT>((uint16_t)(w >> 16));
+}
+
+// ---------------------------------------------------------------- stage 0
+__global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t *__restrict__ v,
+                                                          uint16_t *__restrict__ vt, int T,
+                                                          int T32) {
+    __shared__ uint16_t tile[32][D + 8];
+    const int h = blockIdx.y, t0 = blockIdx.x * 32, tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {  // 32 tokens x 16 chunks of 8 channels
+        const int x = tid + 256 * i, tok = x >> 4, c8 = x & 15;
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (t0 + tok < T) w = *reinterpret_cast<const uint4 *>(v + ((size_t)h * T + t0 + tok) * D + 8 * c8);
+        *reinterpret_cast<uint4 *>(&tile[tok][8 * c8]) = w;
+    }
+    __syncthreads();
+    const int c = tid >> 1, half = tid & 1;  // channel c, tokens 16 half + [0, 16)
+    uint32_t o[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        o[e] = (uint32_t)tile[16 * half + 2 * e][c] | ((uint32_t)tile[16 * half + 2 * e + 1][c] << 16);
+    uint4 *dst = reinterpret_cast<uint4 *>(vt + ((size_t)h * D + c) * T32 + t0 + 16 * half);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// ---------------------------------------------------------------- stage 1
+template <int DT>
+__global__ __launch_bounds__(64) void prefill_fwd_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ vt, float *__restrict__ out, float2 *__restrict__ stats, int T,
+    int T32, int g, float qscale) {
+    __shared__ __align__(16) float px[16][36];  // P [query row][key], rows padded
+    const int hq = blockIdx.y, h = hq / g;
+    const int i0 = blockIdx.x * 16;
+    const int lane = threadIdx.x, r = lane & 15, kb = lane >> 4;
+    // A operand: query row i0 + r, channels 32 m + 8 kb + [0, 8)
+    u4_t aq[4];
+    {
+        const uint16_t *qrow = q + ((size_t)hq * T + min(i0 + r, T - 1)) * D;
+#pragma unroll
+        for (int m = 0; m < 4; m++) aq[m] = *reinterpret_cast<const u4_t *>(qrow + 32 * m + 8 * kb);
+    }
+    // this lane's result rows: i0 + 4 kb + e
+    float m_run[4], l_run[4];
+    f4_t acc[8];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        m_run[e] = -INFINITY;
+        l_run[e] = 0.0f;
+    }
+#pragma unroll
+    for (int n = 0; n < 8; n++) acc[n] = f4_t{0, 0, 0, 0};
+    const int nblk = min(T - 1, i0 + 15) / 32 + 1;
+    const uint16_t *kh = k + (size_t)h * T * D;
+    const uint16_t *vth = vt + (size_t)h * D * T32;
+    for (int jb = 0; jb < nblk; jb++) {
+        const int j0 = 32 * jb;
+        f4_t s[2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const uint16_t *krow = kh + (size_t)min(j0 + 16 * t + r, T - 1) * D;
+            u4_t bk[4];
+#pragma unroll
+            for (int m = 0; m < 4; m++) bk[m] = *reinterpret_cast<const u4_t *>(krow + 32 * m + 8 * kb);
+            f4_t c = {0, 0, 0, 0};
+#pragma unroll
+            for (int m = 0; m < 4; m++) c = mfma_dt<DT>(aq[m], bk[m], c);
+            s[t] = c;
+        }
+        // V operands of this block (issued before the softmax)
+        u4_t bv[8];
+#pragma unroll
+        for (int n = 0; n < 8; n++)
+            bv[n] = *reinterpret_cast<const u4_t *>(vth + (size_t)(16 * n + r) * T32 + j0 + 8 * kb);
+        float p[2][4], alpha[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int i = min(i0 + 4 * kb + e, T - 1);
+            float bm = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const int j = j0 + 16 * t + r;
+                p[t][e] = j <= i ? s[t][e] * qscale : -INFINITY;
+                bm = fmaxf(bm, p[t][e]);
+            }
+            // every row has a key <= i in every block it visits, so bm is finite
+            const float mn = fmaxf(m_run[e], row_max(bm));
+            alpha[e] = __builtin_amdgcn_exp2f(m_run[e] - mn);
+            m_run[e] = mn;
+            float ps = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                p[t][e] = __builtin_amdgcn_exp2f(p[t][e] - mn);
+                ps += p[t][e];
+            }
+            l_run[e] = fmaf(l_run[e], alpha[e], row_sum(ps));
+        }
+#pragma unroll
+        for (int n = 0; n < 8; n++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[n][e] *= alpha[e];
+        wave_sync();  // the previous block's reads of px are done
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) px[4 * kb + e][16 * t + r] = p[t][e];
+        wave_sync();
+        const float4 pa = *reinterpret_cast<const float4 *>(&px[r][8 * kb]);
+        const float4 pb = *reinterpret_cast<const float4 *>(&px[r][8 * kb + 4]);
+        const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+        u4_t ahi, alo;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; e2++) {
+            const uint32_t hw = pack2<DT>(pv[2 * e2], pv[2 * e2 + 1]);
+            ahi[e2] = hw;
+            alo[e2] = pack2<DT>(pv[2 * e2] - lo16<DT>(hw), pv[2 * e2 + 1] - hi16<DT>(hw));
+        }
+#pragma unroll
+        for (int n = 0; n < 8; n++) {
+            acc[n] = mfma_dt<DT>(ahi, bv[n], acc[n]);
+            acc[n] = mfma_dt<DT>(alo, bv[n], acc[n]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const int i = i0 + 4 * kb + e;
+        if (i < T) {
+            const float inv = 1.0f / l_run[e];
+            float *o = out + ((size_t)hq * T + i) * D + r;
+#pragma unroll
+            for (int n = 0; n < 8; n++) o[16 * n] = acc[n][e] * inv;
+            if (r == 0) stats[(size_t)hq * T + i] = make_float2(m_run[e], inv);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- stage 2
+template <int DT>
+__global__ __launch_bounds__(64) void prefill_colsum_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const float2 *__restrict__ stats, float *__restrict__ score, int T, int g, float qscale) {
+    const int h = blockIdx.y, j0 = blockIdx.x * 16;
+    const int lane = threadIdx.x, r = lane & 15, kb = lane >> 4;
+    const int j = j0 + r;  // this lane's key (column)
+    u4_t bk[4];
+    {
+        const uint16_t *krow = k + ((size_t)h * T + min(j, T - 1)) * D;
+#pragma unroll
+        for (int m = 0; m < 4; m++) bk[m] = *reinterpret_cast<const u4_t *>(krow + 32 * m + 8 * kb);
+    }
+    const int nblk = (T - j0 + 15) / 16;  // query blocks i0 = j0 + 16 b
+    float cs = 0.0f;
+    for (int a = 0; a < g; a++) {
+        const int hq = h * g + a;
+        const uint16_t *qh = q + (size_t)hq * T * D;
+        const float2 *sth = stats + (size_t)hq * T;
+        // two query blocks per step: the loads of both go out before the math
+        for (int b = 0; b < nblk; b += 2) {
+            u4_t aq[2][4];
+            float2 st[2][4];
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                const int i0 = j0 + 16 * min(b + u, nblk - 1);
+                const uint16_t *qrow = qh + (size_t)min(i0 + r, T - 1) * D;
+#pragma unroll
+                for (int m = 0; m < 4; m++) aq[u][m] = *reinterpret_cast<const u4_t *>(qrow + 32 * m + 8 * kb);
+#pragma unroll
+                for (int e = 0; e < 4; e++) st[u][e] = sth[min(i0 + 4 * kb + e, T - 1)];
+            }
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                if (b + u >= nblk) break;
+                const int i0 = j0 + 16 * (b + u);
+                f4_t c = {0, 0, 0, 0};
+#pragma unroll
+                for (int m = 0; m < 4; m++) c = mfma_dt<DT>(aq[u][m], bk[m], c);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int i = i0 + 4 * kb + e;
+                    const float pr = __builtin_amdgcn_exp2f(c[e] * qscale - st[u][e].x) * st[u][e].y;
+                    cs += i < T && j <= i ? pr : 0.0f;
+                }
+            }
+        }
+    }
+    cs += __shfl_xor(cs, 16, 64);
+    cs += __shfl_xor(cs, 32, 64);
+    if (kb == 0 && j < T) score[(size_t)h * T + j] = cs;
+}
+
+// ---------------------------------------------------------------- stage 3
+// inclusive scan of v over the workgroup (thread order); *total = the sum
+__device__ __forceinline__ unsigned block_scan(unsigned v, unsigned *buf, unsigned *total) {
+    const int t = threadIdx.x;
+    buf[t] = v;
+    __syncthreads();
+    for (int off = 1; off < kSelThreads; off <<= 1) {
+        const unsigned x = t >= off ? buf[t - off] : 0u;
+        __syncthreads();
+        buf[t] += x;
+        __syncthreads();
+    }
+    const unsigned inc = buf[t];
+    *total = buf[kSelThreads - 1];
+    __syncthreads();
+    return inc;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__restrict__ score,
+                                                             int T, int heavy, int recent,
+                                                             int32_t *__restrict__ keep,
+                                                             int n_keep) {
+    __shared__ unsigned buf[kSelThreads];
+    const int h = blockIdx.x, t = threadIdx.x;
+    const uint32_t *sb = reinterpret_cast<const uint32_t *>(score + (size_t)h * T);
+    const int rec = min(recent, T), n_old = T - rec, hv = min(heavy, n_old);
+    const int chunk = (T + kSelThreads - 1) / kSelThreads;
+    const int b0 = min(T, t * chunk), b1 = min(T, b0 + chunk), ob1 = min(n_old, b1);
+    unsigned thr = 0xffffffffu, need = 0, tot;
+    if (hv > 0) {
+        // largest bit pattern u with #(bits >= u) >= hv: the hv-th largest score
+        unsigned prefix = 0;
+        for (int bit = 31; bit >= 0; bit--) {
+            const unsigned cand = prefix | (1u << bit);
+            unsigned cnt = 0;
+            for (int x = b0; x < ob1; x++) cnt += sb[x] >= cand;
+            block_scan(cnt, buf, &tot);
+            if (tot >= (unsigned)hv) prefix = cand;
+        }
+        thr = prefix;
+        unsigned above = 0;
+        for (int x = b0; x < ob1; x++) above += sb[x] > thr;
+        block_scan(above, buf, &tot);
+        need = (unsigned)hv - tot;  // positions at the threshold score to keep, lowest first
+    }
+    // ties at the threshold before this thread's chunk
+    unsigned ties = 0;
+    for (int x = b0; x < ob1; x++) ties += sb[x] == thr;
+    const unsigned tie0 = block_scan(ties, buf, &tot) - ties;
+    // kept positions of this chunk, then their places
+    unsigned kept = 0, rank = tie0;
+    for (int x = b0; x < b1; x++) {
+        const bool k = x >= n_old || sb[x] > thr || (sb[x] == thr && rank++ < need);
+        kept += k;
+    }
+    const unsigned pos0 = block_scan(kept, buf, &tot) - kept;
+    unsigned pos = pos0;
+    rank = tie0;
+    for (int x = b0; x < b1; x++) {
+        const bool k = x >= n_old || sb[x] > thr || (sb[x] == thr && rank++ < need);
+        if (k && pos < (unsigned)n_keep) keep[(size_t)h * n_keep + pos++] = x;
+    }
+}
+
+// ---------------------------------------------------------------- stage 4
+__global__ __launch_bounds__(64) void gather_kernel(const uint16_t *__restrict__ k,
+                                                    const uint16_t *__restrict__ v,
+                                                    const int32_t *__restrict__ keep,
+                                                    uint16_t *__restrict__ k_sel,
+                                                    uint16_t *__restrict__ v_sel, int T,
+                                                    int n_keep) {
+    const int p = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+    const int src = min(max(keep[(size_t)h * n_keep + p], 0), T - 1);
+    const int c8 = lane & 15;
+    const uint16_t *from = (lane < 16 ? k : v) + ((size_t)h * T + src) * D;
+    uint16_t *to = (lane < 16 ? k_sel : v_sel) + ((size_t)h * n_keep + p) * D;
+    if (lane < 32)
+        *reinterpret_cast<uint4 *>(to + 8 * c8) = *reinterpret_cast<const uint4 *>(from + 8 * c8);
+}
+
+template <int DT>
+hipError_t prefill_launch(const PrefillArgs &a, hipStream_t st) {
+    const int g = a.Hq / a.Hkv;
+    const float qscale = a.scale * kLog2e;
+    hipLaunchKernelGGL(v_transpose_kernel, dim3(a.T32 / 32, a.Hkv), dim3(256), 0, st, a.v, a.vt,
+                       a.T, a.T32);
+    hipLaunchKernelGGL((prefill_fwd_kernel<DT>), dim3((a.T + 15) / 16, a.Hq), dim3(64), 0, st, a.q,
+                       a.k, a.vt, a.out, a.stats, a.T, a.T32, g, qscale);
+    hipLaunchKernelGGL((prefill_colsum_kernel<DT>), dim3((a.T + 15) / 16, a.Hkv), dim3(64), 0, st,
+                       a.q, a.k, a.stats, a.score, a.T, g, qscale);
+    if (a.n_keep > 0) {
+        hipLaunchKernelGGL(select_kernel, dim3(a.Hkv), dim3(kSelThreads), 0, st, a.score, a.T,
+                           a.heavy, a.recent, a.keep, a.n_keep);
+        if (a.k_sel && a.v_sel)
+            hipLaunchKernelGGL(gather_kernel, dim3(a.n_keep, a.Hkv), dim3(64), 0, st, a.k, a.v,
+                               a.keep, a.k_sel, a.v_sel, a.T, a.n_keep);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t st) {
+    return dtype == F16 ? prefill_launch<F16>(a, st) : prefill_launch<BF16>(a, st);
+}
+
+}  // namespace kvq

@@ -21,7 +21,7 @@ PAGE = 128
 RESIDUAL = 128
 
 (ROLE_CHANNELS, ROLE_K, ROLE_V, ROLE_Q, ROLE_STEP_K, ROLE_STEP_V, ROLE_STEP_Q,
- ROLE_LENGTHS) = range(8)
+ ROLE_LENGTHS, ROLE_PREFILL_Q) = range(9)
 
 
 @dataclass(frozen=True)
@@ -39,6 +39,7 @@ class Workload:
     outlier_gain: float = 1.0
     decode_steps: int = 0  # streaming steps after the prefill
     ctx_spread: int = 0    # variable-length batch: lengths uniform in ctx +- ctx_spread
+    select: float = 0.0    # prefill with token selection: heavy and recent share of ctx each
 
     @property
     def seed(self):
@@ -75,6 +76,8 @@ WORKLOADS = {
                  decode_steps=256),
         Workload("llama3_8b_varlen", 6, 16, 32, 8, 8192, 16, BF16, "outlier", 6, 8.0,
                  ctx_spread=7168),
+        Workload("llama3_8b_prefill_select", 7, 1, 32, 8, 8192, 16, BF16, "outlier", 6, 8.0,
+                 select=0.25),
     ]
 }
 
@@ -145,6 +148,12 @@ def seq_lengths(w):
         return np.full(w.B, w.ctx, np.int64)
     r = rng(w.seed, ROLE_LENGTHS)
     return r.integers(w.ctx - w.ctx_spread, w.ctx + w.ctx_spread + 1, size=w.B)
+
+
+def prefill_q(w, T, b=0):
+    """Prefill queries of sequence b: [Hq][T][128] uint16, N(0, 1)."""
+    r = rng(w.seed, ROLE_PREFILL_Q, b)
+    return to_bits(r.standard_normal((w.Hq, T, HEAD_DIM), dtype=np.float32), w.dtype)
 
 
 def query(w, step=None):

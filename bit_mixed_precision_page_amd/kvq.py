@@ -31,7 +31,8 @@ EXPORTS = ["kvq_cache_bytes", "kvq_page_bytes", "kvq_cache_create", "kvq_cache_d
            "kvq_pool_block_of", "kvq_pool_free_blocks", "kvq_pool_page_offset",
            "kvq_pool_window_offset", "kvq_pool_table_offset", "kvq_pool_set_kernel_events",
            "kvq_set_channel_relevance", "kvq_query_relevance", "kvq_pool_set_channel_relevance",
-           "kvq_device_state_init", "kvq_append_decode_device"]
+           "kvq_device_state_init", "kvq_append_decode_device",
+           "kvq_prefill_workspace_bytes", "kvq_prefill_select"]
 
 
 class KvqError(RuntimeError):
@@ -103,6 +104,9 @@ _SIG = {
     "kvq_pool_set_channel_relevance": [_vp, _vp],
     "kvq_device_state_init": [_vp, _vp, _vp],
     "kvq_append_decode_device": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp],
+    "kvq_prefill_workspace_bytes": [_i32, _i32, _i32, ctypes.POINTER(_sz)],
+    "kvq_prefill_select": [_i32, _i32, _i32, _i32, ctypes.c_float, _vp, _vp, _vp, _i32, _i32,
+                           _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, ctypes.POINTER(_i32)],
 }
 for _name, _args in _SIG.items():
     _f = getattr(_L, _name)
@@ -251,6 +255,46 @@ def kvq_set_channel_relevance(handle, rel):
 def kvq_query_relevance(dtype, batch, num_q_heads, num_kv_heads, q, rel, stream=None):
     _check(_L.kvq_query_relevance(dtype, batch, num_q_heads, num_kv_heads, _ptr(q), _ptr(rel),
                                   _stream(stream)), "kvq_query_relevance")
+
+
+def kvq_prefill_workspace_bytes(T, num_q_heads, num_kv_heads):
+    n = _sz()
+    _check(_L.kvq_prefill_workspace_bytes(T, num_q_heads, num_kv_heads, ctypes.byref(n)),
+           "kvq_prefill_workspace_bytes")
+    return n.value
+
+
+def kvq_prefill_select(dtype, T, num_q_heads, num_kv_heads, softmax_scale, q, k, v, heavy, recent,
+                       out, score, keep, k_sel, v_sel, workspace, ws_bytes, stream=None):
+    n = _i32()
+    _check(_L.kvq_prefill_select(dtype, T, num_q_heads, num_kv_heads, softmax_scale, _ptr(q),
+                                 _ptr(k), _ptr(v), heavy, recent, _ptr(out), _ptr(score),
+                                 _ptr(keep), _ptr(k_sel), _ptr(v_sel), _ptr(workspace), ws_bytes,
+                                 _stream(stream), ctypes.byref(n)), "kvq_prefill_select")
+    return n.value
+
+
+def prefill_select(dtype, q, k, v, heavy, recent, softmax_scale=0.0, gather=True, stream=None):
+    """Allocate the outputs (torch device tensors) and run kvq_prefill_select.
+    q: [Hq][T][128], k, v: [Hkv][T][128] int16 bit patterns.  Returns (out,
+    score, keep, k_sel, v_sel); k_sel and v_sel are None without gather."""
+    Hq, T, _ = q.shape
+    Hkv = k.shape[0]
+    dev = q.device
+    rec = min(recent, T)
+    nk = min(heavy, T - rec) + rec
+    out = torch.empty(Hq, T, 128, dtype=torch.float32, device=dev)
+    score = torch.empty(Hkv, T, dtype=torch.float32, device=dev)
+    keep = torch.empty(Hkv, max(nk, 1), dtype=torch.int32, device=dev)
+    k_sel = torch.empty(Hkv, max(nk, 1), 128, dtype=torch.int16, device=dev) if gather else None
+    v_sel = torch.empty_like(k_sel) if gather else None
+    wsb = kvq_prefill_workspace_bytes(T, Hq, Hkv)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    n = kvq_prefill_select(dtype, T, Hq, Hkv, softmax_scale, q, k, v, heavy, recent, out, score,
+                           keep, k_sel, v_sel, ws, wsb, stream)
+    assert n == nk
+    return out, score, keep[:, :nk], (k_sel[:, :nk] if gather else None), \
+        (v_sel[:, :nk] if gather else None)
 
 
 def kvq_pool_set_channel_relevance(handle, rel):

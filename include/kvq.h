@@ -325,6 +325,37 @@ int kvq_pool_set_channel_relevance(kvq_pool *pool, const float *rel);
 /* Timing hooks of the pool's split kernel (as kvq_set_kernel_events). */
 int kvq_pool_set_kernel_events(kvq_pool *pool, void *before, void *after);
 
+/* ---- Prefill with cumulative attention scores and token selection ----
+   MiniKV summary (f-binder), "proposed method": the prefill processes the
+   whole input and keeps the heavy hitters by cumulative attention score plus
+   a recent window (25 % of the budget each by default); a two-stage selective
+   flash-attention gives the attention output and the cumulative scores in
+   linear memory.  One sequence per call:
+     q: device [Hq][T][128] dtype; k, v: device [Hkv][T][128] dtype (query
+     head hq reads KV head hq / (Hq / Hkv)); softmax_scale <= 0 means
+     1/sqrt(128).
+     out: device [Hq][T][128] float32, causal attention (row i attends to
+     positions j <= i).
+     score: device [Hkv][T] float32: score[h][j] = sum over the query heads
+     of KV head h and the rows i >= j of the softmax probability P[i][j].
+     keep: device [Hkv][n_keep] int32: the last min(recent, T) positions plus
+     the min(heavy, T - that) positions of largest score among the others
+     (ties to the lower position), ascending; n_keep is returned at once.
+     k_sel, v_sel: device [Hkv][n_keep][128] dtype, the kept rows of k and v
+     (both NULL: no gather), ready for kvq_quantize_page / kvq_append_token.
+     workspace: device, kvq_prefill_workspace_bytes; the caller owns every
+     buffer, launches are asynchronous on the stream.
+   Preconditions: finite inputs.  Errors: KVQ_EINVAL (shape: 1 <= T <= 2^20,
+   Hq a multiple of Hkv with at most 16 query heads per KV head), KVQ_EALIGN
+   (16-byte alignment), KVQ_EWORKSPACE, KVQ_EHIP. */
+int kvq_prefill_workspace_bytes(int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                                size_t *bytes);
+int kvq_prefill_select(int32_t dtype, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                       float softmax_scale, const void *q, const void *k, const void *v,
+                       int32_t heavy, int32_t recent, float *out, float *score, int32_t *keep,
+                       void *k_sel, void *v_sel, void *workspace, size_t ws_bytes, void *stream,
+                       int32_t *n_keep);
+
 #ifdef __cplusplus
 }
 #endif
