@@ -133,6 +133,8 @@ def main():
         return stream_main(a, w, torch, gen, kvq)
     if w.ctx_spread:
         return pool_main(a, w, torch, gen, kvq)
+    if w.select:
+        return prefill_main(a, w, torch, gen, kvq)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -389,6 +391,88 @@ def stream_main(a, w, torch, gen, kvq):
         "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)
+
+
+def prefill_flops(T, Hq):
+    """Algorithmic flops of one prefill selection: causal Q K^T and P V of the
+    attention (2 T^2 / 2 Hq D flops each) and the Q K^T the cumulative scores
+    recompute (two-stage selective flash-attention, MiniKV summary)."""
+    return 3.0 * T * T * Hq * 128
+
+
+def prefill_main(a, w, torch, gen, kvq):
+    """Prefill of one sequence with cumulative attention scores and
+    heavy-hitter + recent selection (kvq_prefill_select: attention output,
+    scores, kept positions and the gathered kept rows), timed per call."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+
+    T = w.ctx
+    heavy = recent = int(w.select * T)
+    print(f"[bench] workload {w.name}: T={T} Hq={w.Hq} Hkv={w.Hkv} heavy={heavy} recent={recent}",
+          file=sys.stderr, flush=True)
+    q = gen.prefill_q(w, T)
+    K, V = gen.prefill_kv(w, ntok=T)
+    qd, kd, vd = to_dev(q), to_dev(K[0]), to_dev(V[0])
+    rec = min(recent, T)
+    nk = min(heavy, T - rec) + rec
+    out = torch.empty(w.Hq, T, 128, dtype=torch.float32, device=dev)
+    score = torch.empty(w.Hkv, T, dtype=torch.float32, device=dev)
+    keep = torch.empty(w.Hkv, nk, dtype=torch.int32, device=dev)
+    k_sel = torch.empty(w.Hkv, nk, 128, dtype=torch.int16, device=dev)
+    v_sel = torch.empty_like(k_sel)
+    wsb = kvq.kvq_prefill_workspace_bytes(T, w.Hq, w.Hkv)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def call():
+        kvq.kvq_prefill_select(w.dtype, T, w.Hq, w.Hkv, 0.0, qd, kd, vd, heavy, recent, out,
+                               score, keep, k_sel, v_sel, ws, wsb)
+
+    steps = max(1, min(a.steps, 50))
+    warm = max(1, min(a.warmup, 5))
+    for _ in range(warm):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = prefill_flops(T, w.Hq)
+    tf = fl / (ms / 1e3) / 1e12
+    print(f"[bench] {steps} calls, {ms * 1e3:.1f} us per call, {tf:.1f} TFLOP/s algorithmic",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not a.no_cpu_baseline:
+        import oracle
+        ora = oracle.lib()
+        T0 = 1024  # the oracle on the first T0 positions (~10 s of host work)
+        tc = time.time()
+        ora.prefill_attention(w.dtype, q[:, :T0], K[0][:, :T0], V[0][:, :T0], 1.0 / np.sqrt(128))
+        dt = time.time() - tc
+        cpu = {"value": round(prefill_flops(T0, w.Hq) / dt / 1e12, 6), "unit": "TFLOP/s",
+               "cores": ora.num_threads(), "kind": "oracle",
+               "sample": f"fp64 prefill attention + cumulative scores of the first {T0} positions "
+                         f"({w.Hq} query heads) in {dt:.1f} s"}
+    rec_ = {
+        "metric": "prefill attention + cumulative scores + heavy-hitter/recent selection, "
+                  "algorithmic TFLOP/s (one sequence)",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == gen.BF16 else "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": 128, "heavy": heavy, "recent": recent, "kept": nk},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(tf / 2500.0, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec_), flush=True)
 
 
 def pool_main(a, w, torch, gen, kvq):
