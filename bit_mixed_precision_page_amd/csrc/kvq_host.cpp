@@ -247,9 +247,13 @@ namespace {
 constexpr int64_t kPrefillMaxT = 1 << 20;  // positions of one prefill
 
 size_t prefill_stats_bytes(int32_t T, int32_t Hq) { return align256((size_t)Hq * T * 8); }
+size_t prefill_part_bytes(int32_t T, int32_t Hkv) {
+    return align256((size_t)Hkv * kvq::kColsumChunks * T * 4);
+}
 size_t prefill_ws_bytes(int32_t T, int32_t Hq, int32_t Hkv) {
     const size_t T32 = ((size_t)T + 31) / 32 * 32;
-    return prefill_stats_bytes(T, Hq) + (size_t)Hkv * kvq::D * T32 * 2;
+    return prefill_stats_bytes(T, Hq) + prefill_part_bytes(T, Hkv) +
+           (size_t)Hkv * kvq::D * T32 * 2;
 }
 int prefill_shape_ok(int32_t T, int32_t Hq, int32_t Hkv) {
     return T >= 1 && T <= kPrefillMaxT && Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 &&
@@ -540,7 +544,9 @@ int kvq_prefill_select(int32_t dtype, int32_t T, int32_t num_q_heads, int32_t nu
     a.v = static_cast<const uint16_t *>(v);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     a.stats = reinterpret_cast<float2 *>(ws);
-    a.vt = reinterpret_cast<uint16_t *>(ws + prefill_stats_bytes(T, num_q_heads));
+    a.part = reinterpret_cast<float *>(ws + prefill_stats_bytes(T, num_q_heads));
+    a.vt = reinterpret_cast<uint16_t *>(ws + prefill_stats_bytes(T, num_q_heads) +
+                                        prefill_part_bytes(T, num_kv_heads));
     a.out = out;
     a.score = score;
     a.keep = keep;

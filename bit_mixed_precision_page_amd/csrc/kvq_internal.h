@@ -96,6 +96,8 @@ struct DecodePlan {
 };
 size_t decode_workspace_bytes(const Geometry &G, int max_splits);
 
+// Query chunks the column sums of the cumulative scores are split over.
+constexpr int kColsumChunks = 16;
 // Prefill of one sequence: causal attention with cumulative attention scores,
 // heavy-hitter + recent token selection and the gather of the kept rows.
 struct PrefillArgs {
@@ -104,6 +106,7 @@ struct PrefillArgs {
     const uint16_t *q, *k, *v;  // [Hq][T][D], [Hkv][T][D], [Hkv][T][D]
     uint16_t *vt;               // workspace: [Hkv][D][T32] transposed Values
     float2 *stats;              // workspace: [Hq][T] (row max in log2 units, 1 / row sum)
+    float *part;                // workspace: [Hkv][kColsumChunks][T] partial column sums
     float *out, *score;         // [Hq][T][D], [Hkv][T]
     int32_t *keep;              // [Hkv][n_keep]
     uint16_t *k_sel, *v_sel;    // [Hkv][n_keep][D], or null

@@ -20,11 +20,12 @@
 //          dtype hi and lo part (~16 bits for bf16, ~22 for fp16); P V with 2
 //          MFMAs per 16-channel tile, accumulated in the MFMA results.
 //          Writes out (fp32) and per row (max, 1 / sum).
-// Stage 2  cumulative scores: one wave per 16 keys of one KV head runs over
-//          every query head of the group and every 16-row query block at or
-//          after its keys: S again, P = 2^(s - m_i) / l_i from the stage-1
-//          row statistics, column sums in registers.  A wave owns its keys,
-//          so the sums are deterministic.
+// Stage 2  cumulative scores: one wave per (16 keys, chunk of query blocks,
+//          KV head) runs over every query head of the group and every 16-row
+//          query block of its chunk at or after its keys: S again,
+//          P = 2^(s - m_i) / l_i from the stage-1 row statistics, column sums
+//          in registers; a second kernel adds the chunks' partial sums in
+//          chunk order, so the scores do not depend on scheduling.
 // Stage 3  selection, one workgroup per KV head: the heavy-th largest score
 //          by a bitwise search over the score bits (scores are >= 0, so the
 //          bits order like the values), ties at that score resolved to the
@@ -87,7 +88,8 @@ __global__ __launch_bounds__(64) void prefill_fwd_kernel(
     int T32, int g, float qscale) {
     __shared__ __align__(16) float px[16][36];  // P [query row][key], rows padded
     const int hq = blockIdx.y, h = hq / g;
-    const int i0 = blockIdx.x * 16;
+    // the last query blocks see the most keys: dispatched first
+    const int i0 = (gridDim.x - 1 - blockIdx.x) * 16;
     const int lane = threadIdx.x, r = lane & 15, kb = lane >> 4;
     // A operand: query row i0 + r, channels 32 m + 8 kb + [0, 8)
     u4_t aq[4];
@@ -129,6 +131,7 @@ __global__ __launch_bounds__(64) void prefill_fwd_kernel(
         for (int n = 0; n < 8; n++)
             bv[n] = *reinterpret_cast<const u4_t *>(vth + (size_t)(16 * n + r) * T32 + j0 + 8 * kb);
         float p[2][4], alpha[4];
+        bool grew = false;
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             const int i = min(i0 + 4 * kb + e, T - 1);
@@ -141,6 +144,7 @@ __global__ __launch_bounds__(64) void prefill_fwd_kernel(
             }
             // every row has a key <= i in every block it visits, so bm is finite
             const float mn = fmaxf(m_run[e], row_max(bm));
+            grew |= mn > m_run[e];
             alpha[e] = __builtin_amdgcn_exp2f(m_run[e] - mn);
             m_run[e] = mn;
             float ps = 0.0f;
@@ -151,10 +155,12 @@ __global__ __launch_bounds__(64) void prefill_fwd_kernel(
             }
             l_run[e] = fmaf(l_run[e], alpha[e], row_sum(ps));
         }
+        if (__any(grew)) {  // wave-uniform: rescale only when a row maximum grows
 #pragma unroll
-        for (int n = 0; n < 8; n++)
+            for (int n = 0; n < 8; n++)
 #pragma unroll
-            for (int e = 0; e < 4; e++) acc[n][e] *= alpha[e];
+                for (int e = 0; e < 4; e++) acc[n][e] *= alpha[e];
+        }
         wave_sync();  // the previous block's reads of px are done
 #pragma unroll
         for (int t = 0; t < 2; t++)
@@ -191,11 +197,16 @@ __global__ __launch_bounds__(64) void prefill_fwd_kernel(
 }
 
 // ---------------------------------------------------------------- stage 2
+// Workgroup (key tile x, query chunk y, KV head z): query blocks
+// [y cq, y cq + cq) at or after the tile; the partial column sums go to
+// part[h][y][T] and a second kernel adds the chunks in order, so the scores
+// do not depend on scheduling.
 template <int DT>
 __global__ __launch_bounds__(64) void prefill_colsum_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const float2 *__restrict__ stats, float *__restrict__ score, int T, int g, float qscale) {
-    const int h = blockIdx.y, j0 = blockIdx.x * 16;
+    const float2 *__restrict__ stats, float *__restrict__ part, int T, int g, float qscale,
+    int cq, int nchunk) {
+    const int h = blockIdx.z, j0 = blockIdx.x * 16, chunk = blockIdx.y;
     const int lane = threadIdx.x, r = lane & 15, kb = lane >> 4;
     const int j = j0 + r;  // this lane's key (column)
     u4_t bk[4];
@@ -204,7 +215,10 @@ __global__ __launch_bounds__(64) void prefill_colsum_kernel(
 #pragma unroll
         for (int m = 0; m < 4; m++) bk[m] = *reinterpret_cast<const u4_t *>(krow + 32 * m + 8 * kb);
     }
-    const int nblk = (T - j0 + 15) / 16;  // query blocks i0 = j0 + 16 b
+    // query blocks i0 = 16 (qb0 + b), b < nblk
+    const int nqb = (T + 15) / 16;
+    const int qb0 = max(chunk * cq, blockIdx.x);
+    const int nblk = max(0, min(nqb, chunk * cq + cq) - qb0);
     float cs = 0.0f;
     for (int a = 0; a < g; a++) {
         const int hq = h * g + a;
@@ -216,7 +230,7 @@ __global__ __launch_bounds__(64) void prefill_colsum_kernel(
             float2 st[2][4];
 #pragma unroll
             for (int u = 0; u < 2; u++) {
-                const int i0 = j0 + 16 * min(b + u, nblk - 1);
+                const int i0 = 16 * (qb0 + min(b + u, nblk - 1));
                 const uint16_t *qrow = qh + (size_t)min(i0 + r, T - 1) * D;
 #pragma unroll
                 for (int m = 0; m < 4; m++) aq[u][m] = *reinterpret_cast<const u4_t *>(qrow + 32 * m + 8 * kb);
@@ -226,7 +240,7 @@ __global__ __launch_bounds__(64) void prefill_colsum_kernel(
 #pragma unroll
             for (int u = 0; u < 2; u++) {
                 if (b + u >= nblk) break;
-                const int i0 = j0 + 16 * (b + u);
+                const int i0 = 16 * (qb0 + b + u);
                 f4_t c = {0, 0, 0, 0};
 #pragma unroll
                 for (int m = 0; m < 4; m++) c = mfma_dt<DT>(aq[u][m], bk[m], c);
@@ -241,7 +255,18 @@ __global__ __launch_bounds__(64) void prefill_colsum_kernel(
     }
     cs += __shfl_xor(cs, 16, 64);
     cs += __shfl_xor(cs, 32, 64);
-    if (kb == 0 && j < T) score[(size_t)h * T + j] = cs;
+    if (kb == 0 && j < T) part[((size_t)h * nchunk + chunk) * T + j] = cs;
+}
+
+// score[h][j] = sum of the chunks' partial sums, chunk 0 first
+__global__ __launch_bounds__(256) void colsum_reduce_kernel(const float *__restrict__ part,
+                                                            float *__restrict__ score, int T,
+                                                            int nchunk) {
+    const int h = blockIdx.y, j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= T) return;
+    float s = 0.0f;
+    for (int c = 0; c < nchunk; c++) s += part[((size_t)h * nchunk + c) * T + j];
+    score[(size_t)h * T + j] = s;
 }
 
 // ---------------------------------------------------------------- stage 3
@@ -332,8 +357,13 @@ hipError_t prefill_launch(const PrefillArgs &a, hipStream_t st) {
                        a.T, a.T32);
     hipLaunchKernelGGL((prefill_fwd_kernel<DT>), dim3((a.T + 15) / 16, a.Hq), dim3(64), 0, st, a.q,
                        a.k, a.vt, a.out, a.stats, a.T, a.T32, g, qscale);
-    hipLaunchKernelGGL((prefill_colsum_kernel<DT>), dim3((a.T + 15) / 16, a.Hkv), dim3(64), 0, st,
-                       a.q, a.k, a.stats, a.score, a.T, g, qscale);
+    const int nqb = (a.T + 15) / 16;
+    const int cq = (nqb + kColsumChunks - 1) / kColsumChunks;
+    const int nchunk = (nqb + cq - 1) / cq;
+    hipLaunchKernelGGL((prefill_colsum_kernel<DT>), dim3(nqb, nchunk, a.Hkv), dim3(64), 0, st,
+                       a.q, a.k, a.stats, a.part, a.T, g, qscale, cq, nchunk);
+    hipLaunchKernelGGL(colsum_reduce_kernel, dim3((a.T + 255) / 256, a.Hkv), dim3(256), 0, st,
+                       a.part, a.score, a.T, nchunk);
     if (a.n_keep > 0) {
         hipLaunchKernelGGL(select_kernel, dim3(a.Hkv), dim3(kSelThreads), 0, st, a.score, a.T,
                            a.heavy, a.recent, a.keep, a.n_keep);
