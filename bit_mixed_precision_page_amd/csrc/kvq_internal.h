@@ -104,7 +104,7 @@ struct PrefillArgs {
     int T, T32, Hq, Hkv, heavy, recent, n_keep;
     float scale;
     const uint16_t *q, *k, *v;  // [Hq][T][D], [Hkv][T][D], [Hkv][T][D]
-    uint16_t *vt;               // workspace: [Hkv][D][T32] transposed Values
+    uint16_t *vt;               // workspace: [Hkv][T32 / 32][D][32] transposed Values
     float2 *stats;              // workspace: [Hq][T] (row max in log2 units, 1 / row sum)
     float *part;                // workspace: [Hkv][kColsumChunks][T] partial column sums
     float *out, *score;         // [Hq][T][D], [Hkv][T]

@@ -11,15 +11,18 @@
 // the last `recent` positions are kept, plus the `heavy` positions of largest
 // score among the others (ties to the lower position), listed ascending.
 //
-// Stage 0  Values transposed to [Hkv][D][T32] (T32 = T rounded up to 32, zero
-//          tail), so a lane's P.V operand is 16 contiguous bytes.
-// Stage 1  flash attention: one wave per 16 query rows of one query head, 32
-//          keys per step.  S = Q K^T on the matrix cores (the dtype inputs are
-//          exact, fp32 accumulation); online softmax in the log2 domain; P
-//          through a 2 KB LDS transpose into the operand layout, split into a
-//          dtype hi and lo part (~16 bits for bf16, ~22 for fp16); P V with 2
-//          MFMAs per 16-channel tile, accumulated in the MFMA results.
-//          Writes out (fp32) and per row (max, 1 / sum).
+// Stage 0  Values transposed per 32-key block to [Hkv][T32 / 32][D][32]
+//          (T32 = T rounded up to 32, zero tail), keys in the order a lane of
+//          the transposed score tile holds them: a lane's P.V operand is one
+//          16-byte read.
+// Stage 1  flash attention: four-wave workgroups over the query heads of
+//          one KV head (up to four) and 32 query rows per wave; each 32-key
+//          block of Keys and Values is staged once in LDS for the workgroup
+//          (double buffered).  S^T = K Q^T on the matrix cores (the dtype
+//          inputs are exact, fp32 accumulation); online softmax in the log2
+//          domain; P^T split into a dtype hi and lo part (~16 bits for bf16,
+//          ~22 for fp16) feeds O^T = V^T P^T directly, 2 MFMAs per
+//          16-channel tile.  Writes out (fp32) and per row (max, 1 / sum).
 // Stage 2  cumulative scores: one wave per (16 keys, chunk of query blocks,
 //          KV head) runs over every query head of the group and every 16-row
 //          query block of its chunk at or after its keys: S again,
@@ -56,12 +59,22 @@ __device__ __forceinline__ float hi16(uint32_t w) {
     return dec<DT>((uint16_t)(w >> 16));
 }
 
+// Key of slot s in a 32-key block of the Value operand: slots 8 b + [0, 4)
+// hold keys 4 b + [0, 4) and slots 8 b + [4, 8) keys 16 + 4 b + [0, 4), the
+// keys a lane of the transposed score tiles holds (see prefill_fwd_kernel).
+__device__ __forceinline__ int slot_key(int s) {
+    const int b = s >> 3, e = s & 7;
+    return e < 4 ? 4 * b + e : 12 + 4 * b + e;
+}
+
 // ---------------------------------------------------------------- stage 0
+// vt[h][blk][c][s] = v[h][32 blk + slot_key(s)][c], zero past T: each
+// 32-key block's transposed Values are one contiguous 8 KB.
 __global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t *__restrict__ v,
                                                           uint16_t *__restrict__ vt, int T,
                                                           int T32) {
     __shared__ uint16_t tile[32][D + 8];
-    const int h = blockIdx.y, t0 = blockIdx.x * 32, tid = threadIdx.x;
+    const int h = blockIdx.y, blk = blockIdx.x, t0 = blk * 32, tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 2; i++) {  // 32 tokens x 16 chunks of 8 channels
         const int x = tid + 256 * i, tok = x >> 4, c8 = x & 15;
@@ -70,128 +83,176 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t *__rest
         *reinterpret_cast<uint4 *>(&tile[tok][8 * c8]) = w;
     }
     __syncthreads();
-    const int c = tid >> 1, half = tid & 1;  // channel c, tokens 16 half + [0, 16)
+    const int c = tid >> 1, half = tid & 1;  // channel c, slots 16 half + [0, 16)
     uint32_t o[8];
 #pragma unroll
-    for (int e = 0; e < 8; e++)
-        o[e] = (uint32_t)tile[16 * half + 2 * e][c] | ((uint32_t)tile[16 * half + 2 * e + 1][c] << 16);
-    uint4 *dst = reinterpret_cast<uint4 *>(vt + ((size_t)h * D + c) * T32 + t0 + 16 * half);
+    for (int e = 0; e < 8; e++) {
+        const int s = 16 * half + 2 * e;
+        o[e] = (uint32_t)tile[slot_key(s)][c] | ((uint32_t)tile[slot_key(s + 1)][c] << 16);
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(vt + (((size_t)h * (T32 / 32) + blk) * D + c) * 32 + 16 * half);
     dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
     dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
 // ---------------------------------------------------------------- stage 1
+// Workgroup of four waves = hw query heads of one KV head x 4 / hw groups of
+// 32 query rows (hw = 4, 2 or 1, dividing the group size); a wave owns 32
+// rows (two 16-row tiles) of one query head.  Each 32-key block of Keys and
+// transposed Values (16 KB) is loaded once per workgroup into LDS (double
+// buffered, the next block's global loads in flight during this block's
+// math) and read by every wave; each operand read serves both row tiles.
+// The scores are computed transposed, S^T = K Q^T: a lane then holds one
+// query row and keys 4 b + e, 16 + 4 b + e of the block, which is directly
+// the B operand of O^T = V^T P^T once the Values are stored in the slot
+// order of slot_key -- no transpose of P.
+constexpr int kKRow = D + 8;          // LDS Key row (272 B: 16-byte reads conflict-free)
+constexpr int kVRow = 40;             // LDS Value row, 32 slots + pad (80 B)
+constexpr int kKTile = 32 * kKRow;    // elements
+constexpr int kFwdBuf = kKTile + D * kVRow;
+
 template <int DT>
-__global__ __launch_bounds__(64) void prefill_fwd_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ vt, float *__restrict__ out, float2 *__restrict__ stats, int T,
-    int T32, int g, float qscale) {
-    __shared__ __align__(16) float px[16][36];  // P [query row][key], rows padded
-    const int hq = blockIdx.y, h = hq / g;
-    // the last query blocks see the most keys: dispatched first
-    const int i0 = (gridDim.x - 1 - blockIdx.x) * 16;
-    const int lane = threadIdx.x, r = lane & 15, kb = lane >> 4;
-    // A operand: query row i0 + r, channels 32 m + 8 kb + [0, 8)
-    u4_t aq[4];
-    {
-        const uint16_t *qrow = q + ((size_t)hq * T + min(i0 + r, T - 1)) * D;
-#pragma unroll
-        for (int m = 0; m < 4; m++) aq[m] = *reinterpret_cast<const u4_t *>(qrow + 32 * m + 8 * kb);
-    }
-    // this lane's result rows: i0 + 4 kb + e
-    float m_run[4], l_run[4];
-    f4_t acc[8];
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        m_run[e] = -INFINITY;
-        l_run[e] = 0.0f;
-    }
-#pragma unroll
-    for (int n = 0; n < 8; n++) acc[n] = f4_t{0, 0, 0, 0};
-    const int nblk = min(T - 1, i0 + 15) / 32 + 1;
+    int T32, int g, int hw, float qscale) {
+    __shared__ __align__(16) uint16_t lds[2 * kFwdBuf];
+    const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kb = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hq = blockIdx.x * hw + w % hw, h = blockIdx.x * hw / g;
+    const int qr = 128 / hw;  // query rows of the workgroup
+    // the last query rows see the most keys: dispatched first
+    const int i0g = (gridDim.y - 1 - blockIdx.y) * qr;
+    const int i0w = i0g + 32 * (w / hw);
+    const int nbg = (min(T - 1, i0g + qr - 1)) / 32 + 1;
+    const int nbw = i0w < T ? (min(T - 1, i0w + 31)) / 32 + 1 : 0;
+    const int nb = T32 / 32;
     const uint16_t *kh = k + (size_t)h * T * D;
-    const uint16_t *vth = vt + (size_t)h * D * T32;
-    for (int jb = 0; jb < nblk; jb++) {
+    const uint16_t *vth = vt + (size_t)h * nb * D * 32;
+
+    // block jb -> registers (two 16-byte pieces of Keys and two of Values per thread)
+    u4_t pk[2], pv[2];
+    auto gload = [&](int jb) {
         const int j0 = 32 * jb;
-        f4_t s[2];
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int c = tid + 256 * i, key = c >> 4, c8 = c & 15;
+            pk[i] = j0 + key < T ? *reinterpret_cast<const u4_t *>(kh + (size_t)(j0 + key) * D + 8 * c8)
+                                 : u4_t{0, 0, 0, 0};
+            pv[i] = *reinterpret_cast<const u4_t *>(vth + (size_t)jb * D * 32 + 8 * c);
+        }
+    };
+    auto lstore = [&](int buf) {
+        uint16_t *L = lds + buf * kFwdBuf;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int c = tid + 256 * i;
+            *reinterpret_cast<u4_t *>(L + (c >> 4) * kKRow + 8 * (c & 15)) = pk[i];
+            *reinterpret_cast<u4_t *>(L + kKTile + (c >> 2) * kVRow + 8 * (c & 3)) = pv[i];
+        }
+    };
+
+    // B operand of S^T: query row i0w + 16 u + r, channels 32 m + 8 kb + [0, 8)
+    u4_t aq[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const uint16_t *qrow = q + ((size_t)hq * T + min(i0w + 16 * u + r, T - 1)) * D;
+#pragma unroll
+        for (int m = 0; m < 4; m++) aq[u][m] = *reinterpret_cast<const u4_t *>(qrow + 32 * m + 8 * kb);
+    }
+    float m_run[2], l_run[2];  // row max (log2 units); this lane's part of the row sum
+    f4_t acc[2][8];            // O^T: row i0w + 16 u + r, channels 16 n + 4 kb + e
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        m_run[u] = -INFINITY;
+        l_run[u] = 0.0f;
+#pragma unroll
+        for (int n = 0; n < 8; n++) acc[u][n] = f4_t{0, 0, 0, 0};
+    }
+
+    gload(0);
+    lstore(0);
+    if (nbg > 1) gload(1);
+    for (int jb = 0; jb < nbg; jb++) {
+        __syncthreads();  // block jb is in LDS; every wave is done with block jb - 1
+        if (jb + 1 < nbg) lstore((jb + 1) & 1);
+        if (jb + 2 < nbg) gload(jb + 2);
+        if (jb >= nbw) continue;
+        const uint16_t *L = lds + (jb & 1) * kFwdBuf;
+        const int j0 = 32 * jb;
+        f4_t s[2][2];
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-            const uint16_t *krow = kh + (size_t)min(j0 + 16 * t + r, T - 1) * D;
-            u4_t bk[4];
+            s[0][t] = f4_t{0, 0, 0, 0};
+            s[1][t] = f4_t{0, 0, 0, 0};
 #pragma unroll
-            for (int m = 0; m < 4; m++) bk[m] = *reinterpret_cast<const u4_t *>(krow + 32 * m + 8 * kb);
-            f4_t c = {0, 0, 0, 0};
-#pragma unroll
-            for (int m = 0; m < 4; m++) c = mfma_dt<DT>(aq[m], bk[m], c);
-            s[t] = c;
-        }
-        // V operands of this block (issued before the softmax)
-        u4_t bv[8];
-#pragma unroll
-        for (int n = 0; n < 8; n++)
-            bv[n] = *reinterpret_cast<const u4_t *>(vth + (size_t)(16 * n + r) * T32 + j0 + 8 * kb);
-        float p[2][4], alpha[4];
-        bool grew = false;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int i = min(i0 + 4 * kb + e, T - 1);
-            float bm = -INFINITY;
-#pragma unroll
-            for (int t = 0; t < 2; t++) {
-                const int j = j0 + 16 * t + r;
-                p[t][e] = j <= i ? s[t][e] * qscale : -INFINITY;
-                bm = fmaxf(bm, p[t][e]);
+            for (int m = 0; m < 4; m++) {
+                const u4_t ka = *reinterpret_cast<const u4_t *>(L + (16 * t + r) * kKRow + 32 * m + 8 * kb);
+                s[0][t] = mfma_dt<DT>(ka, aq[0][m], s[0][t]);
+                s[1][t] = mfma_dt<DT>(ka, aq[1][m], s[1][t]);
             }
-            // every row has a key <= i in every block it visits, so bm is finite
-            const float mn = fmaxf(m_run[e], row_max(bm));
-            grew |= mn > m_run[e];
-            alpha[e] = __builtin_amdgcn_exp2f(m_run[e] - mn);
-            m_run[e] = mn;
+        }
+        u4_t bhi[2], blo[2];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int i = min(i0w + 16 * u + r, T - 1);
+            float x[8], bm = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 2; t++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int j = j0 + 16 * t + 4 * kb + e;
+                    x[4 * t + e] = j <= i ? s[u][t][e] * qscale : -INFINITY;
+                    bm = fmaxf(bm, x[4 * t + e]);
+                }
+            bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+            // every visited block holds a key <= i, so bm is finite
+            const float mn = fmaxf(m_run[u], bm);
+            const bool grew = mn > m_run[u];
+            const float alpha = __builtin_amdgcn_exp2f(m_run[u] - mn);
+            m_run[u] = mn;
             float ps = 0.0f;
 #pragma unroll
-            for (int t = 0; t < 2; t++) {
-                p[t][e] = __builtin_amdgcn_exp2f(p[t][e] - mn);
-                ps += p[t][e];
+            for (int e = 0; e < 8; e++) {
+                x[e] = __builtin_amdgcn_exp2f(x[e] - mn);
+                ps += x[e];
             }
-            l_run[e] = fmaf(l_run[e], alpha[e], row_sum(ps));
-        }
-        if (__any(grew)) {  // wave-uniform: rescale only when a row maximum grows
+            l_run[u] = fmaf(l_run[u], alpha, ps);
+            if (__any(grew)) {  // wave-uniform: rescale only when a row maximum grows
 #pragma unroll
-            for (int n = 0; n < 8; n++)
+                for (int n = 0; n < 8; n++) acc[u][n] *= alpha;
+            }
 #pragma unroll
-                for (int e = 0; e < 4; e++) acc[n][e] *= alpha[e];
-        }
-        wave_sync();  // the previous block's reads of px are done
-#pragma unroll
-        for (int t = 0; t < 2; t++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) px[4 * kb + e][16 * t + r] = p[t][e];
-        wave_sync();
-        const float4 pa = *reinterpret_cast<const float4 *>(&px[r][8 * kb]);
-        const float4 pb = *reinterpret_cast<const float4 *>(&px[r][8 * kb + 4]);
-        const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-        u4_t ahi, alo;
-#pragma unroll
-        for (int e2 = 0; e2 < 4; e2++) {
-            const uint32_t hw = pack2<DT>(pv[2 * e2], pv[2 * e2 + 1]);
-            ahi[e2] = hw;
-            alo[e2] = pack2<DT>(pv[2 * e2] - lo16<DT>(hw), pv[2 * e2 + 1] - hi16<DT>(hw));
+            for (int d = 0; d < 4; d++) {
+                const uint32_t hw2 = pack2<DT>(x[2 * d], x[2 * d + 1]);
+                bhi[u][d] = hw2;
+                blo[u][d] = pack2<DT>(x[2 * d] - lo16<DT>(hw2), x[2 * d + 1] - hi16<DT>(hw2));
+            }
         }
 #pragma unroll
         for (int n = 0; n < 8; n++) {
-            acc[n] = mfma_dt<DT>(ahi, bv[n], acc[n]);
-            acc[n] = mfma_dt<DT>(alo, bv[n], acc[n]);
+            const u4_t va = *reinterpret_cast<const u4_t *>(L + kKTile + (16 * n + r) * kVRow + 8 * kb);
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                acc[u][n] = mfma_dt<DT>(va, bhi[u], acc[u][n]);
+                acc[u][n] = mfma_dt<DT>(va, blo[u], acc[u][n]);
+            }
         }
     }
 #pragma unroll
-    for (int e = 0; e < 4; e++) {
-        const int i = i0 + 4 * kb + e;
+    for (int u = 0; u < 2; u++) {
+        float l = l_run[u];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        const int i = i0w + 16 * u + r;
         if (i < T) {
-            const float inv = 1.0f / l_run[e];
-            float *o = out + ((size_t)hq * T + i) * D + r;
+            const float inv = 1.0f / l;
+            float *o = out + ((size_t)hq * T + i) * D + 4 * kb;
 #pragma unroll
-            for (int n = 0; n < 8; n++) o[16 * n] = acc[n][e] * inv;
-            if (r == 0) stats[(size_t)hq * T + i] = make_float2(m_run[e], inv);
+            for (int n = 0; n < 8; n++)
+                *reinterpret_cast<f4_t *>(o + 16 * n) = acc[u][n] * inv;
+            if (kb == 0) stats[(size_t)hq * T + i] = make_float2(m_run[u], inv);
         }
     }
 }
@@ -355,8 +416,9 @@ hipError_t prefill_launch(const PrefillArgs &a, hipStream_t st) {
     const float qscale = a.scale * kLog2e;
     hipLaunchKernelGGL(v_transpose_kernel, dim3(a.T32 / 32, a.Hkv), dim3(256), 0, st, a.v, a.vt,
                        a.T, a.T32);
-    hipLaunchKernelGGL((prefill_fwd_kernel<DT>), dim3((a.T + 15) / 16, a.Hq), dim3(64), 0, st, a.q,
-                       a.k, a.vt, a.out, a.stats, a.T, a.T32, g, qscale);
+    const int hw = g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
+    hipLaunchKernelGGL((prefill_fwd_kernel<DT>), dim3(a.Hq / hw, (a.T + 128 / hw - 1) / (128 / hw)),
+                       dim3(256), 0, st, a.q, a.k, a.vt, a.out, a.stats, a.T, a.T32, g, hw, qscale);
     const int nqb = (a.T + 15) / 16;
     const int cq = (nqb + kColsumChunks - 1) / kColsumChunks;
     const int nchunk = (nqb + cq - 1) / cq;
