@@ -23,12 +23,13 @@
 //          domain; P^T split into a dtype hi and lo part (~16 bits for bf16,
 //          ~22 for fp16) feeds O^T = V^T P^T directly, 2 MFMAs per
 //          16-channel tile.  Writes out (fp32) and per row (max, 1 / sum).
-// Stage 2  cumulative scores: one wave per (16 keys, chunk of query blocks,
-//          KV head) runs over every query head of the group and every 16-row
-//          query block of its chunk at or after its keys: S again,
-//          P = 2^(s - m_i) / l_i from the stage-1 row statistics, column sums
-//          in registers; a second kernel adds the chunks' partial sums in
-//          chunk order, so the scores do not depend on scheduling.
+// Stage 2  cumulative scores: four-wave workgroups over 256 keys of one KV
+//          head and a chunk of query rows, Key operands in registers, the
+//          query blocks of every query head of the group streamed through
+//          LDS: S again, P = 2^(s - m_i) / l_i from the stage-1 row
+//          statistics, column sums in registers; a second kernel adds the
+//          chunks' partial sums in chunk order, so the scores do not depend
+//          on scheduling.
 // Stage 3  selection, one workgroup per KV head: the heavy-th largest score
 //          by a bitwise search over the score bits (scores are >= 0, so the
 //          bits order like the values), ties at that score resolved to the
@@ -258,65 +259,107 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------- stage 2
-// Workgroup (key tile x, query chunk y, KV head z): query blocks
-// [y cq, y cq + cq) at or after the tile; the partial column sums go to
-// part[h][y][T] and a second kernel adds the chunks in order, so the scores
+// Workgroup (256 keys x, query chunk y, KV head z) of four waves, 64 keys
+// (four 16-key tiles) per wave, the Key operands held in registers.  The
+// workgroup streams the 32-row query blocks of its chunk at or after its
+// keys, for every query head of the group, through LDS (double buffered,
+// with the row statistics); each Q operand read serves the wave's four key
+// tiles.  S = Q K^T puts one key per lane and four query rows per result
+// register, so the column sums accumulate in registers.  The partial sums go
+// to part[h][y][T] and a second kernel adds the chunks in order: the scores
 // do not depend on scheduling.
+constexpr int kCsKeys = 256;         // keys per workgroup
+constexpr int kCsBuf = 32 * kKRow;   // elements of one staged query block
 template <int DT>
-__global__ __launch_bounds__(64) void prefill_colsum_kernel(
+__global__ __launch_bounds__(256) void prefill_colsum_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const float2 *__restrict__ stats, float *__restrict__ part, int T, int g, float qscale,
-    int cq, int nchunk) {
-    const int h = blockIdx.z, j0 = blockIdx.x * 16, chunk = blockIdx.y;
-    const int lane = threadIdx.x, r = lane & 15, kb = lane >> 4;
-    const int j = j0 + r;  // this lane's key (column)
-    u4_t bk[4];
-    {
-        const uint16_t *krow = k + ((size_t)h * T + min(j, T - 1)) * D;
-#pragma unroll
-        for (int m = 0; m < 4; m++) bk[m] = *reinterpret_cast<const u4_t *>(krow + 32 * m + 8 * kb);
+    int cr, int nchunk) {
+    __shared__ __align__(16) uint16_t lq[2 * kCsBuf];
+    __shared__ __align__(16) float2 lst[2][32];
+    const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kb = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = blockIdx.z, chunk = blockIdx.y, jg = kCsKeys * blockIdx.x, jw = jg + 64 * w;
+    float *dst = part + ((size_t)h * nchunk + chunk) * T;
+    // query rows [r0, r1): the chunk's rows from the first 32-row block holding a key's row
+    const int r0 = max(chunk * cr, jg), r1 = min(T, chunk * cr + cr);
+    if (r0 >= r1) {
+        for (int j = jg + tid; j < min(T, jg + kCsKeys); j += 256) dst[j] = 0.0f;
+        return;
     }
-    // query blocks i0 = 16 (qb0 + b), b < nblk
-    const int nqb = (T + 15) / 16;
-    const int qb0 = max(chunk * cq, blockIdx.x);
-    const int nblk = max(0, min(nqb, chunk * cq + cq) - qb0);
-    float cs = 0.0f;
-    for (int a = 0; a < g; a++) {
-        const int hq = h * g + a;
-        const uint16_t *qh = q + (size_t)hq * T * D;
-        const float2 *sth = stats + (size_t)hq * T;
-        // two query blocks per step: the loads of both go out before the math
-        for (int b = 0; b < nblk; b += 2) {
-            u4_t aq[2][4];
-            float2 st[2][4];
+    u4_t bk[4][4];  // B operand: key jw + 16 kt + r, channels 32 m + 8 kb + [0, 8)
 #pragma unroll
-            for (int u = 0; u < 2; u++) {
-                const int i0 = 16 * (qb0 + min(b + u, nblk - 1));
-                const uint16_t *qrow = qh + (size_t)min(i0 + r, T - 1) * D;
+    for (int kt = 0; kt < 4; kt++) {
+        const uint16_t *krow = k + ((size_t)h * T + min(jw + 16 * kt + r, T - 1)) * D;
 #pragma unroll
-                for (int m = 0; m < 4; m++) aq[u][m] = *reinterpret_cast<const u4_t *>(qrow + 32 * m + 8 * kb);
+        for (int m = 0; m < 4; m++) bk[kt][m] = *reinterpret_cast<const u4_t *>(krow + 32 * m + 8 * kb);
+    }
+    const int nrb = (r1 - r0 + 31) / 32, nsteps = g * nrb;
+    // step s: query head h g + s / nrb, rows r0 + 32 (s % nrb) + [0, 32)
+    u4_t pq[2];
+    float2 ps;
+    auto gload = [&](int s) {
+        const int hq = h * g + s / nrb, rb = r0 + 32 * (s % nrb);
 #pragma unroll
-                for (int e = 0; e < 4; e++) st[u][e] = sth[min(i0 + 4 * kb + e, T - 1)];
-            }
+        for (int i = 0; i < 2; i++) {
+            const int c = tid + 256 * i, row = c >> 4, c8 = c & 15;
+            pq[i] = rb + row < T ? *reinterpret_cast<const u4_t *>(q + ((size_t)hq * T + rb + row) * D + 8 * c8)
+                                 : u4_t{0, 0, 0, 0};
+        }
+        if (tid < 32) ps = rb + tid < T ? stats[(size_t)hq * T + rb + tid] : make_float2(0.0f, 0.0f);
+    };
+    auto lstore = [&](int buf) {
 #pragma unroll
-            for (int u = 0; u < 2; u++) {
-                if (b + u >= nblk) break;
-                const int i0 = 16 * (qb0 + b + u);
+        for (int i = 0; i < 2; i++) {
+            const int c = tid + 256 * i;
+            *reinterpret_cast<u4_t *>(lq + buf * kCsBuf + (c >> 4) * kKRow + 8 * (c & 15)) = pq[i];
+        }
+        if (tid < 32) lst[buf][tid] = ps;
+    };
+    float cs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    gload(0);
+    lstore(0);
+    if (nsteps > 1) gload(1);
+    for (int s = 0; s < nsteps; s++) {
+        __syncthreads();  // step s is in LDS; every wave is done with step s - 1
+        if (s + 1 < nsteps) lstore((s + 1) & 1);
+        if (s + 2 < nsteps) gload(s + 2);
+        const int rb = r0 + 32 * (s % nrb);
+        const uint16_t *L = lq + (s & 1) * kCsBuf;
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int i0 = rb + 16 * u;
+            if (i0 + 15 < jw) continue;  // rows before every key of this wave
+            u4_t aq[4];
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+                aq[m] = *reinterpret_cast<const u4_t *>(L + (16 * u + r) * kKRow + 32 * m + 8 * kb);
+            float2 st[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) st[e] = lst[s & 1][16 * u + 4 * kb + e];
+#pragma unroll
+            for (int kt = 0; kt < 4; kt++) {
                 f4_t c = {0, 0, 0, 0};
 #pragma unroll
-                for (int m = 0; m < 4; m++) c = mfma_dt<DT>(aq[u][m], bk[m], c);
+                for (int m = 0; m < 4; m++) c = mfma_dt<DT>(aq[m], bk[kt][m], c);
+                const int j = jw + 16 * kt + r;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int i = i0 + 4 * kb + e;
-                    const float pr = __builtin_amdgcn_exp2f(c[e] * qscale - st[u][e].x) * st[u][e].y;
-                    cs += i < T && j <= i ? pr : 0.0f;
+                    const float pr = __builtin_amdgcn_exp2f(c[e] * qscale - st[e].x) * st[e].y;
+                    cs[kt] += i < T && j <= i ? pr : 0.0f;
                 }
             }
         }
     }
-    cs += __shfl_xor(cs, 16, 64);
-    cs += __shfl_xor(cs, 32, 64);
-    if (kb == 0 && j < T) part[((size_t)h * nchunk + chunk) * T + j] = cs;
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) {
+        float v = cs[kt];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        const int j = jw + 16 * kt + r;
+        if (kb == 0 && j < T) dst[j] = v;
+    }
 }
 
 // score[h][j] = sum of the chunks' partial sums, chunk 0 first
@@ -419,11 +462,12 @@ hipError_t prefill_launch(const PrefillArgs &a, hipStream_t st) {
     const int hw = g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
     hipLaunchKernelGGL((prefill_fwd_kernel<DT>), dim3(a.Hq / hw, (a.T + 128 / hw - 1) / (128 / hw)),
                        dim3(256), 0, st, a.q, a.k, a.vt, a.out, a.stats, a.T, a.T32, g, hw, qscale);
-    const int nqb = (a.T + 15) / 16;
-    const int cq = (nqb + kColsumChunks - 1) / kColsumChunks;
-    const int nchunk = (nqb + cq - 1) / cq;
-    hipLaunchKernelGGL((prefill_colsum_kernel<DT>), dim3(nqb, nchunk, a.Hkv), dim3(64), 0, st,
-                       a.q, a.k, a.stats, a.part, a.T, g, qscale, cq, nchunk);
+    // query chunks of cr rows (a multiple of 32), at most kColsumChunks of them
+    const int cr = ((a.T + kColsumChunks - 1) / kColsumChunks + 31) / 32 * 32;
+    const int nchunk = (a.T + cr - 1) / cr;
+    hipLaunchKernelGGL((prefill_colsum_kernel<DT>),
+                       dim3((a.T + kCsKeys - 1) / kCsKeys, nchunk, a.Hkv), dim3(256), 0, st, a.q,
+                       a.k, a.stats, a.part, a.T, g, qscale, cr, nchunk);
     hipLaunchKernelGGL(colsum_reduce_kernel, dim3((a.T + 255) / 256, a.Hkv), dim3(256), 0, st,
                        a.part, a.score, a.T, nchunk);
     if (a.n_keep > 0) {
