@@ -31,16 +31,17 @@
 //          chunks' partial sums in chunk order, so the scores do not depend
 //          on scheduling.
 // Stage 3  selection, one workgroup per KV head: the heavy-th largest score
-//          by a bitwise search over the score bits (scores are >= 0, so the
-//          bits order like the values), ties at that score resolved to the
-//          lower positions by a prefix count, then an ascending compaction.
+//          by a radix select over the score bits, 8 bits per pass (scores
+//          are >= 0, so the bits order like the values), ties at that score
+//          resolved to the lower positions by a prefix count, then an
+//          ascending compaction.
 // Stage 4  gather of the kept K and V rows.
 #include "kvq_decode_core.h"
 
 namespace kvq {
 namespace {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 1024;
 
 // fp32 pair -> dtype pair, round to nearest even
 template <int DT>
@@ -374,28 +375,45 @@ __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float *__restr
 }
 
 // ---------------------------------------------------------------- stage 3
-// inclusive scan of v over the workgroup (thread order); *total = the sum
-__device__ __forceinline__ unsigned block_scan(unsigned v, unsigned *buf, unsigned *total) {
-    const int t = threadIdx.x;
-    buf[t] = v;
-    __syncthreads();
-    for (int off = 1; off < kSelThreads; off <<= 1) {
-        const unsigned x = t >= off ? buf[t - off] : 0u;
-        __syncthreads();
-        buf[t] += x;
-        __syncthreads();
+// inclusive scan of v over the workgroup (thread order); *total = the sum.
+// Wave scans, then a scan of the wave totals.
+__device__ __forceinline__ unsigned block_scan(unsigned v, unsigned *wtot, unsigned *total) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const unsigned x = __shfl_up(v, off, 64);
+        if (lane >= off) v += x;
     }
-    const unsigned inc = buf[t];
-    *total = buf[kSelThreads - 1];
+    if (lane == 63) wtot[w] = v;
+    __syncthreads();
+    if (w == 0) {
+        unsigned s = lane < kSelThreads / 64 ? wtot[lane] : 0u;
+#pragma unroll
+        for (int off = 1; off < kSelThreads / 64; off <<= 1) {
+            const unsigned x = __shfl_up(s, off, 64);
+            if (lane >= off) s += x;
+        }
+        if (lane < kSelThreads / 64) wtot[lane] = s;
+    }
+    __syncthreads();
+    const unsigned inc = v + (w > 0 ? wtot[w - 1] : 0u);
+    *total = wtot[kSelThreads / 64 - 1];
     __syncthreads();
     return inc;
 }
 
+// One workgroup per KV head.  The heavy-th largest score among the positions
+// before the window is found by a radix select over the fp32 bits (scores are
+// >= 0, so the bits order like the values), 8 bits per pass with a 256-bin
+// histogram in LDS; the positions at that score are then kept lowest first,
+// and the kept positions are compacted in ascending order.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__restrict__ score,
                                                              int T, int heavy, int recent,
                                                              int32_t *__restrict__ keep,
                                                              int n_keep) {
-    __shared__ unsigned buf[kSelThreads];
+    __shared__ unsigned hist[256];
+    __shared__ unsigned wtot[kSelThreads / 64];
+    __shared__ unsigned pick[2];
     const int h = blockIdx.x, t = threadIdx.x;
     const uint32_t *sb = reinterpret_cast<const uint32_t *>(score + (size_t)h * T);
     const int rec = min(recent, T), n_old = T - rec, hv = min(heavy, n_old);
@@ -403,32 +421,42 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__rest
     const int b0 = min(T, t * chunk), b1 = min(T, b0 + chunk), ob1 = min(n_old, b1);
     unsigned thr = 0xffffffffu, need = 0, tot;
     if (hv > 0) {
-        // largest bit pattern u with #(bits >= u) >= hv: the hv-th largest score
-        unsigned prefix = 0;
-        for (int bit = 31; bit >= 0; bit--) {
-            const unsigned cand = prefix | (1u << bit);
-            unsigned cnt = 0;
-            for (int x = b0; x < ob1; x++) cnt += sb[x] >= cand;
-            block_scan(cnt, buf, &tot);
-            if (tot >= (unsigned)hv) prefix = cand;
+        unsigned prefix = 0, mask = 0;
+        need = (unsigned)hv;  // rank of the wanted score among those matching the prefix
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            if (t < 256) hist[t] = 0;
+            __syncthreads();
+            for (int x = b0; x < ob1; x++) {
+                const uint32_t u = sb[x];
+                if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            // counts of the bins from the top: thread t < 256 holds bin 255 - t
+            const unsigned c = t < 256 ? hist[255 - t] : 0u;
+            const unsigned above = block_scan(c, wtot, &tot) - c;  // in higher bins
+            if (t < 256 && above < need && above + c >= need) {
+                pick[0] = 255u - t;
+                pick[1] = above;
+            }
+            __syncthreads();
+            prefix |= pick[0] << shift;
+            mask |= 255u << shift;
+            need -= pick[1];
+            __syncthreads();
         }
-        thr = prefix;
-        unsigned above = 0;
-        for (int x = b0; x < ob1; x++) above += sb[x] > thr;
-        block_scan(above, buf, &tot);
-        need = (unsigned)hv - tot;  // positions at the threshold score to keep, lowest first
+        thr = prefix;  // the hv-th largest; need = how many at that score are kept
     }
     // ties at the threshold before this thread's chunk
     unsigned ties = 0;
     for (int x = b0; x < ob1; x++) ties += sb[x] == thr;
-    const unsigned tie0 = block_scan(ties, buf, &tot) - ties;
+    const unsigned tie0 = block_scan(ties, wtot, &tot) - ties;
     // kept positions of this chunk, then their places
     unsigned kept = 0, rank = tie0;
     for (int x = b0; x < b1; x++) {
         const bool k = x >= n_old || sb[x] > thr || (sb[x] == thr && rank++ < need);
         kept += k;
     }
-    const unsigned pos0 = block_scan(kept, buf, &tot) - kept;
+    const unsigned pos0 = block_scan(kept, wtot, &tot) - kept;
     unsigned pos = pos0;
     rank = tie0;
     for (int x = b0; x < b1; x++) {
