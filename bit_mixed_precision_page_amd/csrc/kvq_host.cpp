@@ -246,7 +246,7 @@ int pool_flush_full(kvq_pool *p, hipStream_t st, int32_t *n) {
 namespace {
 constexpr int64_t kPrefillMaxT = 1 << 20;  // positions of one prefill
 
-size_t prefill_stats_bytes(int32_t T, int32_t Hq) { return align256((size_t)Hq * T * 8); }
+size_t prefill_stats_bytes(int32_t T, int32_t Hq) { return align256((size_t)Hq * T * 4); }
 size_t prefill_part_bytes(int32_t T, int32_t Hkv) {
     return align256((size_t)Hkv * kvq::kColsumChunks * T * 4);
 }
@@ -543,7 +543,7 @@ int kvq_prefill_select(int32_t dtype, int32_t T, int32_t num_q_heads, int32_t nu
     a.k = static_cast<const uint16_t *>(k);
     a.v = static_cast<const uint16_t *>(v);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    a.stats = reinterpret_cast<float2 *>(ws);
+    a.lse = reinterpret_cast<float *>(ws);
     a.part = reinterpret_cast<float *>(ws + prefill_stats_bytes(T, num_q_heads));
     a.vt = reinterpret_cast<uint16_t *>(ws + prefill_stats_bytes(T, num_q_heads) +
                                         prefill_part_bytes(T, num_kv_heads));

@@ -105,7 +105,7 @@ struct PrefillArgs {
     float scale;
     const uint16_t *q, *k, *v;  // [Hq][T][D], [Hkv][T][D], [Hkv][T][D]
     uint16_t *vt;               // workspace: [Hkv][T32 / 32][D][32] transposed Values
-    float2 *stats;              // workspace: [Hq][T] (row max in log2 units, 1 / row sum)
+    float *lse;                 // workspace: [Hq][T] log2 of each row's softmax denominator
     float *part;                // workspace: [Hkv][kColsumChunks][T] partial column sums
     float *out, *score;         // [Hq][T][D], [Hkv][T]
     int32_t *keep;              // [Hkv][n_keep]

@@ -22,12 +22,13 @@
 //          inputs are exact, fp32 accumulation); online softmax in the log2
 //          domain; P^T split into a dtype hi and lo part (~16 bits for bf16,
 //          ~22 for fp16) feeds O^T = V^T P^T directly, 2 MFMAs per
-//          16-channel tile.  Writes out (fp32) and per row (max, 1 / sum).
+//          16-channel tile.  Writes out (fp32) and per row the log2 of the
+//          softmax denominator.
 // Stage 2  cumulative scores: four-wave workgroups over 256 keys of one KV
 //          head and a chunk of query rows, Key operands in registers, the
 //          query blocks of every query head of the group streamed through
-//          LDS: S again, P = 2^(s - m_i) / l_i from the stage-1 row
-//          statistics, column sums in registers; a second kernel adds the
+//          LDS: S again, P = 2^(s qscale - lse_i) with the row's log2
+//          softmax denominator from stage 1, column sums in registers; a second kernel adds the
 //          chunks' partial sums in chunk order, so the scores do not depend
 //          on scheduling.
 // Stage 3  selection, one workgroup per KV head: the heavy-th largest score
@@ -59,6 +60,22 @@ __device__ __forceinline__ float lo16(uint32_t w) {
 template <int DT>
 __device__ __forceinline__ float hi16(uint32_t w) {
     return dec<DT>((uint16_t)(w >> 16));
+}
+
+// max / sum over the four lanes r, r + 16, r + 32, r + 48 (the four rows of
+// the wave), in all four: v_permlane32_swap of a register with itself pairs
+// rows 0, 1 with rows 2, 3; v_permlane16_swap pairs even rows with odd rows.
+__device__ __forceinline__ float xrow_max(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xrow_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Key of slot s in a 32-key block of the Value operand: slots 8 b + [0, 4)
@@ -113,10 +130,60 @@ constexpr int kVRow = 40;             // LDS Value row, 32 slots + pad (80 B)
 constexpr int kKTile = 32 * kKRow;    // elements
 constexpr int kFwdBuf = kKTile + D * kVRow;
 
+// Online softmax of one 32-key block for the wave's two row tiles.  The
+// reference maximum of a row moves only when a block's maximum exceeds it by
+// more than kRescaleSlack (log2 units), so P stays below 2^kRescaleSlack and
+// the accumulators are rescaled only in the first blocks of a row.  P^T goes
+// out as a dtype hi and lo part, the B operands of O^T = V^T P^T.
+constexpr float kRescaleSlack = 8.0f;
+template <int DT, bool MASK>
+__device__ __forceinline__ void block_softmax(const f4_t (&s)[2][2], int j0, int i0w, int T,
+                                              float qscale, float (&m_run)[2], float (&l_run)[2],
+                                              float (&alpha)[2], bool (&up)[2], u4_t (&bhi)[2],
+                                              u4_t (&blo)[2], int r, int kb) {
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        float x[8];
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                if constexpr (MASK) {
+                    const int i = min(i0w + 16 * u + r, T - 1), j = j0 + 16 * t + 4 * kb + e;
+                    x[4 * t + e] = j <= i ? s[u][t][e] : -INFINITY;
+                } else {
+                    x[4 * t + e] = s[u][t][e];
+                }
+            }
+        float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        // every visited block holds a key <= the row, so the block maximum is finite
+        bm = xrow_max(bm) * qscale;
+        const bool grow = bm > m_run[u] + kRescaleSlack;
+        const float mn = grow ? bm : m_run[u];
+        alpha[u] = __builtin_amdgcn_exp2f(m_run[u] - mn);
+        up[u] = __any(grow);  // wave-uniform
+        m_run[u] = mn;
+        float ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], qscale, -mn));
+            ps += x[e];
+        }
+        l_run[u] = fmaf(l_run[u], alpha[u], ps);
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+            const uint32_t hw2 = pack2<DT>(x[2 * d], x[2 * d + 1]);
+            bhi[u][d] = hw2;
+            blo[u][d] = pack2<DT>(x[2 * d] - lo16<DT>(hw2), x[2 * d + 1] - hi16<DT>(hw2));
+        }
+    }
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ vt, float *__restrict__ out, float2 *__restrict__ stats, int T,
+    const uint16_t *__restrict__ vt, float *__restrict__ out, float *__restrict__ lse, int T,
     int T32, int g, int hw, float qscale) {
     __shared__ __align__(16) uint16_t lds[2 * kFwdBuf];
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kb = lane >> 4;
@@ -162,7 +229,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int m = 0; m < 4; m++) aq[u][m] = *reinterpret_cast<const u4_t *>(qrow + 32 * m + 8 * kb);
     }
-    float m_run[2], l_run[2];  // row max (log2 units); this lane's part of the row sum
+    float m_run[2], l_run[2];  // reference row max (log2 units); this lane's part of the row sum
     f4_t acc[2][8];            // O^T: row i0w + 16 u + r, channels 16 n + 4 kb + e
 #pragma unroll
     for (int u = 0; u < 2; u++) {
@@ -195,43 +262,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
         u4_t bhi[2], blo[2];
+        // the mask matters only where keys pass the wave's first row (the
+        // diagonal block, which also holds any keys past T)
+        float alpha[2];
+        bool up[2];
+        if (j0 + 31 > i0w)
+            block_softmax<DT, true>(s, j0, i0w, T, qscale, m_run, l_run, alpha, up, bhi, blo, r, kb);
+        else
+            block_softmax<DT, false>(s, j0, i0w, T, qscale, m_run, l_run, alpha, up, bhi, blo, r, kb);
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-            const int i = min(i0w + 16 * u + r, T - 1);
-            float x[8], bm = -INFINITY;
+        for (int u = 0; u < 2; u++)
+            if (up[u]) {
 #pragma unroll
-            for (int t = 0; t < 2; t++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int j = j0 + 16 * t + 4 * kb + e;
-                    x[4 * t + e] = j <= i ? s[u][t][e] * qscale : -INFINITY;
-                    bm = fmaxf(bm, x[4 * t + e]);
-                }
-            bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-            // every visited block holds a key <= i, so bm is finite
-            const float mn = fmaxf(m_run[u], bm);
-            const bool grew = mn > m_run[u];
-            const float alpha = __builtin_amdgcn_exp2f(m_run[u] - mn);
-            m_run[u] = mn;
-            float ps = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                x[e] = __builtin_amdgcn_exp2f(x[e] - mn);
-                ps += x[e];
+                for (int n = 0; n < 8; n++) acc[u][n] *= alpha[u];
             }
-            l_run[u] = fmaf(l_run[u], alpha, ps);
-            if (__any(grew)) {  // wave-uniform: rescale only when a row maximum grows
-#pragma unroll
-                for (int n = 0; n < 8; n++) acc[u][n] *= alpha;
-            }
-#pragma unroll
-            for (int d = 0; d < 4; d++) {
-                const uint32_t hw2 = pack2<DT>(x[2 * d], x[2 * d + 1]);
-                bhi[u][d] = hw2;
-                blo[u][d] = pack2<DT>(x[2 * d] - lo16<DT>(hw2), x[2 * d + 1] - hi16<DT>(hw2));
-            }
-        }
 #pragma unroll
         for (int n = 0; n < 8; n++) {
             const u4_t va = *reinterpret_cast<const u4_t *>(L + kKTile + (16 * n + r) * kVRow + 8 * kb);
@@ -244,9 +288,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 #pragma unroll
     for (int u = 0; u < 2; u++) {
-        float l = l_run[u];
-        l += __shfl_xor(l, 16, 64);
-        l += __shfl_xor(l, 32, 64);
+        const float l = xrow_sum(l_run[u]);
         const int i = i0w + 16 * u + r;
         if (i < T) {
             const float inv = 1.0f / l;
@@ -254,7 +296,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int n = 0; n < 8; n++)
                 *reinterpret_cast<f4_t *>(o + 16 * n) = acc[u][n] * inv;
-            if (kb == 0) stats[(size_t)hq * T + i] = make_float2(m_run[u], inv);
+            // log2 of the row's softmax denominator: P[i][j] = 2^(s_ij qscale - lse)
+            if (kb == 0) lse[(size_t)hq * T + i] = m_run[u] + __builtin_amdgcn_logf(l);
         }
     }
 }
@@ -271,13 +314,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // do not depend on scheduling.
 constexpr int kCsKeys = 256;         // keys per workgroup
 constexpr int kCsBuf = 32 * kKRow;   // elements of one staged query block
+
+// column sums of one 16-row tile against the wave's four key tiles
+template <int DT, bool MASK>
+__device__ __forceinline__ void tile_colsum(const u4_t (&aq)[4], const u4_t (&bk)[4][4],
+                                            const float (&st)[4], float (&cs)[4], int i0, int jw,
+                                            int T, float qscale, int r, int kb) {
+#pragma unroll
+    for (int kt = 0; kt < 4; kt++) {
+        f4_t c = {0, 0, 0, 0};
+#pragma unroll
+        for (int m = 0; m < 4; m++) c = mfma_dt<DT>(aq[m], bk[kt][m], c);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const float pr = __builtin_amdgcn_exp2f(fmaf(c[e], qscale, -st[e]));
+            if constexpr (MASK) {
+                const int i = i0 + 4 * kb + e, j = jw + 16 * kt + r;
+                cs[kt] += i < T && j <= i ? pr : 0.0f;
+            } else {
+                cs[kt] += pr;
+            }
+        }
+    }
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void prefill_colsum_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const float2 *__restrict__ stats, float *__restrict__ part, int T, int g, float qscale,
-    int cr, int nchunk) {
+    const float *__restrict__ lse, float *__restrict__ part, int T, int g, float qscale, int cr,
+    int nchunk) {
     __shared__ __align__(16) uint16_t lq[2 * kCsBuf];
-    __shared__ __align__(16) float2 lst[2][32];
+    __shared__ float lst[2][32];
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kb = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = blockIdx.z, chunk = blockIdx.y, jg = kCsKeys * blockIdx.x, jw = jg + 64 * w;
@@ -295,19 +362,25 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
 #pragma unroll
         for (int m = 0; m < 4; m++) bk[kt][m] = *reinterpret_cast<const u4_t *>(krow + 32 * m + 8 * kb);
     }
-    const int nrb = (r1 - r0 + 31) / 32, nsteps = g * nrb;
-    // step s: query head h g + s / nrb, rows r0 + 32 (s % nrb) + [0, 32)
+    const int nsteps = g * ((r1 - r0 + 31) / 32);
+    // steps run over (query head h g + a, rows rb + [0, 32)), rb from r0 to r1 in 32s
+    int la = 0, lrb = r0;  // the next step to load
     u4_t pq[2];
-    float2 ps;
-    auto gload = [&](int s) {
-        const int hq = h * g + s / nrb, rb = r0 + 32 * (s % nrb);
+    float ps;
+    auto gload = [&]() {
+        const int hq = h * g + la;
 #pragma unroll
         for (int i = 0; i < 2; i++) {
             const int c = tid + 256 * i, row = c >> 4, c8 = c & 15;
-            pq[i] = rb + row < T ? *reinterpret_cast<const u4_t *>(q + ((size_t)hq * T + rb + row) * D + 8 * c8)
-                                 : u4_t{0, 0, 0, 0};
+            pq[i] = lrb + row < T ? *reinterpret_cast<const u4_t *>(q + ((size_t)hq * T + lrb + row) * D + 8 * c8)
+                                  : u4_t{0, 0, 0, 0};
         }
-        if (tid < 32) ps = rb + tid < T ? stats[(size_t)hq * T + rb + tid] : make_float2(0.0f, 0.0f);
+        if (tid < 32) ps = lrb + tid < T ? lse[(size_t)hq * T + lrb + tid] : 0.0f;
+        lrb += 32;
+        if (lrb >= r1) {
+            lrb = r0;
+            la++;
+        }
     };
     auto lstore = [&](int buf) {
 #pragma unroll
@@ -318,14 +391,14 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
         if (tid < 32) lst[buf][tid] = ps;
     };
     float cs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    gload(0);
+    gload();
     lstore(0);
-    if (nsteps > 1) gload(1);
+    if (nsteps > 1) gload();
+    int rb = r0;  // rows of the step computed
     for (int s = 0; s < nsteps; s++) {
         __syncthreads();  // step s is in LDS; every wave is done with step s - 1
         if (s + 1 < nsteps) lstore((s + 1) & 1);
-        if (s + 2 < nsteps) gload(s + 2);
-        const int rb = r0 + 32 * (s % nrb);
+        if (s + 2 < nsteps) gload();
         const uint16_t *L = lq + (s & 1) * kCsBuf;
 #pragma unroll
         for (int u = 0; u < 2; u++) {
@@ -335,29 +408,21 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
 #pragma unroll
             for (int m = 0; m < 4; m++)
                 aq[m] = *reinterpret_cast<const u4_t *>(L + (16 * u + r) * kKRow + 32 * m + 8 * kb);
-            float2 st[4];
+            float st[4];
 #pragma unroll
             for (int e = 0; e < 4; e++) st[e] = lst[s & 1][16 * u + 4 * kb + e];
-#pragma unroll
-            for (int kt = 0; kt < 4; kt++) {
-                f4_t c = {0, 0, 0, 0};
-#pragma unroll
-                for (int m = 0; m < 4; m++) c = mfma_dt<DT>(aq[m], bk[kt][m], c);
-                const int j = jw + 16 * kt + r;
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int i = i0 + 4 * kb + e;
-                    const float pr = __builtin_amdgcn_exp2f(c[e] * qscale - st[e].x) * st[e].y;
-                    cs[kt] += i < T && j <= i ? pr : 0.0f;
-                }
-            }
+            // the mask matters only where a key passes a row or rows pass T
+            if (i0 < jw + 63 || i0 + 15 >= T)
+                tile_colsum<DT, true>(aq, bk, st, cs, i0, jw, T, qscale, r, kb);
+            else
+                tile_colsum<DT, false>(aq, bk, st, cs, i0, jw, T, qscale, r, kb);
         }
+        rb += 32;
+        if (rb >= r1) rb = r0;
     }
 #pragma unroll
     for (int kt = 0; kt < 4; kt++) {
-        float v = cs[kt];
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
+        const float v = xrow_sum(cs[kt]);
         const int j = jw + 16 * kt + r;
         if (kb == 0 && j < T) dst[j] = v;
     }
@@ -489,13 +554,13 @@ hipError_t prefill_launch(const PrefillArgs &a, hipStream_t st) {
                        a.T, a.T32);
     const int hw = g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
     hipLaunchKernelGGL((prefill_fwd_kernel<DT>), dim3(a.Hq / hw, (a.T + 128 / hw - 1) / (128 / hw)),
-                       dim3(256), 0, st, a.q, a.k, a.vt, a.out, a.stats, a.T, a.T32, g, hw, qscale);
+                       dim3(256), 0, st, a.q, a.k, a.vt, a.out, a.lse, a.T, a.T32, g, hw, qscale);
     // query chunks of cr rows (a multiple of 32), at most kColsumChunks of them
     const int cr = ((a.T + kColsumChunks - 1) / kColsumChunks + 31) / 32 * 32;
     const int nchunk = (a.T + cr - 1) / cr;
     hipLaunchKernelGGL((prefill_colsum_kernel<DT>),
                        dim3((a.T + kCsKeys - 1) / kCsKeys, nchunk, a.Hkv), dim3(256), 0, st, a.q,
-                       a.k, a.stats, a.part, a.T, g, qscale, cr, nchunk);
+                       a.k, a.lse, a.part, a.T, g, qscale, cr, nchunk);
     hipLaunchKernelGGL(colsum_reduce_kernel, dim3((a.T + 255) / 256, a.Hkv), dim3(256), 0, st,
                        a.part, a.score, a.T, nchunk);
     if (a.n_keep > 0) {
