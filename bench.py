@@ -400,6 +400,13 @@ def prefill_flops(T, Hq):
     return 3.0 * T * T * Hq * 128
 
 
+def prefill_fwd_flops(T, Hq):
+    """Algorithmic flops of the causal attention kernel: Q K^T and P V over
+    the T (T + 1) / 2 causal pairs of every query head, 2 flops per
+    multiply-add, 128 channels."""
+    return 2 * 2 * (T * (T + 1) // 2) * Hq * 128
+
+
 def prefill_main(a, w, torch, gen, kvq):
     """Prefill of one sequence with cumulative attention scores and
     heavy-hitter + recent selection (kvq_prefill_select: attention output,
@@ -435,28 +442,42 @@ def prefill_main(a, w, torch, gen, kvq):
     warm = max(1, min(a.warmup, 5))
     for _ in range(warm):
         call()
+    # HIP events around the attention kernel on every 4th timed call
+    timed = [i for i in range(steps) if a.event_every > 0 and i % a.event_every == 0]
+    hev = HipEvents(len(timed), a.event_fence)
+    ev_of = {i: hev.pair(j) for j, i in enumerate(timed)}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(steps):
+    for i in range(steps):
+        ev = ev_of.get(i)
+        if ev is not None:
+            kvq.kvq_prefill_set_kernel_events(ev[0], ev[1])
         call()
+        if ev is not None:
+            kvq.kvq_prefill_set_kernel_events(None, None)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     fl = prefill_flops(T, w.Hq)
     tf = fl / (ms / 1e3) / 1e12
-    print(f"[bench] {steps} calls, {ms * 1e3:.1f} us per call, {tf:.1f} TFLOP/s algorithmic",
+    kus = [hev.elapsed_ms(j) * 1e3 for j in range(len(timed))]
+    k_us = sum(kus) / len(kus) if kus else None
+    k_tf = prefill_fwd_flops(T, w.Hq) / (k_us / 1e6) / 1e12 if kus else None
+    print(f"[bench] {steps} calls, {ms * 1e3:.1f} us per call, {tf:.1f} TFLOP/s algorithmic; "
+          f"attention kernel {k_us:.1f} us, {k_tf:.1f} TFLOP/s" if kus else
+          f"[bench] {steps} calls, {ms * 1e3:.1f} us per call, {tf:.1f} TFLOP/s algorithmic",
           file=sys.stderr, flush=True)
     cpu = None
     if not a.no_cpu_baseline:
         import oracle
         ora = oracle.lib()
-        T0 = 1024  # the oracle on the first T0 positions (~10 s of host work)
+        T0 = min(T, 8192)  # the oracle on the first T0 positions (~10-15 s of host work)
         tc = time.time()
         ora.prefill_attention(w.dtype, q[:, :T0], K[0][:, :T0], V[0][:, :T0], 1.0 / np.sqrt(128))
         dt = time.time() - tc
         cpu = {"value": round(prefill_flops(T0, w.Hq) / dt / 1e12, 6), "unit": "TFLOP/s",
-               "cores": ora.num_threads(), "kind": "oracle",
+               "cores": min(ora.num_threads(), w.Hkv), "kind": "oracle",
                "sample": f"fp64 prefill attention + cumulative scores of the first {T0} positions "
                          f"({w.Hq} query heads) in {dt:.1f} s"}
     rec_ = {
@@ -468,8 +489,10 @@ def prefill_main(a, w, torch, gen, kvq):
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": 128, "heavy": heavy, "recent": recent, "kept": nk},
-        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": 2500.0,
-                     "unit": "TFLOP/s", "frac": round(tf / 2500.0, 4), "traffic": None},
+        "roofline": {"bound": "mfma", "kernel": "prefill_fwd_kernel",
+                     "achieved": round(k_tf, 2) if k_tf else None, "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(k_tf / 2500.0, 4) if k_tf else None,
+                     "kernel_us": round(k_us, 2) if k_us else None, "traffic": None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec_), flush=True)

@@ -245,6 +245,7 @@ int pool_flush_full(kvq_pool *p, hipStream_t st, int32_t *n) {
 // ------------------------------------------------------------- prefill ----
 namespace {
 constexpr int64_t kPrefillMaxT = 1 << 20;  // positions of one prefill
+hipEvent_t g_prefill_ev_before = nullptr, g_prefill_ev_after = nullptr;
 
 size_t prefill_stats_bytes(int32_t T, int32_t Hq) { return align256((size_t)Hq * T * 4); }
 size_t prefill_part_bytes(int32_t T, int32_t Hkv) {
@@ -552,8 +553,17 @@ int kvq_prefill_select(int32_t dtype, int32_t T, int32_t num_q_heads, int32_t nu
     a.keep = keep;
     a.k_sel = static_cast<uint16_t *>(k_sel);
     a.v_sel = static_cast<uint16_t *>(v_sel);
+    a.ev_before = g_prefill_ev_before;
+    a.ev_after = g_prefill_ev_after;
     *n_keep = nk;
     return hip_status(kvq::launch_prefill(dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+int kvq_prefill_set_kernel_events(void *before, void *after) {
+    if ((before == nullptr) != (after == nullptr)) return KVQ_EINVAL;
+    g_prefill_ev_before = static_cast<hipEvent_t>(before);
+    g_prefill_ev_after = static_cast<hipEvent_t>(after);
+    return KVQ_OK;
 }
 
 int kvq_query_relevance(int32_t dtype, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

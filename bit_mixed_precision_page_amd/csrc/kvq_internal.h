@@ -110,6 +110,7 @@ struct PrefillArgs {
     float *out, *score;         // [Hq][T][D], [Hkv][T]
     int32_t *keep;              // [Hkv][n_keep]
     uint16_t *k_sel, *v_sel;    // [Hkv][n_keep][D], or null
+    hipEvent_t ev_before, ev_after;  // optional, around the attention kernel
 };
 hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream);
 // Waves per workgroup of the dense decode kernel: each wave streams its own

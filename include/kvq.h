@@ -356,6 +356,13 @@ int kvq_prefill_select(int32_t dtype, int32_t T, int32_t num_q_heads, int32_t nu
                        void *k_sel, void *v_sel, void *workspace, size_t ws_bytes, void *stream,
                        int32_t *n_keep);
 
+/* Optional timing hooks of kvq_prefill_select: when set (non-NULL hipEvent_t
+   values), every later call records `before` on its stream just before the
+   attention kernel and `after` just after it.  NULL, NULL clears them.  The
+   setting is process-wide: not for calls made concurrently from several
+   threads. */
+int kvq_prefill_set_kernel_events(void *before, void *after);
+
 #ifdef __cplusplus
 }
 #endif
