@@ -264,3 +264,38 @@ def test_pool_call_errors_leave_state(kvq):
             kvq.kvq_pool_set_kernel_events(h, FAKE, None)
     finally:
         kvq.kvq_pool_destroy(h)
+
+
+def test_prefill_argument_checks():
+    """kvq_prefill_select rejects bad shapes, budgets, pointers, alignment and
+    short workspaces before launching anything; the workspace grows with T."""
+    from bit_mixed_precision_page_amd import kvq
+
+    def code(f):
+        with pytest.raises(kvq.KvqError) as e:
+            f()
+        return e.value.name
+
+    ws = kvq.kvq_prefill_workspace_bytes(300, 8, 2)
+    assert ws >= 8 * 300 * 4 + 2 * 128 * 320 * 2
+    assert kvq.kvq_prefill_workspace_bytes(301, 8, 2) >= ws
+    for T, hq, hkv in [(0, 8, 2), ((1 << 20) + 1, 8, 2), (300, 6, 4), (300, 34, 2), (300, 2, 4)]:
+        assert code(lambda: kvq.kvq_prefill_workspace_bytes(T, hq, hkv)) == "KVQ_EINVAL"
+
+    def call(dtype=1, T=300, heavy=10, recent=10, q=FAKE, keep=FAKE, k_sel=FAKE, v_sel=FAKE,
+             wsb=ws):
+        return kvq.kvq_prefill_select(dtype, T, 8, 2, 0.0, q, FAKE, FAKE, heavy, recent, FAKE,
+                                      FAKE, keep, k_sel, v_sel, FAKE, wsb, stream=0)
+    assert code(lambda: call(dtype=7)) == "KVQ_EINVAL"
+    assert code(lambda: call(T=0)) == "KVQ_EINVAL"
+    assert code(lambda: call(heavy=-1)) == "KVQ_EINVAL"
+    assert code(lambda: call(recent=-1)) == "KVQ_EINVAL"
+    assert code(lambda: call(q=None)) == "KVQ_EINVAL"
+    assert code(lambda: call(keep=None)) == "KVQ_EINVAL"
+    assert code(lambda: call(k_sel=None)) == "KVQ_EINVAL"
+    assert code(lambda: call(q=FAKE + 8)) == "KVQ_EALIGN"
+    assert code(lambda: call(keep=FAKE + 4)) == "KVQ_EALIGN"
+    assert code(lambda: call(wsb=ws - 1)) == "KVQ_EWORKSPACE"
+    # timing hooks: both or neither
+    assert code(lambda: kvq.kvq_prefill_set_kernel_events(FAKE, None)) == "KVQ_EINVAL"
+    kvq.kvq_prefill_set_kernel_events(None, None)
