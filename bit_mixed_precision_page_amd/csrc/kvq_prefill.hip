@@ -181,7 +181,7 @@ __device__ __forceinline__ void block_softmax(const f4_t (&s)[2][2], int j0, int
 }
 
 template <int DT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_fwd_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void prefill_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ vt, float *__restrict__ out, float *__restrict__ lse, int T,
     int T32, int g, int hw, float qscale) {

@@ -86,7 +86,8 @@ def test_prefill_bf16_gqa4(T):
 
 def test_prefill_fp16_group_sizes():
     base = W["tiny"]
-    for Hq, Hkv, T in [(8, 1, 129), (2, 2, 70), (16, 1, 40)]:
+    # group sizes 8, 1, 16 (four heads per workgroup, or one), 3 (one), 6 (two)
+    for Hq, Hkv, T in [(8, 1, 129), (2, 2, 70), (16, 1, 40), (6, 2, 200), (12, 2, 97)]:
         w = dataclasses.replace(base, Hq=Hq, Hkv=Hkv)
         _check(w, T, heavy=17, recent=9)
 
