@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 }
 
 // ---------------------------------------------------------------- stage 2
-// Workgroup (256 keys x, query chunk y, KV head z) of four waves, 64 keys
+// Workgroup (256 keys, query chunk, KV head) of four waves, 64 keys
 // (four 16-key tiles) per wave, the Key operands held in registers.  The
 // workgroup streams the 32-row query blocks of its chunk at or after its
 // keys, for every query head of the group, through LDS (double buffered,
@@ -338,6 +338,12 @@ __device__ __forceinline__ void tile_colsum(const u4_t (&aq)[4], const u4_t (&bk
     }
 }
 
+// key blocks of kCsKeys with a query row of chunk y at or after their first key
+__host__ __device__ __forceinline__ int cs_blocks(int y, int cr, int T) {
+    const int nkb = (T + kCsKeys - 1) / kCsKeys;
+    return min(nkb, (min(T, (y + 1) * cr) + kCsKeys - 1) / kCsKeys);
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void prefill_colsum_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -347,14 +353,15 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
     __shared__ float lst[2][32];
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kb = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = blockIdx.z, chunk = blockIdx.y, jg = kCsKeys * blockIdx.x, jw = jg + 64 * w;
+    // only the (key block, chunk) pairs with a row at or after a key are
+    // launched: chunk y holds cs_blocks(y) key blocks; the last chunks first
+    const int h = blockIdx.y;
+    int chunk = nchunk - 1, kx = blockIdx.x;
+    while (kx >= cs_blocks(chunk, cr, T)) kx -= cs_blocks(chunk--, cr, T);
+    const int jg = kCsKeys * kx, jw = jg + 64 * w;
     float *dst = part + ((size_t)h * nchunk + chunk) * T;
     // query rows [r0, r1): the chunk's rows from the first 32-row block holding a key's row
     const int r0 = max(chunk * cr, jg), r1 = min(T, chunk * cr + cr);
-    if (r0 >= r1) {
-        for (int j = jg + tid; j < min(T, jg + kCsKeys); j += 256) dst[j] = 0.0f;
-        return;
-    }
     u4_t bk[4][4];  // B operand: key jw + 16 kt + r, channels 32 m + 8 kb + [0, 8)
 #pragma unroll
     for (int kt = 0; kt < 4; kt++) {
@@ -431,11 +438,13 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
 // score[h][j] = sum of the chunks' partial sums, chunk 0 first
 __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float *__restrict__ part,
                                                             float *__restrict__ score, int T,
-                                                            int nchunk) {
+                                                            int cr, int nchunk) {
     const int h = blockIdx.y, j = blockIdx.x * 256 + threadIdx.x;
     if (j >= T) return;
+    // chunks before c0 hold no row at or after the key block of j
+    const int c0 = kCsKeys * (j / kCsKeys) / cr;
     float s = 0.0f;
-    for (int c = 0; c < nchunk; c++) s += part[((size_t)h * nchunk + c) * T + j];
+    for (int c = c0; c < nchunk; c++) s += part[((size_t)h * nchunk + c) * T + j];
     score[(size_t)h * T + j] = s;
 }
 
@@ -560,11 +569,12 @@ hipError_t prefill_launch(const PrefillArgs &a, hipStream_t st) {
     // query chunks of cr rows (a multiple of 32), at most kColsumChunks of them
     const int cr = ((a.T + kColsumChunks - 1) / kColsumChunks + 31) / 32 * 32;
     const int nchunk = (a.T + cr - 1) / cr;
-    hipLaunchKernelGGL((prefill_colsum_kernel<DT>),
-                       dim3((a.T + kCsKeys - 1) / kCsKeys, nchunk, a.Hkv), dim3(256), 0, st, a.q,
-                       a.k, a.lse, a.part, a.T, g, qscale, cr, nchunk);
+    int n_cs = 0;
+    for (int y = 0; y < nchunk; y++) n_cs += cs_blocks(y, cr, a.T);
+    hipLaunchKernelGGL((prefill_colsum_kernel<DT>), dim3(n_cs, a.Hkv), dim3(256), 0, st, a.q, a.k,
+                       a.lse, a.part, a.T, g, qscale, cr, nchunk);
     hipLaunchKernelGGL(colsum_reduce_kernel, dim3((a.T + 255) / 256, a.Hkv), dim3(256), 0, st,
-                       a.part, a.score, a.T, nchunk);
+                       a.part, a.score, a.T, cr, nchunk);
     if (a.n_keep > 0) {
         hipLaunchKernelGGL(select_kernel, dim3(a.Hkv), dim3(kSelThreads), 0, st, a.score, a.T,
                            a.heavy, a.recent, a.keep, a.n_keep);
