@@ -303,25 +303,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 }
 
 // ---------------------------------------------------------------- stage 2
-// Workgroup (256 keys, query chunk, KV head) of four waves, 64 keys
-// (four 16-key tiles) per wave, the Key operands held in registers.  The
+// Workgroup (kCsKeys keys, query chunk, KV head) of four waves, kCsKT 16-key
+// tiles per wave, the Key operands held in registers.  The
 // workgroup streams the 32-row query blocks of its chunk at or after its
 // keys, for every query head of the group, through LDS (double buffered,
-// with the row statistics); each Q operand read serves the wave's four key
+// with the row statistics); each Q operand read serves the wave's kCsKT key
 // tiles.  S = Q K^T puts one key per lane and four query rows per result
 // register, so the column sums accumulate in registers.  The partial sums go
 // to part[h][y][T] and a second kernel adds the chunks in order: the scores
 // do not depend on scheduling.
-constexpr int kCsKeys = 256;         // keys per workgroup
-constexpr int kCsBuf = 32 * kKRow;   // elements of one staged query block
+constexpr int kCsKT = 4;                   // 16-key tiles per wave
+constexpr int kCsKeys = 4 * 16 * kCsKT;    // keys per workgroup
+constexpr int kCsRows = 64;                // query rows per step
+constexpr int kCsBuf = kCsRows * kKRow;    // elements of one staged query block
 
-// column sums of one 16-row tile against the wave's four key tiles
+// column sums of one 16-row tile against the wave's kCsKT key tiles
 template <int DT, bool MASK>
-__device__ __forceinline__ void tile_colsum(const u4_t (&aq)[4], const u4_t (&bk)[4][4],
-                                            const float (&st)[4], float (&cs)[4], int i0, int jw,
-                                            int T, float qscale, int r, int kb) {
+__device__ __forceinline__ void tile_colsum(const u4_t (&aq)[4], const u4_t (&bk)[kCsKT][4],
+                                            const float (&st)[4], float (&cs)[kCsKT], int i0,
+                                            int jw, int T, float qscale, int r, int kb) {
 #pragma unroll
-    for (int kt = 0; kt < 4; kt++) {
+    for (int kt = 0; kt < kCsKT; kt++) {
         f4_t c = {0, 0, 0, 0};
 #pragma unroll
         for (int m = 0; m < 4; m++) c = mfma_dt<DT>(aq[m], bk[kt][m], c);
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
     const float *__restrict__ lse, float *__restrict__ part, int T, int g, float qscale, int cr,
     int nchunk) {
     __shared__ __align__(16) uint16_t lq[2 * kCsBuf];
-    __shared__ float lst[2][32];
+    __shared__ float lst[2][kCsRows];
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kb = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     // only the (key block, chunk) pairs with a row at or after a key are
@@ -358,32 +360,33 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
     const int h = blockIdx.y;
     int chunk = nchunk - 1, kx = blockIdx.x;
     while (kx >= cs_blocks(chunk, cr, T)) kx -= cs_blocks(chunk--, cr, T);
-    const int jg = kCsKeys * kx, jw = jg + 64 * w;
+    const int jg = kCsKeys * kx, jw = jg + 16 * kCsKT * w;
     float *dst = part + ((size_t)h * nchunk + chunk) * T;
-    // query rows [r0, r1): the chunk's rows from the first 32-row block holding a key's row
+    // query rows [r0, r1): the chunk's rows from the first key (cr and the key
+    // blocks are multiples of kCsRows, so steps never cross into another chunk)
     const int r0 = max(chunk * cr, jg), r1 = min(T, chunk * cr + cr);
-    u4_t bk[4][4];  // B operand: key jw + 16 kt + r, channels 32 m + 8 kb + [0, 8)
+    u4_t bk[kCsKT][4];  // B operand: key jw + 16 kt + r, channels 32 m + 8 kb + [0, 8)
 #pragma unroll
-    for (int kt = 0; kt < 4; kt++) {
+    for (int kt = 0; kt < kCsKT; kt++) {
         const uint16_t *krow = k + ((size_t)h * T + min(jw + 16 * kt + r, T - 1)) * D;
 #pragma unroll
         for (int m = 0; m < 4; m++) bk[kt][m] = *reinterpret_cast<const u4_t *>(krow + 32 * m + 8 * kb);
     }
-    const int nsteps = g * ((r1 - r0 + 31) / 32);
-    // steps run over (query head h g + a, rows rb + [0, 32)), rb from r0 to r1 in 32s
+    const int nsteps = g * ((r1 - r0 + kCsRows - 1) / kCsRows);
+    // steps run over (query head h g + a, rows rb + [0, kCsRows)), rb from r0 to r1
     int la = 0, lrb = r0;  // the next step to load
-    u4_t pq[2];
+    u4_t pq[kCsRows / 16];
     float ps;
     auto gload = [&]() {
         const int hq = h * g + la;
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
+        for (int i = 0; i < kCsRows / 16; i++) {
             const int c = tid + 256 * i, row = c >> 4, c8 = c & 15;
             pq[i] = lrb + row < T ? *reinterpret_cast<const u4_t *>(q + ((size_t)hq * T + lrb + row) * D + 8 * c8)
                                   : u4_t{0, 0, 0, 0};
         }
-        if (tid < 32) ps = lrb + tid < T ? lse[(size_t)hq * T + lrb + tid] : 0.0f;
-        lrb += 32;
+        if (tid < kCsRows) ps = lrb + tid < T ? lse[(size_t)hq * T + lrb + tid] : 0.0f;
+        lrb += kCsRows;
         if (lrb >= r1) {
             lrb = r0;
             la++;
@@ -391,13 +394,13 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
     };
     auto lstore = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
+        for (int i = 0; i < kCsRows / 16; i++) {
             const int c = tid + 256 * i;
             *reinterpret_cast<u4_t *>(lq + buf * kCsBuf + (c >> 4) * kKRow + 8 * (c & 15)) = pq[i];
         }
-        if (tid < 32) lst[buf][tid] = ps;
+        if (tid < kCsRows) lst[buf][tid] = ps;
     };
-    float cs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float cs[kCsKT] = {};
     gload();
     lstore(0);
     if (nsteps > 1) gload();
@@ -408,7 +411,7 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
         if (s + 2 < nsteps) gload();
         const uint16_t *L = lq + (s & 1) * kCsBuf;
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
+        for (int u = 0; u < kCsRows / 16; u++) {
             const int i0 = rb + 16 * u;
             if (i0 + 15 < jw) continue;  // rows before every key of this wave
             u4_t aq[4];
@@ -419,16 +422,16 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
 #pragma unroll
             for (int e = 0; e < 4; e++) st[e] = lst[s & 1][16 * u + 4 * kb + e];
             // the mask matters only where a key passes a row or rows pass T
-            if (i0 < jw + 63 || i0 + 15 >= T)
+            if (i0 < jw + 16 * kCsKT - 1 || i0 + 15 >= T)
                 tile_colsum<DT, true>(aq, bk, st, cs, i0, jw, T, qscale, r, kb);
             else
                 tile_colsum<DT, false>(aq, bk, st, cs, i0, jw, T, qscale, r, kb);
         }
-        rb += 32;
+        rb += kCsRows;
         if (rb >= r1) rb = r0;
     }
 #pragma unroll
-    for (int kt = 0; kt < 4; kt++) {
+    for (int kt = 0; kt < kCsKT; kt++) {
         const float v = xrow_sum(cs[kt]);
         const int j = jw + 16 * kt + r;
         if (kb == 0 && j < T) dst[j] = v;
@@ -566,8 +569,8 @@ hipError_t prefill_launch(const PrefillArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((prefill_fwd_kernel<DT>), dim3(a.Hq / hw, (a.T + 128 / hw - 1) / (128 / hw)),
                        dim3(256), 0, st, a.q, a.k, a.vt, a.out, a.lse, a.T, a.T32, g, hw, qscale);
     if (a.ev_after) (void)hipEventRecord(a.ev_after, st);
-    // query chunks of cr rows (a multiple of 32), at most kColsumChunks of them
-    const int cr = ((a.T + kColsumChunks - 1) / kColsumChunks + 31) / 32 * 32;
+    // query chunks of cr rows (a multiple of kCsRows), at most kColsumChunks of them
+    const int cr = ((a.T + kColsumChunks - 1) / kColsumChunks + kCsRows - 1) / kCsRows * kCsRows;
     const int nchunk = (a.T + cr - 1) / cr;
     int n_cs = 0;
     for (int y = 0; y < nchunk; y++) n_cs += cs_blocks(y, cr, a.T);
