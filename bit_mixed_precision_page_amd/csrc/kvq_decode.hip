@@ -157,27 +157,28 @@ int slots3() {
 template <int DT, int G, int KH>
 hipError_t launch3(const Geometry &Gm, uint8_t *cache, const uint16_t *kn, const uint16_t *vn,
                    int slot, const uint16_t *q, float *ml, float *acc, const DecodePlan &pl,
-                   hipStream_t st) {
+                   hipEvent_t e0, hipEvent_t e1, hipStream_t st) {
     dim3 grid(pl.total_splits * Gm.Hkv * Gm.B);
-    hipLaunchKernelGGL((decode_split_kernel<DT, G, KH>), grid, dim3(64 * kDecodeWaves), 0, st, cache, cache,
-                       kn, vn, slot, q, ml,
-                       acc, Gm.Hkv, Gm.max_pages, Gm.page_bytes, Gm.k, Gm.res_base,
-                       pl.n_pages, pl.n_res, pl.page_splits, pl.groups_per_split,
-                       pl.total_splits - pl.page_splits,
-                       pl.max_splits, Gm.scale * kLog2e, pl.dstate);
+    // with timing events: the dispatch's own start and end timestamps
+    hipExtLaunchKernelGGL((decode_split_kernel<DT, G, KH>), grid, dim3(64 * kDecodeWaves), 0, st,
+                          e0, e1, 0, (const uint8_t *)cache, cache, kn, vn, slot, q, ml, acc,
+                          Gm.Hkv, Gm.max_pages, Gm.page_bytes, Gm.k, Gm.res_base, pl.n_pages,
+                          pl.n_res, pl.page_splits, pl.groups_per_split,
+                          pl.total_splits - pl.page_splits, pl.max_splits, Gm.scale * kLog2e,
+                          pl.dstate);
     return hipGetLastError();
 }
 
 template <int DT, int G>
 hipError_t launch2(const Geometry &Gm, uint8_t *cache, const uint16_t *kn, const uint16_t *vn,
                    int slot, const uint16_t *q, float *ml, float *acc, const DecodePlan &pl,
-                   hipStream_t st) {
+                   hipEvent_t e0, hipEvent_t e1, hipStream_t st) {
     switch ((Gm.k + 31) / 32) {
-        case 0: return launch3<DT, G, 0>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
-        case 1: return launch3<DT, G, 1>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
-        case 2: return launch3<DT, G, 2>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
-        case 3: return launch3<DT, G, 3>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
-        case 4: return launch3<DT, G, 4>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
+        case 0: return launch3<DT, G, 0>(Gm, cache, kn, vn, slot, q, ml, acc, pl, e0, e1, st);
+        case 1: return launch3<DT, G, 1>(Gm, cache, kn, vn, slot, q, ml, acc, pl, e0, e1, st);
+        case 2: return launch3<DT, G, 2>(Gm, cache, kn, vn, slot, q, ml, acc, pl, e0, e1, st);
+        case 3: return launch3<DT, G, 3>(Gm, cache, kn, vn, slot, q, ml, acc, pl, e0, e1, st);
+        case 4: return launch3<DT, G, 4>(Gm, cache, kn, vn, slot, q, ml, acc, pl, e0, e1, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -185,13 +186,13 @@ hipError_t launch2(const Geometry &Gm, uint8_t *cache, const uint16_t *kn, const
 template <int DT>
 hipError_t launch1(const Geometry &Gm, uint8_t *cache, const uint16_t *kn, const uint16_t *vn,
                    int slot, const uint16_t *q, float *ml, float *acc, const DecodePlan &pl,
-                   hipStream_t st) {
+                   hipEvent_t e0, hipEvent_t e1, hipStream_t st) {
     switch (Gm.g) {
-        case 1: return launch2<DT, 1>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
-        case 2: return launch2<DT, 2>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
-        case 4: return launch2<DT, 4>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
-        case 8: return launch2<DT, 8>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
-        case 16: return launch2<DT, 16>(Gm, cache, kn, vn, slot, q, ml, acc, pl, st);
+        case 1: return launch2<DT, 1>(Gm, cache, kn, vn, slot, q, ml, acc, pl, e0, e1, st);
+        case 2: return launch2<DT, 2>(Gm, cache, kn, vn, slot, q, ml, acc, pl, e0, e1, st);
+        case 4: return launch2<DT, 4>(Gm, cache, kn, vn, slot, q, ml, acc, pl, e0, e1, st);
+        case 8: return launch2<DT, 8>(Gm, cache, kn, vn, slot, q, ml, acc, pl, e0, e1, st);
+        case 16: return launch2<DT, 16>(Gm, cache, kn, vn, slot, q, ml, acc, pl, e0, e1, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -240,12 +241,10 @@ hipError_t launch_decode(const Geometry &G, uint8_t *cache, const uint16_t *q,
     if (slot < 0) kn = vn = q;  // never dereferenced: no window token equals slot -1
     float *ml = reinterpret_cast<float *>(workspace);
     float *acc = ml + (size_t)G.B * G.Hq * pl.max_splits * 2;
-    hipError_t e;
-    if (ev_before && (e = hipEventRecord(ev_before, st)) != hipSuccess) return e;
-    e = G.dtype == F16 ? launch1<F16>(G, cache, kn, vn, slot, q, ml, acc, pl, st)
-                       : launch1<BF16>(G, cache, kn, vn, slot, q, ml, acc, pl, st);
+    const hipError_t e =
+        G.dtype == F16 ? launch1<F16>(G, cache, kn, vn, slot, q, ml, acc, pl, ev_before, ev_after, st)
+                       : launch1<BF16>(G, cache, kn, vn, slot, q, ml, acc, pl, ev_before, ev_after, st);
     if (e != hipSuccess) return e;
-    if (ev_after && (e = hipEventRecord(ev_after, st)) != hipSuccess) return e;
     if (pl.total_splits > kMaxCombine) return hipErrorInvalidValue;
     const int rows = G.B * G.Hq;
     if (pl.total_splits <= 16)

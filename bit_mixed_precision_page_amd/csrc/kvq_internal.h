@@ -2,6 +2,7 @@
 // the 2-bit mixed-precision KV cache library (gfx950).  Not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>

@@ -95,25 +95,26 @@ int pslots3() {
 template <int DT, int G, int KH>
 hipError_t plaunch3(const Geometry &Gm, uint8_t *mem, const int32_t *table, const uint16_t *kn,
                     const uint16_t *vn, const uint16_t *q, float *ml, float *acc,
-                    const PoolPlan &pl, hipStream_t st) {
+                    const PoolPlan &pl, hipEvent_t e0, hipEvent_t e1, hipStream_t st) {
     const uint32_t wgs = pl.page_pref[pl.n_seq] + pl.win_pref[pl.n_seq];
     if (wgs == 0) return hipSuccess;
-    hipLaunchKernelGGL((pool_split_kernel<DT, G, KH>), dim3(wgs), dim3(64), 0, st, mem, mem, kn,
-                       vn, q, ml, acc, table, Gm.Hkv, Gm.max_pages, Gm.page_bytes, Gm.k,
-                       Gm.res_base, Gm.scale * kLog2e, pl);
+    // with timing events: the dispatch's own start and end timestamps
+    hipExtLaunchKernelGGL((pool_split_kernel<DT, G, KH>), dim3(wgs), dim3(64), 0, st, e0, e1, 0,
+                          (const uint8_t *)mem, mem, kn, vn, q, ml, acc, table, Gm.Hkv,
+                          Gm.max_pages, Gm.page_bytes, Gm.k, Gm.res_base, Gm.scale * kLog2e, pl);
     return hipGetLastError();
 }
 
 template <int DT, int G>
 hipError_t plaunch2(const Geometry &Gm, uint8_t *mem, const int32_t *table, const uint16_t *kn,
                     const uint16_t *vn, const uint16_t *q, float *ml, float *acc,
-                    const PoolPlan &pl, hipStream_t st) {
+                    const PoolPlan &pl, hipEvent_t e0, hipEvent_t e1, hipStream_t st) {
     switch ((Gm.k + 31) / 32) {
-        case 0: return plaunch3<DT, G, 0>(Gm, mem, table, kn, vn, q, ml, acc, pl, st);
-        case 1: return plaunch3<DT, G, 1>(Gm, mem, table, kn, vn, q, ml, acc, pl, st);
-        case 2: return plaunch3<DT, G, 2>(Gm, mem, table, kn, vn, q, ml, acc, pl, st);
-        case 3: return plaunch3<DT, G, 3>(Gm, mem, table, kn, vn, q, ml, acc, pl, st);
-        case 4: return plaunch3<DT, G, 4>(Gm, mem, table, kn, vn, q, ml, acc, pl, st);
+        case 0: return plaunch3<DT, G, 0>(Gm, mem, table, kn, vn, q, ml, acc, pl, e0, e1, st);
+        case 1: return plaunch3<DT, G, 1>(Gm, mem, table, kn, vn, q, ml, acc, pl, e0, e1, st);
+        case 2: return plaunch3<DT, G, 2>(Gm, mem, table, kn, vn, q, ml, acc, pl, e0, e1, st);
+        case 3: return plaunch3<DT, G, 3>(Gm, mem, table, kn, vn, q, ml, acc, pl, e0, e1, st);
+        case 4: return plaunch3<DT, G, 4>(Gm, mem, table, kn, vn, q, ml, acc, pl, e0, e1, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -121,13 +122,13 @@ hipError_t plaunch2(const Geometry &Gm, uint8_t *mem, const int32_t *table, cons
 template <int DT>
 hipError_t plaunch1(const Geometry &Gm, uint8_t *mem, const int32_t *table, const uint16_t *kn,
                     const uint16_t *vn, const uint16_t *q, float *ml, float *acc,
-                    const PoolPlan &pl, hipStream_t st) {
+                    const PoolPlan &pl, hipEvent_t e0, hipEvent_t e1, hipStream_t st) {
     switch (Gm.g) {
-        case 1: return plaunch2<DT, 1>(Gm, mem, table, kn, vn, q, ml, acc, pl, st);
-        case 2: return plaunch2<DT, 2>(Gm, mem, table, kn, vn, q, ml, acc, pl, st);
-        case 4: return plaunch2<DT, 4>(Gm, mem, table, kn, vn, q, ml, acc, pl, st);
-        case 8: return plaunch2<DT, 8>(Gm, mem, table, kn, vn, q, ml, acc, pl, st);
-        case 16: return plaunch2<DT, 16>(Gm, mem, table, kn, vn, q, ml, acc, pl, st);
+        case 1: return plaunch2<DT, 1>(Gm, mem, table, kn, vn, q, ml, acc, pl, e0, e1, st);
+        case 2: return plaunch2<DT, 2>(Gm, mem, table, kn, vn, q, ml, acc, pl, e0, e1, st);
+        case 4: return plaunch2<DT, 4>(Gm, mem, table, kn, vn, q, ml, acc, pl, e0, e1, st);
+        case 8: return plaunch2<DT, 8>(Gm, mem, table, kn, vn, q, ml, acc, pl, e0, e1, st);
+        case 16: return plaunch2<DT, 16>(Gm, mem, table, kn, vn, q, ml, acc, pl, e0, e1, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -167,12 +168,10 @@ hipError_t launch_pool_decode(const Geometry &G, uint8_t *mem, const int32_t *ta
     if (pl.max_splits > kMaxCombine) return hipErrorInvalidValue;
     float *ml = reinterpret_cast<float *>(workspace);
     float *acc = ml + (size_t)G.B * G.Hq * pl.max_splits * 2;
-    hipError_t e;
-    if (ev_before && (e = hipEventRecord(ev_before, st)) != hipSuccess) return e;
-    e = G.dtype == F16 ? plaunch1<F16>(G, mem, table, kn, vn, q, ml, acc, pl, st)
-                       : plaunch1<BF16>(G, mem, table, kn, vn, q, ml, acc, pl, st);
+    hipError_t e =
+        G.dtype == F16 ? plaunch1<F16>(G, mem, table, kn, vn, q, ml, acc, pl, ev_before, ev_after, st)
+                       : plaunch1<BF16>(G, mem, table, kn, vn, q, ml, acc, pl, ev_before, ev_after, st);
     if (e != hipSuccess) return e;
-    if (ev_after && (e = hipEventRecord(ev_after, st)) != hipSuccess) return e;
     int max_n = 0;
     for (int b = 0; b < pl.n_seq; b++)
         max_n = std::max(max_n, (int)(pl.page_pref[b + 1] - pl.page_pref[b] + pl.win_pref[b + 1] -

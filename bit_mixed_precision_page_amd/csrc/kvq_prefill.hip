@@ -565,10 +565,10 @@ hipError_t prefill_launch(const PrefillArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(v_transpose_kernel, dim3(a.T32 / 32, a.Hkv), dim3(256), 0, st, a.v, a.vt,
                        a.T, a.T32);
     const int hw = g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
-    if (a.ev_before) (void)hipEventRecord(a.ev_before, st);
-    hipLaunchKernelGGL((prefill_fwd_kernel<DT>), dim3(a.Hq / hw, (a.T + 128 / hw - 1) / (128 / hw)),
-                       dim3(256), 0, st, a.q, a.k, a.vt, a.out, a.lse, a.T, a.T32, g, hw, qscale);
-    if (a.ev_after) (void)hipEventRecord(a.ev_after, st);
+    // with timing events: the dispatch's own start and end timestamps
+    hipExtLaunchKernelGGL((prefill_fwd_kernel<DT>), dim3(a.Hq / hw, (a.T + 128 / hw - 1) / (128 / hw)),
+                          dim3(256), 0, st, a.ev_before, a.ev_after, 0, a.q, a.k,
+                          (const uint16_t *)a.vt, a.out, a.lse, a.T, a.T32, g, hw, qscale);
     // query chunks of cr rows (a multiple of kCsRows), at most kColsumChunks of them
     const int cr = ((a.T + kColsumChunks - 1) / kColsumChunks + kCsRows - 1) / kCsRows * kCsRows;
     const int nchunk = (a.T + cr - 1) / cr;
