@@ -157,3 +157,43 @@ def test_prefill_full_size_sampled():
     for h in range(w.Hkv):
         want = ora.select_tokens(score[h].astype(np.float64), heavy, recent)
         assert keep[h].tolist() == want.tolist()
+
+
+def test_prefill_long_sequence_sampled():
+    """A 65536-token sequence (two KV heads, eight query heads): the first 256
+    rows against the oracle, the last key's score against its softmax
+    probabilities, the score totals, and the selection rule on the GPU scores
+    (many query chunks, every tile count of the score pass past its first)."""
+    from bit_mixed_precision_page_amd import kvq
+    w = dataclasses.replace(W["llama3_8b_prefill_select"], Hq=8, Hkv=2, ctx=65536)
+    T = w.ctx
+    heavy = recent = T // 8
+    q, k, v = _inputs(w, T)
+    out, score, keep, k_sel, v_sel = kvq.prefill_select(w.dtype, dev(q), dev(k), dev(v), heavy,
+                                                        recent)
+    torch.cuda.synchronize()
+    score, keep = host(score), host(keep)
+    out0 = host(out[:, :256])
+    del out, k_sel, v_sel
+    ora = oracle.lib()
+    T0 = 256
+    o_ref, _ = ora.prefill_attention(w.dtype, q[:, :T0], k[:, :T0], v[:, :T0], 1.0 / np.sqrt(128))
+    err = np.abs(out0 - o_ref).max()
+    g = w.Hq // w.Hkv
+    qf = gen.from_bits(q[:, T - 1], w.dtype).astype(np.float64)
+    kf = gen.from_bits(k, w.dtype).astype(np.float64)
+    last = []
+    for h in range(w.Hkv):
+        s = qf[h * g:(h + 1) * g] @ kf[h].T / np.sqrt(128)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        last.append(p[:, T - 1].sum())
+    lerr = np.abs(score[:, T - 1] - np.array(last)).max()
+    say(f"    T={T}: rows 0..{T0 - 1} |out - oracle| = {err:.2e}, last-key score err {lerr:.2e}, "
+        f"score totals {score.sum(axis=1).min():.1f}..{score.sum(axis=1).max():.1f}")
+    assert err <= TOL
+    assert lerr <= 1e-5
+    assert np.allclose(score.sum(axis=1), g * T, rtol=1e-4)
+    for h in range(w.Hkv):
+        want = ora.select_tokens(score[h].astype(np.float64), heavy, recent)
+        assert keep[h].tolist() == want.tolist()
