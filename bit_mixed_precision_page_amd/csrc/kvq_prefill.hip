@@ -125,8 +125,8 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t *__rest
 // query row and keys 4 b + e, 16 + 4 b + e of the block, which is directly
 // the B operand of O^T = V^T P^T once the Values are stored in the slot
 // order of slot_key -- no transpose of P.
-constexpr int kKRow = D + 8;          // LDS Key row (272 B: 16-byte reads conflict-free)
-constexpr int kVRow = 40;             // LDS Value row, 32 slots + pad (80 B)
+constexpr int kKRow = D + 8;          // LDS Key row (272 B: consecutive rows start 4 banks apart)
+constexpr int kVRow = 40;             // LDS Value row, 32 slots + pad (80 B: 20 banks apart)
 constexpr int kKTile = 32 * kKRow;    // elements
 constexpr int kFwdBuf = kKTile + D * kVRow;
 
