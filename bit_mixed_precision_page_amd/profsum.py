@@ -30,7 +30,8 @@ ROOT = os.path.dirname(HERE)
 COPY = "__amd_rocclr_copyBuffer"
 # sources each profiled kernel is built from: a counter record holds only for that code
 KERNEL_SRC = {"decode_split_kernel": ["kvq_decode_core.h", "kvq_decode.hip"],
-              "pool_split_kernel": ["kvq_decode_core.h", "kvq_pool.hip"]}
+              "pool_split_kernel": ["kvq_decode_core.h", "kvq_pool.hip"],
+              "prefill_fwd_kernel": ["kvq_decode_core.h", "kvq_prefill.hip"]}
 
 
 def source_sha256(kernel):
