@@ -543,19 +543,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__rest
 }
 
 // ---------------------------------------------------------------- stage 4
-__global__ __launch_bounds__(64) void gather_kernel(const uint16_t *__restrict__ k,
-                                                    const uint16_t *__restrict__ v,
-                                                    const int32_t *__restrict__ keep,
-                                                    uint16_t *__restrict__ k_sel,
-                                                    uint16_t *__restrict__ v_sel, int T,
-                                                    int n_keep) {
-    const int p = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+// eight kept positions per workgroup: thread (row, K or V, 16-byte chunk)
+__global__ __launch_bounds__(256) void gather_kernel(const uint16_t *__restrict__ k,
+                                                     const uint16_t *__restrict__ v,
+                                                     const int32_t *__restrict__ keep,
+                                                     uint16_t *__restrict__ k_sel,
+                                                     uint16_t *__restrict__ v_sel, int T,
+                                                     int n_keep) {
+    const int h = blockIdx.y, t = threadIdx.x, p = 8 * blockIdx.x + (t >> 5);
+    if (p >= n_keep) return;
     const int src = min(max(keep[(size_t)h * n_keep + p], 0), T - 1);
-    const int c8 = lane & 15;
-    const uint16_t *from = (lane < 16 ? k : v) + ((size_t)h * T + src) * D;
-    uint16_t *to = (lane < 16 ? k_sel : v_sel) + ((size_t)h * n_keep + p) * D;
-    if (lane < 32)
-        *reinterpret_cast<uint4 *>(to + 8 * c8) = *reinterpret_cast<const uint4 *>(from + 8 * c8);
+    const int c8 = t & 15;
+    const bool isk = (t & 16) == 0;
+    const uint16_t *from = (isk ? k : v) + ((size_t)h * T + src) * D;
+    uint16_t *to = (isk ? k_sel : v_sel) + ((size_t)h * n_keep + p) * D;
+    *reinterpret_cast<uint4 *>(to + 8 * c8) = *reinterpret_cast<const uint4 *>(from + 8 * c8);
 }
 
 template <int DT>
@@ -582,8 +584,8 @@ hipError_t prefill_launch(const PrefillArgs &a, hipStream_t st) {
         hipLaunchKernelGGL(select_kernel, dim3(a.Hkv), dim3(kSelThreads), 0, st, a.score, a.T,
                            a.heavy, a.recent, a.keep, a.n_keep);
         if (a.k_sel && a.v_sel)
-            hipLaunchKernelGGL(gather_kernel, dim3(a.n_keep, a.Hkv), dim3(64), 0, st, a.k, a.v,
-                               a.keep, a.k_sel, a.v_sel, a.T, a.n_keep);
+            hipLaunchKernelGGL(gather_kernel, dim3((a.n_keep + 7) / 8, a.Hkv), dim3(256), 0, st,
+                               a.k, a.v, a.keep, a.k_sel, a.v_sel, a.T, a.n_keep);
     }
     return hipGetLastError();
 }
