@@ -120,7 +120,7 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
-              "(the path shards by (sequence, KV head) with no exchange; see the design notes)",
+              "(the path would shard by (sequence, KV head), with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
     import torch
