@@ -49,6 +49,8 @@ def parse():
                          "kvq_append_decode, same results)")
     ap.add_argument("--event-fence", action="store_true",
                     help="events with the default system-scope fence (slower markers)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="prefill selection workload: sequence length (0 = the workload's)")
     ap.add_argument("--query-aware", action="store_true",
                     help="rank Key channels by group range x query relevance (relevance of "
                          "the first decode query) instead of magnitude")
@@ -420,7 +422,7 @@ def prefill_main(a, w, torch, gen, kvq):
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
 
-    T = w.ctx
+    T = a.tokens if a.tokens > 0 else w.ctx
     heavy = recent = int(w.select * T)
     print(f"[bench] workload {w.name}: T={T} Hq={w.Hq} Hkv={w.Hkv} heavy={heavy} recent={recent}",
           file=sys.stderr, flush=True)
