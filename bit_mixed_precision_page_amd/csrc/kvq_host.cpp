@@ -251,10 +251,20 @@ size_t prefill_stats_bytes(int32_t T, int32_t Hq) { return align256((size_t)Hq *
 size_t prefill_part_bytes(int32_t T, int32_t Hkv) {
     return align256((size_t)Hkv * kvq::kColsumChunks * T * 4);
 }
-size_t prefill_ws_bytes(int32_t T, int32_t Hq, int32_t Hkv) {
+size_t prefill_vt_bytes(int32_t T, int32_t Hkv) {
     const size_t T32 = ((size_t)T + 31) / 32 * 32;
-    return prefill_stats_bytes(T, Hq) + prefill_part_bytes(T, Hkv) +
-           (size_t)Hkv * kvq::D * T32 * 2;
+    return align256((size_t)Hkv * kvq::D * T32 * 2);
+}
+// partials of the key-split attention (none when the keys are not split)
+size_t prefill_split_bytes(int32_t T, int32_t Hq, int32_t Hkv) {
+    int kbc;
+    const int s = kvq::prefill_key_splits(T, Hq, Hkv, &kbc);
+    return s > 1 ? align256((size_t)Hq * T * s * 2 * 4) + align256((size_t)Hq * T * s * kvq::D * 4)
+                 : 0;
+}
+size_t prefill_ws_bytes(int32_t T, int32_t Hq, int32_t Hkv) {
+    return prefill_stats_bytes(T, Hq) + prefill_part_bytes(T, Hkv) + prefill_vt_bytes(T, Hkv) +
+           prefill_split_bytes(T, Hq, Hkv);
 }
 int prefill_shape_ok(int32_t T, int32_t Hq, int32_t Hkv) {
     return T >= 1 && T <= kPrefillMaxT && Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 &&
@@ -548,6 +558,15 @@ int kvq_prefill_select(int32_t dtype, int32_t T, int32_t num_q_heads, int32_t nu
     a.part = reinterpret_cast<float *>(ws + prefill_stats_bytes(T, num_q_heads));
     a.vt = reinterpret_cast<uint16_t *>(ws + prefill_stats_bytes(T, num_q_heads) +
                                         prefill_part_bytes(T, num_kv_heads));
+    a.nsplit = kvq::prefill_key_splits(T, num_q_heads, num_kv_heads, &a.kbc);
+    {
+        uint8_t *sp = ws + prefill_stats_bytes(T, num_q_heads) + prefill_part_bytes(T, num_kv_heads) +
+                      prefill_vt_bytes(T, num_kv_heads);
+        a.pml = a.nsplit > 1 ? reinterpret_cast<float *>(sp) : nullptr;
+        a.pacc = a.nsplit > 1
+                     ? reinterpret_cast<float *>(sp + align256((size_t)num_q_heads * T * a.nsplit * 2 * 4))
+                     : nullptr;
+    }
     a.out = out;
     a.score = score;
     a.keep = keep;

@@ -5,6 +5,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 
@@ -99,6 +100,23 @@ size_t decode_workspace_bytes(const Geometry &G, int max_splits);
 
 // Query chunks the column sums of the cumulative scores are split over.
 constexpr int kColsumChunks = 16;
+// Short sequences give the attention kernel too few workgroups for the chip:
+// then the keys of each row block are split into up to kPrefillMaxKeySplits
+// chunks of kbc 32-key blocks, each chunk a workgroup writing unnormalized
+// partials that a merge kernel combines.  Returns the chunk count (1: no
+// split, kbc = every block).
+constexpr int kPrefillSplitWgs = 768;     // three attention workgroups per CU
+constexpr int kPrefillMaxKeySplits = 4;
+inline int prefill_key_splits(int T, int Hq, int Hkv, int *kbc) {
+    const int g = Hq / Hkv, hw = g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
+    const int qr = 128 / hw, nb = (T + 31) / 32;
+    const long wgs = (long)(Hq / hw) * ((T + qr - 1) / qr);
+    int s = 1;
+    if (wgs < kPrefillSplitWgs)
+        s = (int)std::min<long>(kPrefillMaxKeySplits, (kPrefillSplitWgs + wgs - 1) / wgs);
+    *kbc = (nb + s - 1) / s;
+    return (nb + *kbc - 1) / *kbc;
+}
 // Prefill of one sequence: causal attention with cumulative attention scores,
 // heavy-hitter + recent token selection and the gather of the kept rows.
 struct PrefillArgs {
@@ -111,6 +129,8 @@ struct PrefillArgs {
     float *out, *score;         // [Hq][T][D], [Hkv][T]
     int32_t *keep;              // [Hkv][n_keep]
     uint16_t *k_sel, *v_sel;    // [Hkv][n_keep][D], or null
+    int nsplit, kbc;            // key chunks per row block, 32-key blocks per chunk
+    float *pml, *pacc;          // workspace when nsplit > 1: [Hq][T][nsplit] (m, l), (.., D) acc
     hipEvent_t ev_before, ev_after;  // optional, around the attention kernel
 };
 hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream);

@@ -43,6 +43,7 @@ namespace kvq {
 namespace {
 
 constexpr int kSelThreads = 1024;
+constexpr int kSelCache = 16384;  // scores cached in LDS (64 KB)
 
 // fp32 pair -> dtype pair, round to nearest even
 template <int DT>
@@ -184,7 +185,8 @@ template <int DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void prefill_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ vt, float *__restrict__ out, float *__restrict__ lse, int T,
-    int T32, int g, int hw, float qscale) {
+    int T32, int g, int hw, float qscale, int kbc, int nsplit, float *__restrict__ pml,
+    float *__restrict__ pacc) {
     __shared__ __align__(16) uint16_t lds[2 * kFwdBuf];
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kb = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -198,6 +200,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int nb = T32 / 32;
     const uint16_t *kh = k + (size_t)h * T * D;
     const uint16_t *vth = vt + (size_t)h * nb * D * 32;
+    // key chunk of this workgroup: blocks [jb0, jb1) (every block when the
+    // keys are not split)
+    const int chunk = blockIdx.z, jb0 = chunk * kbc;
+    if (jb0 >= nbg) return;  // workgroup-uniform: no key of the chunk precedes its rows
+    const int jb1 = min(nbg, jb0 + kbc);
 
     // block jb -> registers (two 16-byte pieces of Keys and two of Values per thread)
     u4_t pk[2], pv[2];
@@ -239,13 +246,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         for (int n = 0; n < 8; n++) acc[u][n] = f4_t{0, 0, 0, 0};
     }
 
-    gload(0);
-    lstore(0);
-    if (nbg > 1) gload(1);
-    for (int jb = 0; jb < nbg; jb++) {
+    gload(jb0);
+    lstore(jb0 & 1);
+    if (jb0 + 1 < jb1) gload(jb0 + 1);
+    for (int jb = jb0; jb < jb1; jb++) {
         __syncthreads();  // block jb is in LDS; every wave is done with block jb - 1
-        if (jb + 1 < nbg) lstore((jb + 1) & 1);
-        if (jb + 2 < nbg) gload(jb + 2);
+        if (jb + 1 < jb1) lstore((jb + 1) & 1);
+        if (jb + 2 < jb1) gload(jb + 2);
         if (jb >= nbw) continue;
         const uint16_t *L = lds + (jb & 1) * kFwdBuf;
         const int j0 = 32 * jb;
@@ -286,6 +293,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             }
         }
     }
+    if (nsplit > 1) {
+        // unnormalized partials of this key chunk; a wave whose rows end
+        // before the chunk writes none (the merge does not read them)
+        if (jb0 >= nbw) return;
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const float l = xrow_sum(l_run[u]);
+            const int i = i0w + 16 * u + r;
+            if (i < T) {
+                const size_t pr = ((size_t)hq * T + i) * nsplit + chunk;
+                float *o = pacc + pr * D + 4 * kb;
+#pragma unroll
+                for (int n = 0; n < 8; n++) *reinterpret_cast<f4_t *>(o + 16 * n) = acc[u][n];
+                if (kb == 0) *reinterpret_cast<float2 *>(pml + 2 * pr) = make_float2(m_run[u], l);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < 2; u++) {
         const float l = xrow_sum(l_run[u]);
@@ -300,6 +325,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             if (kb == 0) lse[(size_t)hq * T + i] = m_run[u] + __builtin_amdgcn_logf(l);
         }
     }
+}
+
+// Key-split attention: row (hq, i) combines the partials of the chunks that
+// hold keys <= i, one wave per row, two channels per lane.
+__global__ __launch_bounds__(256) void prefill_merge_kernel(const float *__restrict__ pml,
+                                                            const float *__restrict__ pacc,
+                                                            float *__restrict__ out,
+                                                            float *__restrict__ lse, int T,
+                                                            int rows, int nsplit, int kbc) {
+    const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const int i = row % T, nch = min(nsplit, (i / 32) / kbc + 1);
+    float2 st[kPrefillMaxKeySplits], x[kPrefillMaxKeySplits];
+    float M = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kPrefillMaxKeySplits; c++) {
+        if (c < nch) {
+            const size_t pr = (size_t)row * nsplit + c;
+            st[c] = *reinterpret_cast<const float2 *>(pml + 2 * pr);
+            x[c] = *reinterpret_cast<const float2 *>(pacc + pr * D + 2 * lane);
+            M = fmaxf(M, st[c].x);
+        }
+    }
+    float L = 0.0f, ax = 0.0f, ay = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kPrefillMaxKeySplits; c++) {
+        if (c < nch) {
+            const float w = __builtin_amdgcn_exp2f(st[c].x - M);
+            L = fmaf(w, st[c].y, L);
+            ax = fmaf(w, x[c].x, ax);
+            ay = fmaf(w, x[c].y, ay);
+        }
+    }
+    const float inv = 1.0f / L;
+    *reinterpret_cast<float2 *>(out + (size_t)row * D + 2 * lane) = make_float2(ax * inv, ay * inv);
+    if (lane == 0) lse[row] = M + __builtin_amdgcn_logf(L);
 }
 
 // ---------------------------------------------------------------- stage 2
@@ -491,8 +553,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__rest
     __shared__ unsigned hist[256];
     __shared__ unsigned wtot[kSelThreads / 64];
     __shared__ unsigned pick[2];
+    __shared__ uint32_t cache[kSelCache];
     const int h = blockIdx.x, t = threadIdx.x;
     const uint32_t *sb = reinterpret_cast<const uint32_t *>(score + (size_t)h * T);
+    // scores of up to kSelCache positions are read once into LDS
+    const bool cached = T <= kSelCache;
+    if (cached) {
+        for (int x = t; x < T; x += kSelThreads) cache[x] = sb[x];
+        __syncthreads();
+    }
+    auto bits = [&](int x) { return cached ? cache[x] : sb[x]; };
     const int rec = min(recent, T), n_old = T - rec, hv = min(heavy, n_old);
     const int chunk = (T + kSelThreads - 1) / kSelThreads;
     const int b0 = min(T, t * chunk), b1 = min(T, b0 + chunk), ob1 = min(n_old, b1);
@@ -504,40 +574,59 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__rest
             if (t < 256) hist[t] = 0;
             __syncthreads();
             for (int x = b0; x < ob1; x++) {
-                const uint32_t u = sb[x];
+                const uint32_t u = bits(x);
                 if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
             }
             __syncthreads();
-            // counts of the bins from the top: thread t < 256 holds bin 255 - t
-            const unsigned c = t < 256 ? hist[255 - t] : 0u;
-            const unsigned above = block_scan(c, wtot, &tot) - c;  // in higher bins
-            if (t < 256 && above < need && above + c >= need) {
-                pick[0] = 255u - t;
-                pick[1] = above;
+            // the first wave finds the bin holding the need-th largest: lane l
+            // holds bins 255 - 4 l - [0, 4), the counts above it by a wave scan
+            if (t < 64) {
+                unsigned c[4], s4 = 0;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    c[e] = hist[255 - 4 * t - e];
+                    s4 += c[e];
+                }
+                unsigned inc = s4;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const unsigned y = __shfl_up(inc, off, 64);
+                    if (t >= off) inc += y;
+                }
+                unsigned above = inc - s4;  // in higher bins
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    if (above < need && above + c[e] >= need) {
+                        pick[0] = 255u - 4 * t - e;
+                        pick[1] = above;
+                    }
+                    above += c[e];
+                }
             }
             __syncthreads();
             prefix |= pick[0] << shift;
             mask |= 255u << shift;
             need -= pick[1];
-            __syncthreads();
         }
         thr = prefix;  // the hv-th largest; need = how many at that score are kept
     }
     // ties at the threshold before this thread's chunk
     unsigned ties = 0;
-    for (int x = b0; x < ob1; x++) ties += sb[x] == thr;
+    for (int x = b0; x < ob1; x++) ties += bits(x) == thr;
     const unsigned tie0 = block_scan(ties, wtot, &tot) - ties;
     // kept positions of this chunk, then their places
     unsigned kept = 0, rank = tie0;
     for (int x = b0; x < b1; x++) {
-        const bool k = x >= n_old || sb[x] > thr || (sb[x] == thr && rank++ < need);
+        const uint32_t u = bits(x);
+        const bool k = x >= n_old || u > thr || (u == thr && rank++ < need);
         kept += k;
     }
     const unsigned pos0 = block_scan(kept, wtot, &tot) - kept;
     unsigned pos = pos0;
     rank = tie0;
     for (int x = b0; x < b1; x++) {
-        const bool k = x >= n_old || sb[x] > thr || (sb[x] == thr && rank++ < need);
+        const uint32_t u = bits(x);
+        const bool k = x >= n_old || u > thr || (u == thr && rank++ < need);
         if (k && pos < (unsigned)n_keep) keep[(size_t)h * n_keep + pos++] = x;
     }
 }
@@ -568,9 +657,15 @@ hipError_t prefill_launch(const PrefillArgs &a, hipStream_t st) {
                        a.T, a.T32);
     const int hw = g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
     // with timing events: the dispatch's own start and end timestamps
-    hipExtLaunchKernelGGL((prefill_fwd_kernel<DT>), dim3(a.Hq / hw, (a.T + 128 / hw - 1) / (128 / hw)),
-                          dim3(256), 0, st, a.ev_before, a.ev_after, 0, a.q, a.k,
-                          (const uint16_t *)a.vt, a.out, a.lse, a.T, a.T32, g, hw, qscale);
+    hipExtLaunchKernelGGL((prefill_fwd_kernel<DT>),
+                          dim3(a.Hq / hw, (a.T + 128 / hw - 1) / (128 / hw), a.nsplit), dim3(256),
+                          0, st, a.ev_before, a.ev_after, 0, a.q, a.k, (const uint16_t *)a.vt,
+                          a.out, a.lse, a.T, a.T32, g, hw, qscale, a.kbc, a.nsplit, a.pml, a.pacc);
+    if (a.nsplit > 1) {
+        const int rows = a.Hq * a.T;
+        hipLaunchKernelGGL(prefill_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, a.pml,
+                           a.pacc, a.out, a.lse, a.T, rows, a.nsplit, a.kbc);
+    }
     // query chunks of cr rows (a multiple of kCsRows), at most kColsumChunks of them
     const int cr = ((a.T + kColsumChunks - 1) / kColsumChunks + kCsRows - 1) / kCsRows * kCsRows;
     const int nchunk = (a.T + cr - 1) / cr;
