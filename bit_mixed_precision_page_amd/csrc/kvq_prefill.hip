@@ -23,7 +23,9 @@
 //          domain; P^T split into a dtype hi and lo part (~16 bits for bf16,
 //          ~22 for fp16) feeds O^T = V^T P^T directly, 2 MFMAs per
 //          16-channel tile.  Writes out (fp32) and per row the log2 of the
-//          softmax denominator.
+//          softmax denominator.  A short sequence (too few workgroups for
+//          the chip) splits each row block's keys into chunks whose
+//          unnormalized partials a merge kernel combines.
 // Stage 2  cumulative scores: four-wave workgroups over 256 keys of one KV
 //          head and a chunk of query rows, Key operands in registers, the
 //          query blocks of every query head of the group streamed through
