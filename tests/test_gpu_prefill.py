@@ -197,3 +197,34 @@ def test_prefill_long_sequence_sampled():
     for h in range(w.Hkv):
         want = ora.select_tokens(score[h].astype(np.float64), heavy, recent)
         assert keep[h].tolist() == want.tolist()
+
+
+def test_prefill_timing_hook():
+    """kvq_prefill_set_kernel_events: the attention kernel's own dispatch
+    timestamps land in the two events; the outputs are those of a call
+    without the hook; clearing it leaves later calls untimed."""
+    import ctypes
+    from bit_mixed_precision_page_amd import kvq
+    hip = ctypes.CDLL("libamdhip64.so")
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    w = dataclasses.replace(W["llama3_8b_prefill_select"], Hq=8, Hkv=2)
+    T = 1024
+    q, k, v = _inputs(w, T)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    ref = kvq.prefill_select(w.dtype, qd, kd, vd, 64, 64)
+    kvq.kvq_prefill_set_kernel_events(ev[0].value, ev[1].value)
+    try:
+        got = kvq.prefill_select(w.dtype, qd, kd, vd, 64, 64)
+        torch.cuda.synchronize()
+    finally:
+        kvq.kvq_prefill_set_kernel_events(None, None)
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+    say(f"    attention kernel {ms.value * 1e3:.1f} us")
+    assert 0.0 < ms.value < 1000.0
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    for e in ev:
+        hip.hipEventDestroy(e)
