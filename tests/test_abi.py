@@ -299,3 +299,20 @@ def test_prefill_argument_checks():
     # timing hooks: both or neither
     assert code(lambda: kvq.kvq_prefill_set_kernel_events(FAKE, None)) == "KVQ_EINVAL"
     kvq.kvq_prefill_set_kernel_events(None, None)
+
+
+def test_prefill_workspace_covers_the_key_split():
+    """Short sequences split the keys and need room for the per-chunk partials
+    (m, l and 128 accumulators per row and chunk); long ones do not."""
+    from bit_mixed_precision_page_amd import kvq
+
+    def base(T, hq, hkv):
+        t32 = (T + 31) // 32 * 32
+        return hq * T * 4 + hkv * 16 * T * 4 + hkv * 128 * t32 * 2
+
+    # 1024 tokens, 32 / 8 heads: 256 attention workgroups -> three key chunks
+    ws = kvq.kvq_prefill_workspace_bytes(1024, 32, 8)
+    assert ws >= base(1024, 32, 8) + 32 * 1024 * 3 * (2 + 128) * 4
+    # 8192 tokens: 2048 workgroups, no split, no partials
+    ws = kvq.kvq_prefill_workspace_bytes(8192, 32, 8)
+    assert base(8192, 32, 8) <= ws < base(8192, 32, 8) + 4 * 256
