@@ -216,6 +216,7 @@ def main():
     n_flush = 0
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
+    t_host = time.perf_counter()
     for i in range(a.steps):
         s = a.warmup + i
         flushed, n_pages, n_res = step(s, ev_of.get(i))
@@ -226,6 +227,7 @@ def main():
             split_bytes.append(ab - w.B * w.Hq * 128 * 4)  # pages + window + query
         n_flush += int(flushed)
     end.record()
+    host_us = (time.perf_counter() - t_host) / a.steps * 1e6  # launch loop, host side
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
     ms_step = ms / a.steps
@@ -237,7 +239,7 @@ def main():
     splits = kvq.kvq_get_decode_splits(caches[0].handle)
     print(f"[bench] {a.steps} steps in {ms:.3f} ms ({ms_step * 1e3:.1f} us/step, "
           f"split kernel avg {kern_avg_s * 1e6:.1f} us over {len(timed)} launches, "
-          f"{n_flush} flushes)", file=sys.stderr, flush=True)
+          f"{n_flush} flushes; host {host_us:.1f} us/step to launch)", file=sys.stderr, flush=True)
 
     cpu = None
     if not a.no_cpu_baseline:
