@@ -239,13 +239,13 @@ hipError_t launch_decode(const Geometry &G, uint8_t *cache, const uint16_t *q,
                          const uint16_t *kn, const uint16_t *vn, int slot,
                          hipEvent_t ev_before, hipEvent_t ev_after, hipStream_t st) {
     if (slot < 0) kn = vn = q;  // never dereferenced: no window token equals slot -1
+    if (pl.total_splits > kMaxCombine) return hipErrorInvalidValue;  // before any launch
     float *ml = reinterpret_cast<float *>(workspace);
     float *acc = ml + (size_t)G.B * G.Hq * pl.max_splits * 2;
     const hipError_t e =
         G.dtype == F16 ? launch1<F16>(G, cache, kn, vn, slot, q, ml, acc, pl, ev_before, ev_after, st)
                        : launch1<BF16>(G, cache, kn, vn, slot, q, ml, acc, pl, ev_before, ev_after, st);
     if (e != hipSuccess) return e;
-    if (pl.total_splits > kMaxCombine) return hipErrorInvalidValue;
     const int rows = G.B * G.Hq;
     if (pl.total_splits <= 16)
         return launch_combine_wave<16>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st);

@@ -89,10 +89,12 @@ int max_splits_of(const kvq::Geometry &G) {
     return std::min(4 * G.max_pages, kMaxSplits) + kvq::R / 32;
 }
 
-kvq::DecodePlan plan_of(const kvq_cache *c) {
+// Decode plan for the cache's pages and n_res window tokens (the host
+// counter, or one more for a fused step whose token is not yet counted).
+kvq::DecodePlan plan_of(const kvq_cache *c, int n_res) {
     kvq::DecodePlan pl{};
     pl.n_pages = c->n_pages;
-    pl.n_res = c->n_res;
+    pl.n_res = n_res;
     pl.max_splits = max_splits_of(c->G);
     if (c->n_pages > 0) {
         constexpr int NW = kvq::kDecodeWaves;
@@ -118,9 +120,10 @@ kvq::DecodePlan plan_of(const kvq_cache *c) {
         pl.groups_per_split = (groups + S * NW - 1) / (S * NW);  // per wave
         pl.page_splits = (groups + pl.groups_per_split * NW - 1) / (pl.groups_per_split * NW);
     }
-    pl.total_splits = pl.page_splits + (c->n_res + 32 * kvq::kDecodeWaves - 1) / (32 * kvq::kDecodeWaves);
+    pl.total_splits = pl.page_splits + (n_res + 32 * kvq::kDecodeWaves - 1) / (32 * kvq::kDecodeWaves);
     return pl;
 }
+kvq::DecodePlan plan_of(const kvq_cache *c) { return plan_of(c, c->n_res); }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
 
@@ -186,12 +189,14 @@ kvq::PoolPlan pool_plan(const kvq_pool *p, const int *slot_of) {
     pl.win_pref[0] = 0;
     for (int b = 0; b < G.B; b++) {
         const bool on = p->live[b] != 0;
+        // a sequence given a new token (slot_of[b] >= 0) is planned with it
+        const int nres = on ? p->n_res[b] + (slot_of && slot_of[b] >= 0 ? 1 : 0) : 0;
         const int S = on ? (4 * p->n_pages[b] + gps - 1) / gps : 0;
-        const int W = on ? (p->n_res[b] + 31) / 32 : 0;
+        const int W = on ? (nres + 31) / 32 : 0;
         pl.page_pref[b + 1] = pl.page_pref[b] + (uint32_t)(G.Hkv * S);
         pl.win_pref[b + 1] = (uint16_t)(pl.win_pref[b] + G.Hkv * W);
         pl.n_pages[b] = (uint16_t)(on ? p->n_pages[b] : 0);
-        pl.n_res[b] = (uint8_t)(on ? p->n_res[b] : 0);
+        pl.n_res[b] = (uint8_t)nres;
         pl.slot[b] = (uint8_t)(on && slot_of && slot_of[b] >= 0 ? slot_of[b] : kvq::kPoolNoSlot);
     }
     for (int b = G.B; b < kvq::kPoolMaxSeqs; b++) {
@@ -246,6 +251,7 @@ int pool_flush_full(kvq_pool *p, hipStream_t st, int32_t *n) {
 namespace {
 constexpr int64_t kPrefillMaxT = 1 << 20;  // positions of one prefill
 hipEvent_t g_prefill_ev_before = nullptr, g_prefill_ev_after = nullptr;
+int g_prefill_max_key_splits = 0;  // 0 = automatic
 
 size_t prefill_stats_bytes(int32_t T, int32_t Hq) { return align256((size_t)Hq * T * 4); }
 size_t prefill_part_bytes(int32_t T, int32_t Hkv) {
@@ -392,15 +398,16 @@ int kvq_append_decode(kvq_cache *c, const void *k, const void *v, const void *q,
         c->n_pages += 1;
         c->n_res = 0;
     }
-    // the plan and the kernel see the window with the new token in it
+    // the plan and the kernel see the window with the new token in it; the
+    // counter moves only once the launch that writes the token succeeded
     const int slot = c->n_res;
-    c->n_res += 1;
-    kvq::DecodePlan pl = plan_of(c);
+    kvq::DecodePlan pl = plan_of(c, c->n_res + 1);
     hipError_t e = kvq::launch_decode(c->G, c->mem, static_cast<const uint16_t *>(q), out,
                                       workspace, pl, static_cast<const uint16_t *>(k),
                                       static_cast<const uint16_t *>(v), slot, c->ev_before,
                                       c->ev_after, st);
     if (e != hipSuccess) return KVQ_EHIP;
+    c->n_res = slot + 1;
     if (flushed) *flushed = flush ? 1 : 0;
     return KVQ_OK;
 }
@@ -558,7 +565,8 @@ int kvq_prefill_select(int32_t dtype, int32_t T, int32_t num_q_heads, int32_t nu
     a.part = reinterpret_cast<float *>(ws + prefill_stats_bytes(T, num_q_heads));
     a.vt = reinterpret_cast<uint16_t *>(ws + prefill_stats_bytes(T, num_q_heads) +
                                         prefill_part_bytes(T, num_kv_heads));
-    a.nsplit = kvq::prefill_key_splits(T, num_q_heads, num_kv_heads, &a.kbc);
+    a.nsplit = kvq::prefill_key_splits(T, num_q_heads, num_kv_heads, &a.kbc,
+                                       g_prefill_max_key_splits);
     {
         uint8_t *sp = ws + prefill_stats_bytes(T, num_q_heads) + prefill_part_bytes(T, num_kv_heads) +
                       prefill_vt_bytes(T, num_kv_heads);
@@ -576,6 +584,12 @@ int kvq_prefill_select(int32_t dtype, int32_t T, int32_t num_q_heads, int32_t nu
     a.ev_after = g_prefill_ev_after;
     *n_keep = nk;
     return hip_status(kvq::launch_prefill(dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+int kvq_prefill_set_max_key_splits(int32_t n) {
+    if (n < 0 || n > kvq::kPrefillMaxKeySplits) return KVQ_EINVAL;
+    g_prefill_max_key_splits = n;
+    return KVQ_OK;
 }
 
 int kvq_prefill_set_kernel_events(void *before, void *after) {
@@ -751,11 +765,10 @@ int kvq_pool_append_decode(kvq_pool *p, const void *k, const void *v, const void
     int rc = pool_flush_full(p, st, &nf);
     if (rc) return rc;
     // the plan and the kernel see every window with its new token in it
+    // (the host counters move only once the launch that writes the tokens
+    // succeeded)
     int slot_of[kvq::kPoolMaxSeqs];
-    for (int b = 0; b < p->G.B; b++) {
-        slot_of[b] = p->live[b] ? p->n_res[b] : -1;
-        if (p->live[b]) p->n_res[b] += 1;
-    }
+    for (int b = 0; b < p->G.B; b++) slot_of[b] = p->live[b] ? p->n_res[b] : -1;
     const kvq::PoolPlan pl = pool_plan(p, slot_of);
     hipError_t e = kvq::launch_pool_decode(p->G, p->mem, pool_table(p),
                                            static_cast<const uint16_t *>(q), out, workspace, pl,
@@ -763,6 +776,8 @@ int kvq_pool_append_decode(kvq_pool *p, const void *k, const void *v, const void
                                            static_cast<const uint16_t *>(v), p->ev_before,
                                            p->ev_after, st);
     if (e != hipSuccess) return KVQ_EHIP;
+    for (int b = 0; b < p->G.B; b++)
+        if (p->live[b]) p->n_res[b] += 1;
     if (n_flushed) *n_flushed = nf;
     return KVQ_OK;
 }

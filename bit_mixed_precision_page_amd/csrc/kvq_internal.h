@@ -107,13 +107,15 @@ constexpr int kColsumChunks = 16;
 // split, kbc = every block).
 constexpr int kPrefillSplitWgs = 768;     // three attention workgroups per CU
 constexpr int kPrefillMaxKeySplits = 4;
-inline int prefill_key_splits(int T, int Hq, int Hkv, int *kbc) {
+// cap > 0 bounds the chunk count (a caller's override; 0 = automatic).
+inline int prefill_key_splits(int T, int Hq, int Hkv, int *kbc, int cap = 0) {
     const int g = Hq / Hkv, hw = g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
     const int qr = 128 / hw, nb = (T + 31) / 32;
     const long wgs = (long)(Hq / hw) * ((T + qr - 1) / qr);
     int s = 1;
     if (wgs < kPrefillSplitWgs)
         s = (int)std::min<long>(kPrefillMaxKeySplits, (kPrefillSplitWgs + wgs - 1) / wgs);
+    if (cap > 0) s = std::min(s, cap);
     *kbc = (nb + s - 1) / s;
     return (nb + *kbc - 1) / *kbc;
 }

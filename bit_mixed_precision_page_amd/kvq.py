@@ -32,7 +32,8 @@ EXPORTS = ["kvq_cache_bytes", "kvq_page_bytes", "kvq_cache_create", "kvq_cache_d
            "kvq_pool_window_offset", "kvq_pool_table_offset", "kvq_pool_set_kernel_events",
            "kvq_set_channel_relevance", "kvq_query_relevance", "kvq_pool_set_channel_relevance",
            "kvq_device_state_init", "kvq_append_decode_device",
-           "kvq_prefill_workspace_bytes", "kvq_prefill_select", "kvq_prefill_set_kernel_events"]
+           "kvq_prefill_workspace_bytes", "kvq_prefill_select", "kvq_prefill_set_kernel_events",
+           "kvq_prefill_set_max_key_splits"]
 
 
 class KvqError(RuntimeError):
@@ -100,6 +101,7 @@ _SIG = {
     "kvq_pool_table_offset": [_vp, ctypes.POINTER(_sz)],
     "kvq_pool_set_kernel_events": [_vp, _vp, _vp],
     "kvq_prefill_set_kernel_events": [_vp, _vp],
+    "kvq_prefill_set_max_key_splits": [_i32],
     "kvq_set_channel_relevance": [_vp, _vp],
     "kvq_query_relevance": [_i32, _i32, _i32, _i32, _vp, _vp, _vp],
     "kvq_pool_set_channel_relevance": [_vp, _vp],
@@ -404,6 +406,11 @@ def kvq_prefill_set_kernel_events(before, after):
     """Timing hooks around the prefill attention kernel (hipEvent_t values or None)."""
     _check(_L.kvq_prefill_set_kernel_events(_ptr(before), _ptr(after)),
            "kvq_prefill_set_kernel_events")
+
+
+def kvq_prefill_set_max_key_splits(n):
+    """Cap on the prefill's key chunks (1..4), 0 = automatic."""
+    _check(_L.kvq_prefill_set_max_key_splits(n), "kvq_prefill_set_max_key_splits")
 
 
 # -- convenience owner of the device buffers -----------------------------------

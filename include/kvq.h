@@ -363,6 +363,14 @@ int kvq_prefill_select(int32_t dtype, int32_t T, int32_t num_q_heads, int32_t nu
    threads. */
 int kvq_prefill_set_kernel_events(void *before, void *after);
 
+/* Upper bound on the key chunks of kvq_prefill_select (n = 1..4; 0 restores
+   the automatic choice, which splits the keys of a short sequence into up to
+   four chunks so that the attention kernel fills the chip, and merges them).
+   Results agree with the automatic choice up to fp32 summation order; the
+   workspace size does not change.  Process-wide, like the timing hooks.
+   Errors: KVQ_EINVAL (n outside 0..4). */
+int kvq_prefill_set_max_key_splits(int32_t n);
+
 #ifdef __cplusplus
 }
 #endif

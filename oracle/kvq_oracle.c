@@ -187,6 +187,16 @@ void ora_quantize_group(int dt, const uint16_t *x, int n, int stride, int L,
     }
 }
 
+/* n independent groups of glen contiguous values each (group i at
+   x[i * glen]), quantized one after another with the quantizer above: scale
+   and zero of group i in s_out[i], z_out[i], its codes at code[i * glen]. */
+void ora_quantize_groups(int dt, const uint16_t *x, int n, int glen, int L,
+                         uint16_t *s_out, uint16_t *z_out, uint8_t *code) {
+    for (int i = 0; i < n; i++)
+        ora_quantize_group(dt, x + (size_t)i * glen, glen, 1, ORA_PLANT == 22 ? 3 : L, s_out + i,
+                           z_out + i, code + (size_t)i * glen, 1); /* plant: L ignored */
+}
+
 /* ------------------------------------------------------------------------
  * R3: magnitude-ranked channel selection (Kitty abstract; notes.yuuk.io open
  * questions).  K is [ntok][nch] stored values.  boosted[c] = 1 for the k
@@ -617,6 +627,74 @@ int ora_prefill_attention(int dt, int T, int Hq, int Hkv, const uint16_t *q,
         free(Vh);
         free(w);
     }
+    return err;
+}
+
+/* R20: the causal attention output of chosen query positions only, in
+   double precision, for checks of long sequences where the full run costs
+   O(T^2).  rows[0..nrows) are query positions (any order, each < T); out:
+   [Hq][nrows][D] doubles, out[hq][r] = sum over j <= rows[r] of
+   softmax_j(scale q_{hq,rows[r]} . k_j) v_j with the KV head of hq (R12).
+   Each (query head, row) is computed on its own, as one row of the full
+   prefill above. */
+int ora_prefill_rows(int dt, int T, int Hq, int Hkv, const uint16_t *q,
+                     const uint16_t *k, const uint16_t *v, double scale, int nrows,
+                     const int32_t *rows, double *out) {
+    if (T <= 0 || Hkv <= 0 || Hq % Hkv || nrows < 0) return -1;
+    for (int r = 0; r < nrows; r++)
+        if (rows[r] < 0 || rows[r] >= T) return -1;
+    int g = Hq / Hkv;
+    size_t n = (size_t)Hkv * T * D;
+    double *Kd = (double *)malloc(sizeof(double) * n);
+    double *Vd = (double *)malloc(sizeof(double) * n);
+    if (!Kd || !Vd) {
+        free(Kd);
+        free(Vd);
+        return -2;
+    }
+#pragma omp parallel for schedule(static)
+    for (long x = 0; x < (long)n; x++) {
+        Kd[x] = ora_decode(dt, k[x]);
+        Vd[x] = ora_decode(dt, v[x]);
+    }
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long job = 0; job < (long)Hq * nrows; job++) {
+        int hq = (int)(job / nrows), r = (int)(job % nrows);
+        int h = hq / g, i = rows[r];
+        double *w = (double *)malloc(sizeof(double) * (size_t)(i + 1));
+        if (!w) {
+            err = -2;
+            continue;
+        }
+        const uint16_t *qi = q + ((size_t)hq * T + i) * D;
+        const double *Kh = Kd + (size_t)h * T * D, *Vh = Vd + (size_t)h * T * D;
+        double qd[D];
+        for (int c = 0; c < D; c++) qd[c] = ora_decode(dt, qi[c]);
+        int last = ORA_PLANT == 21 ? i - 1 : i; /* plant: the diagonal key left out */
+        double m = -INFINITY;
+        for (int j = 0; j <= last; j++) {
+            double d = 0.0;
+            for (int c = 0; c < D; c++) d += qd[c] * Kh[(size_t)j * D + c];
+            w[j] = scale * d;
+            if (w[j] > m) m = w[j];
+        }
+        double l = 0.0;
+        for (int j = 0; j <= last; j++) {
+            w[j] = exp(w[j] - m);
+            l += w[j];
+        }
+        double o[D];
+        for (int c = 0; c < D; c++) o[c] = 0.0;
+        for (int j = 0; j <= last; j++) {
+            double pr = w[j] / l;
+            for (int c = 0; c < D; c++) o[c] += pr * Vh[(size_t)j * D + c];
+        }
+        for (int c = 0; c < D; c++) out[((size_t)hq * nrows + r) * D + c] = o[c];
+        free(w);
+    }
+    free(Kd);
+    free(Vd);
     return err;
 }
 

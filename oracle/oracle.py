@@ -85,6 +85,10 @@ class OracleLib:
         L.ora_prefill_attention.argtypes = [ctypes.c_int] * 4 + [_u16p, _u16p, _u16p,
                                                                  ctypes.c_double, _f64p, _f64p]
         L.ora_select_tokens.argtypes = [ctypes.c_int, _f64p, ctypes.c_int, ctypes.c_int, _i32p]
+        L.ora_quantize_groups.argtypes = [ctypes.c_int, _u16p, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, _u16p, _u16p, _u8p]
+        L.ora_prefill_rows.argtypes = [ctypes.c_int] * 4 + [_u16p, _u16p, _u16p, ctypes.c_double,
+                                                            ctypes.c_int, _i32p, _f64p]
         self.L = L
 
     # -- stored dtypes -----------------------------------------------------
@@ -108,6 +112,18 @@ class OracleLib:
         self.L.ora_quantize_group(dt, _ptr(x, _u16p), n, 1, L, _ptr(s, _u16p),
                                   _ptr(z, _u16p), _ptr(codes, _u8p), 1)
         return int(s[0]), int(z[0]), codes
+
+    def quantize_groups(self, dt, x_bits, L):
+        """n groups of glen values (x_bits [n][glen] u16), each quantized on its
+        own (R2) -> (scales [n] u16, zeros [n] u16, codes [n][glen] u8)."""
+        x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        n, glen = x.shape
+        s = np.zeros(n, np.uint16)
+        z = np.zeros(n, np.uint16)
+        codes = np.zeros((n, glen), np.uint8)
+        self.L.ora_quantize_groups(dt, _ptr(x, _u16p), n, glen, L, _ptr(s, _u16p),
+                                   _ptr(z, _u16p), _ptr(codes, _u8p))
+        return s, z, codes
 
     def select_channels(self, K_bits, k):
         K = np.ascontiguousarray(K_bits, dtype=np.uint16)
@@ -247,6 +263,25 @@ class OracleLib:
         if rc:
             raise ValueError(f"ora_prefill_attention failed ({rc})")
         return out, score
+
+    def prefill_rows(self, dt, q, k, v, scale, rows):
+        """Causal prefill attention output of the query positions `rows` only
+        (R20): q [Hq][T][D], k, v [Hkv][T][D] u16 -> out [Hq][len(rows)][D]
+        float64."""
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        k = np.ascontiguousarray(k, dtype=np.uint16)
+        v = np.ascontiguousarray(v, dtype=np.uint16)
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+        Hq, T, d = q.shape
+        Hkv = k.shape[0]
+        assert d == D and k.shape == (Hkv, T, D) and v.shape == k.shape
+        out = np.empty((Hq, len(rows), D), np.float64)
+        rc = self.L.ora_prefill_rows(dt, T, Hq, Hkv, _ptr(q, _u16p), _ptr(k, _u16p),
+                                     _ptr(v, _u16p), float(scale), len(rows), _ptr(rows, _i32p),
+                                     _ptr(out, _f64p))
+        if rc:
+            raise ValueError(f"ora_prefill_rows failed ({rc})")
+        return out
 
     def select_tokens(self, score, heavy, recent):
         """R22: kept positions (ascending) of one KV head's scores [T]."""

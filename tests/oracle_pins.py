@@ -152,6 +152,25 @@ def pin_quantizer_progression(ora):
                 assert (codes == perm).all(), "progression must quantize to its index"
 
 
+def pin_quantizer_groups_batched(ora):
+    """The batched quantizer (one call over many groups) returns, for every
+    group, what the single-group quantizer returns, and its codes keep the
+    round-trip invariant."""
+    r = np.random.default_rng(5)
+    for dt in (F16, BF16):
+        for L in (3, 15):
+            n, glen = 200, 9
+            scale = np.exp(r.uniform(-8, 8, size=(n, 1)))
+            x = _bits(dt, (r.standard_normal((n, glen)) * scale).astype(np.float32))
+            s, z, codes = ora.quantize_groups(dt, x, L)
+            assert codes.max() <= L
+            for i in range(n):
+                so, zo, co = ora.quantize_group(dt, x[i], L)
+                assert s[i] == so and z[i] == zo and (codes[i] == co).all(), (dt, L, i)
+                xv, sf, zf = _val(dt, x[i]), _val(dt, [s[i]])[0], _val(dt, [z[i]])[0]
+                assert (np.abs(xv - (codes[i] * sf + zf)) <= _roundtrip_bound(sf, xv - zf)).all()
+
+
 def pin_quantizer_golden(ora):
     fx = json.load(open(os.path.join(GOLDEN, "quantizer_worked.json")))
     for g in fx["groups"]:
@@ -551,6 +570,22 @@ def pin_prefill_attention_sdpa(ora):
         out, _ = ora.prefill_attention(dt, q, k, v, scale)
         ref = _causal_sdpa(_val(dt, q), _val(dt, k), _val(dt, v), Hq // Hkv, scale)
         assert np.abs(out - ref).max() < 1e-12, (dt, Hq, Hkv, T)
+
+
+def pin_prefill_rows(ora):
+    """Chosen query rows of the causal attention equal the rows of torch fp64
+    causal SDPA (library routine) and of the full oracle run, including the
+    first row (one key) and the last."""
+    r = np.random.default_rng(75)
+    for dt, Hq, Hkv, T in [(BF16, 4, 2, 61), (F16, 3, 1, 9)]:
+        q, k, v = _prefill_inputs(r, dt, Hq, Hkv, T, kscale=2.0)
+        scale = 1.0 / np.sqrt(D)
+        rows = np.array([T - 1, 0, T // 2, 1, T - 2], np.int32)
+        got = ora.prefill_rows(dt, q, k, v, scale, rows)
+        ref = _causal_sdpa(_val(dt, q), _val(dt, k), _val(dt, v), Hq // Hkv, scale)
+        assert np.abs(got - ref[:, rows]).max() < 1e-12, (dt, Hq, Hkv, T)
+        full, _ = ora.prefill_attention(dt, q, k, v, scale)
+        assert np.abs(got - full[:, rows]).max() < 1e-12
 
 
 def pin_prefill_score_total(ora):

@@ -316,3 +316,13 @@ def test_prefill_workspace_covers_the_key_split():
     # 8192 tokens: 2048 workgroups, no split, no partials
     ws = kvq.kvq_prefill_workspace_bytes(8192, 32, 8)
     assert base(8192, 32, 8) <= ws < base(8192, 32, 8) + 4 * 256
+
+
+def test_prefill_key_split_cap_checks(kvq):
+    """kvq_prefill_set_max_key_splits accepts 0 (automatic) to 4 and rejects
+    anything else without changing the setting."""
+    for n in (-1, 5, 100):
+        with pytest.raises(kvq.KvqError):
+            kvq.kvq_prefill_set_max_key_splits(n)
+    for n in (1, 4, 0):
+        kvq.kvq_prefill_set_max_key_splits(n)

@@ -45,6 +45,24 @@ def _run(w, T, heavy, recent, scale=0.0, check_oracle_rows=None):
         host(v_sel).view(np.uint16)
 
 
+def _late_rows(T, last=128, spread=64):
+    """The last `last` query positions plus `spread` positions spread over the
+    sequence: rows that see many 32-key blocks and many online-softmax
+    rescale events."""
+    rows = set(range(max(0, T - last), T)) | set(np.linspace(0, T - 1, spread).astype(int).tolist())
+    return np.array(sorted(rows), np.int32)
+
+
+def _check_rows(w, q, k, v, out_rows, rows, scale=None):
+    """GPU output rows (out_rows [Hq][len(rows)][D]) against the oracle's fp64
+    causal attention of the same query positions."""
+    sc = 1.0 / np.sqrt(128) if scale is None else scale
+    ref = oracle.lib().prefill_rows(w.dtype, q, k, v, sc, rows)
+    err = np.abs(out_rows - ref).max()
+    assert np.isfinite(out_rows).all()
+    return err
+
+
 def _check(w, T, heavy, recent, scale=0.0):
     ora = oracle.lib()
     q, k, v, out, score, keep, k_sel, v_sel = _run(w, T, heavy, recent, scale)
@@ -100,6 +118,22 @@ def test_prefill_selection_edges():
     _check(w, 64, heavy=64, recent=0, scale=0.2)  # explicit scale
 
 
+@pytest.mark.parametrize("cap", [1, 2])
+def test_prefill_forced_key_splits(cap):
+    """Short sequences normally take the key-split path; with the chunk count
+    capped at 1 the unsplit multi-block path (lazy rescale over many 32-key
+    blocks) runs, and with 2 a two-chunk split: every output row, score and
+    kept position against the oracle."""
+    from bit_mixed_precision_page_amd import kvq
+    w = dataclasses.replace(W["llama3_8b_prefill_select"], Hq=8, Hkv=2)
+    kvq.kvq_prefill_set_max_key_splits(cap)
+    try:
+        for T in (300, 777):
+            _check(w, T, heavy=T // 4, recent=T // 4)
+    finally:
+        kvq.kvq_prefill_set_max_key_splits(0)
+
+
 def test_prefill_selected_rows_quantize_like_the_oracle():
     """The kept rows (two full pages here) go through kvq_quantize_page: page
     bytes bit-exact with the oracle's pages of the same rows."""
@@ -123,9 +157,10 @@ def test_prefill_selected_rows_quantize_like_the_oracle():
 def test_prefill_full_size_sampled():
     """The benchmark shape (one Llama-3-8B-shaped sequence of 8192 tokens): rows
     0..383 against the oracle run on the first 384 positions (causal: those
-    rows see nothing later), the last key's score against its single softmax
-    probability per head, score totals, and the selection rule on the GPU's
-    scores."""
+    rows see nothing later), the last 128 rows and 64 rows spread over the
+    sequence (every query head) against the oracle's rows, the last key's
+    score against its single softmax probability per head, score totals, and
+    the selection rule on the GPU's scores."""
     from bit_mixed_precision_page_amd import kvq
     w = W["llama3_8b_prefill_select"]
     T = w.ctx
@@ -139,6 +174,11 @@ def test_prefill_full_size_sampled():
     T0 = 384
     o_ref, _ = ora.prefill_attention(w.dtype, q[:, :T0], k[:, :T0], v[:, :T0], 1.0 / np.sqrt(128))
     err = np.abs(out[:, :T0] - o_ref).max()
+    rows = _late_rows(T)
+    rerr = _check_rows(w, q, k, v, out[:, rows], rows)
+    say(f"    full size: {len(rows)} late and spread rows of every query head "
+        f"|out - oracle| = {rerr:.2e}")
+    assert rerr <= TOL
     g = w.Hq // w.Hkv
     qf = gen.from_bits(q[:, T - 1], w.dtype).astype(np.float64)
     kf = gen.from_bits(k, w.dtype).astype(np.float64)
@@ -161,7 +201,8 @@ def test_prefill_full_size_sampled():
 
 def test_prefill_long_sequence_sampled():
     """A 65536-token sequence (two KV heads, eight query heads): the first 256
-    rows against the oracle, the last key's score against its softmax
+    rows, the last 128 rows and 64 rows spread over the sequence against the
+    oracle, the last key's score against its softmax
     probabilities, the score totals, and the selection rule on the GPU scores
     (many query chunks, every tile count of the score pass past its first)."""
     from bit_mixed_precision_page_amd import kvq
@@ -174,11 +215,16 @@ def test_prefill_long_sequence_sampled():
     torch.cuda.synchronize()
     score, keep = host(score), host(keep)
     out0 = host(out[:, :256])
+    rows = _late_rows(T)
+    out_rows = host(out[:, torch.from_numpy(rows.astype(np.int64)).cuda()])
     del out, k_sel, v_sel
     ora = oracle.lib()
     T0 = 256
     o_ref, _ = ora.prefill_attention(w.dtype, q[:, :T0], k[:, :T0], v[:, :T0], 1.0 / np.sqrt(128))
     err = np.abs(out0 - o_ref).max()
+    rerr = _check_rows(w, q, k, v, out_rows, rows)
+    say(f"    T={T}: {len(rows)} late and spread rows |out - oracle| = {rerr:.2e}")
+    assert rerr <= TOL
     g = w.Hq // w.Hkv
     qf = gen.from_bits(q[:, T - 1], w.dtype).astype(np.float64)
     kf = gen.from_bits(k, w.dtype).astype(np.float64)

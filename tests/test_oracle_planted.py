@@ -30,6 +30,8 @@ PLANTS = {
     18: "cumulative scores summed before the softmax normalization",
     19: "token selection ties to the higher position",
     20: "recent window one position short",
+    21: "prefill rows without the diagonal key",
+    22: "batched quantizer ignores the level count",
 }
 
 
