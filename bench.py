@@ -4,16 +4,21 @@
 One step = one decode step of one attention layer: append the new token's K
 and V into the window (flushing a full window into a page when needed) and
 run split-K decode attention of the new query over the whole cache, through
-the fused kvq_append_decode entry point (--unfused: the two separate calls).  Layers
-rotate over enough independent cache replicas (>= 1 GiB) that every step
-reads its cache from HBM, not from the 256 MB Infinity Cache.  Inputs are
-seeded synthetic tensors of the workload's shape, resident in HBM before the
-timed region.
+the fused kvq_append_decode entry point (--unfused: the two separate calls).
+Layers rotate over enough independent cache replicas (>= 1 GiB) that every
+step reads its cache from HBM, not from the 256 MB Infinity Cache; the
+replicas' window fills are staggered so that they flush one at a time, at
+the steady-state rate of one flush per 128 steps, whatever the step count.
+Inputs are seeded synthetic tensors of the workload's shape, resident in HBM
+before the timed region.
 
 Prints one JSON line: value = algorithmic bytes moved by the timed steps /
-elapsed time (GB/s); roofline = the split decode kernel's algorithmic bytes
-per launch / its average launch time (HIP events around each launch); and
-cpu_baseline = the CPU oracle timed on one full decode-attention call.
+elapsed time (GB/s); step_us = per-step percentiles (from the split kernel's
+own dispatch timestamps on a second run of as many steps), flush steps apart;
+graph_step_us = the same step replayed from a captured HIP graph; roofline =
+the split decode kernel's algorithmic bytes per launch / its average launch
+time; copy_gbs = a measured 1 GiB device copy; cpu_baseline = the CPU oracle
+on the same cache.
 """
 import argparse
 import json
@@ -49,8 +54,17 @@ def parse():
                          "kvq_append_decode, same results)")
     ap.add_argument("--event-fence", action="store_true",
                     help="events with the default system-scope fence (slower markers)")
+    ap.add_argument("--ctx", type=int, default=0,
+                    help="decode workloads: context length in tokens, a multiple of 128 "
+                         "(0 = the workload's)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="decode workloads: every replica starts with this many window tokens "
+                         "(1..128) instead of the staggered fills")
     ap.add_argument("--tokens", type=int, default=0,
                     help="prefill selection workload: sequence length (0 = the workload's)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip the graph-replayed step (kvq_append_decode_device captured once "
+                         "per layer replica)")
     ap.add_argument("--query-aware", action="store_true",
                     help="rank Key channels by group range x query relevance (relevance of "
                          "the first decode query) instead of magnitude")
@@ -118,6 +132,62 @@ class HipEvents:
         return ms.value
 
 
+def staggered_windows(L):
+    """Window fill of layer replica i when the timed steps start, spread
+    evenly over 1..128 and centred away from a flush: the replicas then flush
+    one at a time, about every 128 steps (the steady-state rate), whatever
+    the number of timed steps."""
+    return [max(1, 128 - (128 * i + 64) // L) for i in range(L)]
+
+
+def copy_bandwidth(torch, dev, nbytes, reps=5):
+    """Device-to-device copy of nbytes: read + written bytes / time (GB/s),
+    the best of `reps` copies."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    return 2 * nbytes / (best / 1e3) / 1e9
+
+
+def read_bandwidth(torch, dev, nbytes, reps=5):
+    """Read-only stream of nbytes (a float32 sum of a 1 GiB tensor): bytes /
+    time (GB/s), the best of `reps` -- the bandwidth a kernel that only reads
+    can reach, beside the copy's read + write."""
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    x.sum()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        x.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del x
+    return nbytes / (best / 1e3) / 1e9
+
+
+def pctl(x):
+    x = np.asarray(x, dtype=np.float64)
+    if x.size == 0:
+        return None
+    return {"p10": round(float(np.percentile(x, 10)), 2), "p50": round(float(np.median(x)), 2),
+            "p90": round(float(np.percentile(x, 90)), 2), "n": int(x.size)}
+
+
+def dtype_name(gen, w):
+    return "bf16" if w.dtype == gen.BF16 else "f16"
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -131,6 +201,11 @@ def main():
     from bit_mixed_precision_page_amd import kvq
 
     w = gen.WORKLOADS[a.workload]
+    if a.ctx:
+        if a.ctx % PAGE or a.ctx < 2 * PAGE:
+            raise SystemExit("--ctx must be a multiple of 128 and at least 256")
+        import dataclasses
+        w = dataclasses.replace(w, ctx=a.ctx)
     if w.decode_steps:
         return stream_main(a, w, torch, gen, kvq)
     if w.ctx_spread:
@@ -146,12 +221,14 @@ def main():
     t0 = time.time()
     print(f"[bench] workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} ctx={w.ctx} k={w.boost}",
           file=sys.stderr, flush=True)
-    # Cache state: (ctx/128 - 1) bulk pages + 127 window tokens, so that the
-    # first timed append brings every layer to exactly ctx tokens.
+    # Cache state: (ctx/128 - 1) bulk pages + a full window of 128 tokens;
+    # replica i starts its timed steps with the first n_i of those window
+    # tokens (staggered_windows), so the layers reach ctx tokens one after
+    # another and flush one at a time.
     bulk = w.ctx // PAGE - 1
-    n_win = PAGE - 1
+    n_win = PAGE
     K, V = gen.prefill_kv(w, ntok=bulk * PAGE + n_win)
-    steps_total = a.warmup + a.steps
+    steps_total = a.warmup + 2 * a.steps
     max_pages = w.ctx // PAGE + 1 + (steps_total // PAGE + 2)
     cfg = kvq.config(w.B, w.Hq, w.Hkv, w.boost, max_pages, w.dtype)
     base = kvq.Cache(cfg, device=dev)
@@ -163,13 +240,21 @@ def main():
     torch.cuda.synchronize()
     del Kd, Vd
     n_pages0, n_res0 = base.state
-    layers = max(2, math.ceil(a.rotate_bytes / base.nbytes))
-    caches = [base]
-    for _ in range(layers - 1):
-        c = kvq.Cache(cfg, device=dev)
-        c.mem.copy_(base.mem)
-        kvq.kvq_set_state(c.handle, n_pages0, n_res0)
-        caches.append(c)
+    assert (n_pages0, n_res0) == (bulk, n_win)
+    # (never more replicas than timed steps: a tiny cache is launch-bound anyway)
+    layers = min(max(2, math.ceil(a.rotate_bytes / base.nbytes)), max(2, a.steps))
+    caches = [base] + [kvq.Cache(cfg, device=dev) for _ in range(layers - 1)]
+    snap = base.mem.clone()
+    wins = [a.window] * layers if a.window else staggered_windows(layers)
+
+    def restore():
+        """Every replica back to the staggered starting state."""
+        for c, n in zip(caches, wins):
+            c.mem.copy_(snap)
+            kvq.kvq_set_state(c.handle, n_pages0, n)
+        torch.cuda.synchronize()
+
+    restore()
     if a.splits:
         for c in caches:
             kvq.kvq_set_decode_splits(c.handle, a.splits)
@@ -184,13 +269,13 @@ def main():
     timed = [i for i in range(a.steps) if a.event_every > 0 and i % a.event_every == 0]
     hev = HipEvents(len(timed), a.event_fence)
     ev_of = {i: hev.pair(j) for j, i in enumerate(timed)}
+    hall = HipEvents(a.steps, a.event_fence)  # every step's split kernel (distribution phase)
     torch.cuda.synchronize()
     print(f"[bench] setup {time.time() - t0:.1f}s; {layers} layer replicas of "
           f"{base.nbytes / 1e6:.1f} MB (replica bytes {base.nbytes}); state {n_pages0} pages + "
-          f"{n_res0} window", file=sys.stderr, flush=True)
+          f"windows {wins}", file=sys.stderr, flush=True)
 
     pb = base.page_bytes
-    state = [list(c.state) for c in caches]
 
     def step(s, ev=None):
         li = s % layers
@@ -210,6 +295,10 @@ def main():
     for s in range(a.warmup):
         step(s)
     torch.cuda.synchronize()
+    restore()  # warm-up steps leave no trace in the timed state
+
+    # -- phase 1 (headline): K steps between two events; the split kernel's
+    # own dispatch timestamps on every event_every-th step give its duration
     total_bytes = 0
     attn_bytes_sum = 0
     split_bytes = []
@@ -218,7 +307,7 @@ def main():
     start.record()
     t_host = time.perf_counter()
     for i in range(a.steps):
-        s = a.warmup + i
+        s = i  # layer i % layers at its (i // layers)-th visit
         flushed, n_pages, n_res = step(s, ev_of.get(i))
         ab = attention_bytes(w, pb, n_pages, n_res)
         attn_bytes_sum += ab
@@ -241,6 +330,62 @@ def main():
           f"split kernel avg {kern_avg_s * 1e6:.1f} us over {len(timed)} launches, "
           f"{n_flush} flushes; host {host_us:.1f} us/step to launch)", file=sys.stderr, flush=True)
 
+    # -- phase 2 (distribution): the next K steps with every split kernel's
+    # dispatch timestamps; a step = from one split kernel's start to the
+    # next's (its combine, and the next step's flush when there is one)
+    flush_at = []
+    for i in range(a.steps):
+        s = a.steps + i
+        f, _, _ = step(s, hall.pair(i))
+        flush_at.append(bool(f))
+    torch.cuda.synchronize()
+    kern_all = np.array([hall.elapsed_ms(j) for j in range(a.steps)]) * 1e3
+    gaps = []
+    for i in range(a.steps - 1):
+        ms_i = hall.ct.c_float()
+        hall.hip.hipEventElapsedTime(hall.ct.byref(ms_i), hall.ev[2 * i], hall.ev[2 * (i + 1)])
+        gaps.append(ms_i.value * 1e3)
+    gaps = np.array(gaps)
+    fl = np.array(flush_at[1:])  # interval i holds the flush of step i + 1
+    # (the timestamps themselves widen each step a little: "mean" beside
+    # ms_per_step shows by how much)
+    step_dist = {"from": "split kernel start to the next step's start, per-step dispatch "
+                         "timestamps", "mean": round(float(gaps.mean()), 2),
+                 "non_flush": pctl(gaps[~fl]), "flush": pctl(gaps[fl]),
+                 "split_kernel": pctl(kern_all[~np.array(flush_at)])}
+
+    # -- graph-replayed step (kvq_append_decode_device captured once per
+    # layer replica): the launch-floor comparison
+    graph_us = None
+    if not a.unfused and a.graph:
+        restore()
+        sts = [c.device_state() for c in caches]
+        side = torch.cuda.Stream()
+        graphs = []
+        for li, c in enumerate(caches):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                c.append_decode_device(kts[li % steps_total], vts[li % steps_total],
+                                       qs[li % steps_total], out, sts[li])
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for li in range(layers):  # one untimed replay each
+            graphs[li].replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for i in range(a.steps):
+            graphs[i % layers].replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_us = g0.elapsed_time(g1) / a.steps * 1e3
+        err_flags = [int(x.cpu()[3]) for x in sts]
+        assert not any(err_flags), "a graph-replayed step found its cache full"
+        print(f"[bench] graph-replayed steps: {graph_us:.1f} us/step", file=sys.stderr, flush=True)
+
+    copy_gbs = copy_bandwidth(torch, dev, 1 << 30)
+    read_gbs = read_bandwidth(torch, dev, 1 << 30)
+
     cpu = None
     if not a.no_cpu_baseline:
         import oracle
@@ -249,8 +394,6 @@ def main():
         oc.quantize_pages(K[:, :, :bulk * PAGE], V[:, :, :bulk * PAGE])
         for t in range(n_win):
             oc.append(K[:, :, bulk * PAGE + t], V[:, :, bulk * PAGE + t])
-        kt, vt = gen.step_kv(w, 0)
-        oc.append(kt, vt)
         q0 = gen.query(w, step=0)
         # repeated full decode-attention calls until ~10 s of CPU work
         tc = time.time()
@@ -270,20 +413,27 @@ def main():
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype_name(gen, w), "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": 128, "ctx": w.ctx, "boost_channels": w.boost,
                    "key_group": 32, "value_group": 32, "window": 128,
-                   "storage": "2-bit K/V pages + bf16 window",
-                   "layers_rotated": layers, "page_splits": splits,
+                   "storage": f"2-bit K/V pages + {dtype_name(gen, w)} window",
+                   "accumulate": "f32", "layers_rotated": layers, "page_splits": splits,
                    "step": "append + attention, " + ("two calls" if a.unfused else "fused")},
         "tokens_per_s": round(w.B / (ms_step / 1e3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "attention_gbs": round(attn_gbs, 2),
+        "flushes": n_flush,
+        "step_us": step_dist,
+        "graph_step_us": round(graph_us, 2) if graph_us else None,
+        "copy_gbs": round(copy_gbs, 1),
+        "pct_copy_bw": round(100.0 * achieved / copy_gbs, 2),
+        "read_gbs": round(read_gbs, 1),
+        "pct_read_bw": round(100.0 * achieved / read_gbs, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "kernel_us": round(kern_avg_s * 1e6, 2), "traffic": traffic},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -305,7 +455,8 @@ def stream_main(a, w, torch, gen, kvq):
           f"{w.decode_steps} decode steps", file=sys.stderr, flush=True)
     K, V = gen.prefill_kv(w, ntok=bulk * PAGE)
     Kd, Vd = to_dev(K), to_dev(V)
-    del K, V
+    if a.no_cpu_baseline:
+        del K, V
     cfg = kvq.config(w.B, w.Hq, w.Hkv, w.boost, w.max_pages, w.dtype)
     scratch = kvq.Cache(cfg, device=dev)
     base = kvq.Cache(cfg, device=dev)
@@ -349,35 +500,50 @@ def stream_main(a, w, torch, gen, kvq):
     out = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device=dev)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(w.decode_steps)]
+    # the split kernel's own dispatch timestamps on layer 0 of every step
+    hev = HipEvents(w.decode_steps, a.event_fence)
     torch.cuda.synchronize()
     flush_step = None
-    bytes_steps = []
+    bytes_steps, split_bytes = [], []
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(w.decode_steps):
         evs[i][0].record()
-        for c in caches:
+        for li, c in enumerate(caches):
+            if li == 0:
+                kvq.kvq_set_kernel_events(c.handle, *hev.pair(i))
             if a.unfused:
                 flushed = c.append_token(kts[i], vts[i])
                 c.decode_attention(qs[i], out)
             else:
                 flushed = c.append_decode(kts[i], vts[i], qs[i], out)
+            if li == 0:
+                kvq.kvq_set_kernel_events(c.handle, None, None)
         evs[i][1].record()
         if flushed:
             flush_step = i + 1
         n_pages, n_res = caches[0].state
-        bytes_steps.append(attention_bytes(w, pb, n_pages, n_res) + append_bytes(w, pb, flushed))
+        ab = attention_bytes(w, pb, n_pages, n_res)
+        bytes_steps.append(ab + append_bytes(w, pb, flushed))
+        split_bytes.append(ab - w.B * w.Hq * 128 * 4)  # pages + window + query
     end.record()
     torch.cuda.synchronize()
     step_ms = np.array([x.elapsed_time(y) for x, y in evs]) / layers  # per layer step
     total_ms = start.elapsed_time(end)
     value = float(np.sum(bytes_steps)) * layers / (total_ms / 1e3) / 1e9
+    kern_s = np.array([hev.elapsed_ms(i) for i in range(w.decode_steps)]) / 1e3
+    achieved = float(np.mean(np.array(split_bytes) / kern_s)) / 1e9
+    print(f"[bench] {w.decode_steps} steps x {layers} layers in {total_ms:.3f} ms; split kernel "
+          f"{kern_s.mean() * 1e6:.1f} us mean ({achieved:.0f} GB/s)", file=sys.stderr, flush=True)
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = stream_cpu_baseline(w, gen, K, V, pb)
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": w.decode_steps, "warmup": 0,
         "ms_per_step": round(total_ms / w.decode_steps / layers, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype_name(gen, w), "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": 128, "ctx": bulk * PAGE, "decode_steps": w.decode_steps,
                    "boost_channels": w.boost, "layers_rotated": layers,
@@ -392,9 +558,44 @@ def stream_main(a, w, torch, gen, kvq):
                     if flush_step else None},
         "prefill_quantize": {"pages": units * bulk, "ms": round(q_ms, 3),
                              "gbs": round((q_in + q_out) / (q_ms / 1e3) / 1e9, 1)},
-        "cpu_baseline": None,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "kernel_us": round(float(kern_s.mean()) * 1e6, 2),
+                     "traffic": pmc_traffic("decode_split_kernel", w.name)},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def stream_cpu_baseline(w, gen, K, V, pb):
+    """The oracle on the long-context stream: its own quantization of the
+    prefill pages (timed, reported beside), then the decode steps' appends
+    with decode attention timed at steps 1, 128, 129 (after the flush) and
+    256, in fp64 on the host cores."""
+    import oracle
+    ora = oracle.lib()
+    oc = oracle.OracleCache(w.dtype, w.B, w.Hq, w.Hkv, w.boost, w.max_pages)
+    tq = time.time()
+    oc.quantize_pages(K, V)
+    tq = time.time() - tq
+    units = w.B * w.Hkv
+    q_bytes = units * w.prefill_pages * (PAGE * 128 * 2 * 2 + pb)
+    at_bytes, at_s = 0, 0.0
+    for s in range(1, w.decode_steps + 1):
+        kt, vt = gen.step_kv(w, s)
+        oc.append(kt, vt)
+        if s in (1, 128, 129, 256):
+            q = gen.query(w, step=s)
+            tc = time.time()
+            oc.attention(q)
+            at_s += time.time() - tc
+            at_bytes += attention_bytes(w, pb, oc.n_pages, oc.n_res)
+    return {"value": round(at_bytes / at_s / 1e9, 4), "unit": "GB/s", "cores": ora.num_threads(),
+            "kind": "oracle",
+            "sample": (f"fp64 decode attention at steps 1, 128, 129, 256 ({units} units of "
+                       f"{w.prefill_pages}-{w.prefill_pages + 1} pages + window) in {at_s:.1f} s"),
+            "quantize": {"gbs": round(q_bytes / tq / 1e9, 4),
+                         "sample": f"{units * w.prefill_pages} prefill pages in {tq:.1f} s"}}
 
 
 def prefill_flops(T, Hq):
@@ -511,6 +712,38 @@ def prefill_main(a, w, torch, gen, kvq):
     print(json.dumps(rec_), flush=True)
 
 
+def pool_cpu_baseline(w, gen, lengths, pb):
+    """The oracle's fp64 decode attention over the batch's sequences, one at a
+    time (each with its own page count and window, the oracle's own pages),
+    until ~10 s of attention work."""
+    import oracle
+    ora = oracle.lib()
+    at_bytes, at_s, done = 0, 0.0, 0
+    q_all = gen.query(w, step=0)
+    for b, n in enumerate(lengths):
+        K = np.empty((1, w.Hkv, n, 128), np.uint16)
+        V = np.empty_like(K)
+        for h in range(w.Hkv):
+            K[0, h], V[0, h] = gen.unit_kv(w, b, h, n)
+        n_pages = n // PAGE
+        oc = oracle.OracleCache(w.dtype, 1, w.Hq, w.Hkv, w.boost, max(n_pages, 1))
+        if n_pages:
+            oc.quantize_pages(K[:, :, :n_pages * PAGE], V[:, :, :n_pages * PAGE])
+        for t in range(n_pages * PAGE, n):
+            oc.append(K[:, :, t], V[:, :, t])
+        tc = time.time()
+        oc.attention(q_all[b:b + 1])
+        at_s += time.time() - tc
+        at_bytes += w.Hkv * (oc.n_pages * pb + oc.n_res * 2 * 128 * 2) + w.Hq * 128 * (2 + 4)
+        done += 1
+        if at_s > 10.0:
+            break
+    return {"value": round(at_bytes / at_s / 1e9, 4), "unit": "GB/s", "cores": ora.num_threads(),
+            "kind": "oracle",
+            "sample": (f"fp64 decode attention of {done} of the {len(lengths)} sequences "
+                       f"({sum(lengths[:done])} tokens) in {at_s:.1f} s")}
+
+
 def pool_main(a, w, torch, gen, kvq):
     """A variable-length batch in the block pool: every sequence prefilled
     with its own length (pages in pool blocks, the tail in its window), then
@@ -617,7 +850,7 @@ def pool_main(a, w, torch, gen, kvq):
         "metric": METRIC + " (variable-length batch, block pool)", "value": round(value, 2),
         "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": dtype_name(gen, w), "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": 128, "lengths": lengths, "boost_channels": w.boost,
                    "layers_rotated": layers, "step": "append + attention, fused (pool)"},
@@ -626,7 +859,7 @@ def pool_main(a, w, torch, gen, kvq):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": pmc_traffic("pool_split_kernel", w.name)},
-        "cpu_baseline": None,
+        "cpu_baseline": None if a.no_cpu_baseline else pool_cpu_baseline(w, gen, lengths, pb),
     }
     print(json.dumps(rec), flush=True)
 

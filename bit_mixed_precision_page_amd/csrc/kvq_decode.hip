@@ -41,14 +41,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     }
     const int n_units = gridDim.x / (page_splits + win_splits);
     int unit, split;
-    if ((int)blockIdx.x < page_splits * n_units) {
-        unit = blockIdx.x / page_splits;
-        split = blockIdx.x % page_splits;
-    } else {
-        const int l = blockIdx.x - page_splits * n_units;
-        unit = l / win_splits;
-        split = page_splits + l % win_splits;
-    }
+    dense_split_of(blockIdx.x, n_units, page_splits, win_splits, &unit, &split);
     split_body<DT, G, KH, false, kDecodeWaves>(cache, window_w, knew, vnew, slot, q, ws_ml, ws_acc, Hkv,
                                  max_pages, page_bytes, k, res_base, n_pages, n_res, page_splits,
                                  gps, max_splits, qscale, unit, split, nullptr);

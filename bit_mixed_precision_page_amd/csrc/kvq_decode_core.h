@@ -1,11 +1,13 @@
 // kvq_decode_core.h -- device code of the split-K GQA decode attention over
 // the packed cache (gfx950), shared by the dense cache and the block pool.
 //
-// Grid (split, KV head, sequence); one 64-lane wave per workgroup.  A page
-// split streams its pages one 32-token Key group at a time (two 16-token
-// tiles): while a group is computed, the next group's codes and metadata
-// (about 3.2 KB) are already in flight in a second register set, so a wave
-// needs few registers and four waves share each SIMD.
+// A split of one (sequence, KV head) unit is a workgroup of one wave (block
+// pool) or four (dense cache: one per SIMD, their partials merged in LDS);
+// the kernels map their 1-D grids onto (unit, split).  Each wave of a page
+// split streams its run of 32-token Key groups (two 16-token tiles): while a
+// group is computed, the next group's codes and metadata (about 3.2 KB) are
+// already in flight in a second register set, so a wave needs few registers
+// and four waves share each SIMD.
 //
 //  QK  (16 rows of weights) x (32 channels x 16 tokens) per MFMA.  The B
 //      operand is the 2-bit Key code itself: masking a packed word (or the
@@ -53,7 +55,7 @@ namespace kvq {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMaxCombine = 272;  // splits one combine workgroup merges (>= 256 + 4 window splits)
+constexpr int kMaxCombine = kMaxCombineSplits;  // >= 256 page + 4 window splits
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
@@ -350,7 +352,7 @@ __device__ __forceinline__ void split_body(
     auto put_acc = [&](int hh, int c, float v) {
         if constexpr (NW == 1) {
             const size_t bq = (size_t)b * Hq + h * G + hh;
-            ws_acc[(bq * max_splits + split) * D + c] = v;
+            ws_acc[partial_index(bq, max_splits, split) * D + c] = v;
         } else {
             mine[hh * (D + 2) + c] = v;
         }
@@ -358,8 +360,8 @@ __device__ __forceinline__ void split_body(
     auto put_ml = [&](int hh, float m, float l) {
         if constexpr (NW == 1) {
             const size_t bq = (size_t)b * Hq + h * G + hh;
-            ws_ml[(bq * max_splits + split) * 2 + 0] = m;
-            ws_ml[(bq * max_splits + split) * 2 + 1] = l;
+            ws_ml[partial_index(bq, max_splits, split) * 2 + 0] = m;
+            ws_ml[partial_index(bq, max_splits, split) * 2 + 1] = l;
         } else {
             mine[hh * (D + 2) + D] = m;
             mine[hh * (D + 2) + D + 1] = l;
@@ -387,10 +389,10 @@ __device__ __forceinline__ void split_body(
                     }
                 }
                 const size_t bq = (size_t)b * Hq + h * G + hh;
-                ws_acc[(bq * max_splits + split) * D + c] = a;
+                ws_acc[partial_index(bq, max_splits, split) * D + c] = a;
                 if (c == 0) {
-                    ws_ml[(bq * max_splits + split) * 2 + 0] = M;
-                    ws_ml[(bq * max_splits + split) * 2 + 1] = l;
+                    ws_ml[partial_index(bq, max_splits, split) * 2 + 0] = M;
+                    ws_ml[partial_index(bq, max_splits, split) * 2 + 1] = l;
                 }
             }
         }
@@ -401,9 +403,9 @@ __device__ __forceinline__ void split_body(
         // Every global load of the split (the token's K row, the V values of
         // this lane's two channels for all 32 tokens, q) is issued before any
         // arithmetic, so the split pays one memory latency.
-        const int w = (split - page_splits) * NW + wv;
-        const int t0 = 32 * w;
-        const int nt = min(32, n_res - t0);
+        const WaveWork ww = wave_work(split, wv, NW, page_splits, gps, n_pages, n_res);
+        const int t0 = ww.t0;
+        const int nt = ww.t1 - ww.t0;
         const uint16_t *kw = reinterpret_cast<const uint16_t *>(cache + res_base +
                                                                 (size_t)unit * 2 * R * D * 2);
         const uint16_t *vw = kw + (size_t)R * D;
@@ -551,8 +553,8 @@ __device__ __forceinline__ void split_body(
         }
     }
     // groups [g0, g1) of this unit (four per page), two register sets in turn
-    const int g0 = (split * NW + wv) * gps;
-    const int g1 = min(4 * n_pages, g0 + gps);
+    const WaveWork ww = wave_work(split, wv, NW, page_splits, gps, n_pages, n_res);
+    const int g0 = ww.g0, g1 = ww.g1;
     const uint8_t *ubase = cache + (size_t)unit * max_pages * page_bytes;
     auto page_ptr = [&](int p) {
         if constexpr (POOL)

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <new>
 #include <vector>
@@ -91,7 +92,7 @@ int max_splits_of(const kvq::Geometry &G) {
 
 // Decode plan for the cache's pages and n_res window tokens (the host
 // counter, or one more for a fused step whose token is not yet counted).
-kvq::DecodePlan plan_of(const kvq_cache *c, int n_res) {
+kvq::DecodePlan plan_of(const kvq_cache *c, int n_res, int slots = 0) {
     kvq::DecodePlan pl{};
     pl.n_pages = c->n_pages;
     pl.n_res = n_res;
@@ -112,7 +113,7 @@ kvq::DecodePlan plan_of(const kvq_cache *c, int n_res) {
             // groups fill several rounds and the hardware's dispatch balances
             // them.
             const int units = c->G.B * c->G.Hkv;
-            const int per_unit = kvq::decode_slots(c->G) / units;
+            const int per_unit = (slots > 0 ? slots : kvq::decode_slots(c->G)) / units;
             S = per_unit >= NW ? per_unit / NW
                                : (groups + kRoundGroups * NW - 1) / (kRoundGroups * NW);
         }
@@ -125,7 +126,203 @@ kvq::DecodePlan plan_of(const kvq_cache *c, int n_res) {
 }
 kvq::DecodePlan plan_of(const kvq_cache *c) { return plan_of(c, c->n_res); }
 
+// Plan of the graph-replayable step: page splits fixed for every replay (the
+// override, or one round of resident waves sized for the host counters at
+// this call; at least one, at most one wave per group of one more page than
+// the cache holds now); the groups per wave follow on the device from the
+// counters of each replay.
+kvq::DecodePlan device_step_plan(const kvq_cache *c, int slots = 0) {
+    constexpr int NW = kvq::kDecodeWaves;
+    const int cap = std::min(kMaxSplits, (4 * std::min(c->G.max_pages, c->n_pages + 1) + NW - 1) / NW);
+    int S;
+    if (c->splits_override > 0) {
+        S = c->splits_override;
+    } else {
+        const int units = c->G.B * c->G.Hkv;
+        const int per_unit = (slots > 0 ? slots : kvq::decode_slots(c->G)) / units;
+        S = per_unit >= NW ? per_unit / NW
+                           : (4 * (c->n_pages + 1) + kRoundGroups * NW - 1) / (kRoundGroups * NW);
+    }
+    kvq::DecodePlan pl{};
+    pl.page_splits = std::max(1, std::min(S, cap));
+    pl.groups_per_split = 1;  // derived on the device from the counters
+    pl.total_splits = pl.page_splits + (kvq::R + 32 * NW - 1) / (32 * NW);
+    pl.max_splits = max_splits_of(c->G);
+    return pl;
+}
+
+// The groups per wave a graph-replayed step derives on the device for
+// n_pages pages (the same expression as the kernel's).
+int device_step_gps(const kvq::DecodePlan &pl, int n_pages) {
+    constexpr int NW = kvq::kDecodeWaves;
+    return std::max(1, (4 * n_pages + pl.page_splits * NW - 1) / (pl.page_splits * NW));
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
+
+// ------------------------------------------------ host-side extent check ----
+// Every workgroup and wave of a decode launch, walked with the kernels' own
+// index helpers (kvq_internal.h): the byte ranges each wave reads and each
+// split's partial slot must lie inside the cache and the workspace, every Key
+// group and window token of a unit must be read by exactly one wave, and the
+// split count must fit the combine kernel.  Out-of-range buffer loads on the
+// device read zeros instead of faulting, so this is where an offset mistake
+// in a plan shows.
+struct PlanCheck {
+    char *msg;
+    size_t len;
+    int fail(const char *what, long a, long b, long c2) {
+        if (msg && len) snprintf(msg, len, "%s (%ld, %ld, %ld)", what, a, b, c2);
+        return KVQ_EINVAL;
+    }
+};
+
+bool inside(size_t off, size_t n, size_t lo, size_t hi) { return off >= lo && n <= hi - off && off <= hi; }
+
+// One unit's work at (n_pages, n_res) under a split plan; `page_at` maps a
+// page index to its byte offset, `win_off` is the unit's window K offset.
+template <class PageAt>
+int check_unit(PlanCheck &pc, const kvq::Geometry &G, int unit, int n_pages, int n_res,
+               int page_splits, int win_splits, int gps, int nw, int max_splits,
+               size_t pages_lo, size_t pages_hi, size_t win_off, size_t win_hi, size_t ws_bytes,
+               PageAt page_at, std::vector<uint8_t> &seen_g, std::vector<uint8_t> &seen_t) {
+    seen_g.assign((size_t)4 * n_pages, 0);
+    seen_t.assign((size_t)n_res, 0);
+    const size_t rows = (size_t)G.B * G.Hq;
+    const size_t ml_bytes = rows * max_splits * 2 * sizeof(float);
+    const int b = unit / G.Hkv, h = unit % G.Hkv;
+    for (int split = 0; split < page_splits + win_splits; split++) {
+        if (split >= max_splits) return pc.fail("split beyond the workspace stride", unit, split, max_splits);
+        for (int hh = 0; hh < G.g; hh++) {
+            const size_t bq = (size_t)b * G.Hq + (size_t)h * G.g + hh;
+            const size_t pi = kvq::partial_index(bq, max_splits, split);
+            if (pi >= rows * max_splits || !inside(ml_bytes + pi * kvq::D * 4, kvq::D * 4, 0, ws_bytes) ||
+                !inside(pi * 8, 8, 0, ml_bytes))
+                return pc.fail("partial outside the workspace", unit, split, hh);
+        }
+        for (int wv = 0; wv < nw; wv++) {
+            const kvq::WaveWork w = kvq::wave_work(split, wv, nw, page_splits, gps, n_pages, n_res);
+            if (w.window) {
+                if (split < page_splits) return pc.fail("window work in a page split", unit, split, wv);
+                if (n_res < 1) return pc.fail("window split without window tokens", unit, split, wv);
+                for (int t = w.t0; t < w.t1; t++) {
+                    if (t < 0 || t >= n_res) return pc.fail("window token out of range", unit, t, n_res);
+                    if (seen_t[t]++) return pc.fail("window token read twice", unit, t, split);
+                }
+                // loads of a wave past the last token read token n_res - 1
+                const int tmax = w.t1 > w.t0 ? w.t1 - 1 : n_res - 1;
+                const size_t kb = win_off + (size_t)tmax * kvq::D * 2;
+                const size_t vb = win_off + (size_t)kvq::R * kvq::D * 2 + (size_t)tmax * kvq::D * 2;
+                if (!inside(win_off, 2, 0, win_hi) || !inside(kb, kvq::D * 2, 0, win_hi) ||
+                    !inside(vb, kvq::D * 2, 0, win_hi))
+                    return pc.fail("window bytes outside the cache", unit, tmax, split);
+            } else {
+                if (split >= page_splits) return pc.fail("page work in a window split", unit, split, wv);
+                if (w.g0 < 0 || (w.g1 > w.g0 && w.g1 > 4 * n_pages))
+                    return pc.fail("Key group out of range", unit, w.g0, w.g1);
+                for (int g = w.g0; g < w.g1; g++) {
+                    if (seen_g[g]++) return pc.fail("Key group read twice", unit, g, split);
+                    const int p = g >> 2;
+                    if (p >= G.max_pages) return pc.fail("page beyond capacity", unit, p, G.max_pages);
+                    const size_t off = page_at(p);
+                    if (!inside(off, G.page_bytes, pages_lo, pages_hi))
+                        return pc.fail("page bytes outside the page region", unit, p, (long)off);
+                }
+            }
+        }
+    }
+    for (int g = 0; g < 4 * n_pages; g++)
+        if (!seen_g[g]) return pc.fail("Key group never read", unit, g, n_pages);
+    for (int t = 0; t < n_res; t++)
+        if (!seen_t[t]) return pc.fail("window token never read", unit, t, n_res);
+    return KVQ_OK;
+}
+
+// The dense kernel's grid for `pl` at the counters (n_pages, n_res).
+int check_dense(PlanCheck &pc, const kvq_cache *c, const kvq::DecodePlan &pl, int n_pages,
+                int n_res, int gps, size_t ws_bytes) {
+    const kvq::Geometry &G = c->G;
+    constexpr int NW = kvq::kDecodeWaves;
+    if (pl.total_splits > kvq::kMaxCombineSplits)
+        return pc.fail("more splits than the combine kernel merges", pl.total_splits, 0, 0);
+    if (ws_bytes < kvq::decode_workspace_bytes(G, pl.max_splits))
+        return pc.fail("workspace smaller than the plan needs", (long)ws_bytes, 0, 0);
+    const int win_splits = pl.total_splits - pl.page_splits;
+    if (win_splits < 0 || (n_res > 0 && win_splits * 32 * NW < n_res))
+        return pc.fail("window splits do not cover the window", win_splits, n_res, 0);
+    const int units = G.B * G.Hkv;
+    // every workgroup of the grid maps to a (unit, split) of the plan
+    const long grid = (long)pl.total_splits * units;
+    std::vector<uint8_t> seen((size_t)grid, 0);
+    for (long x = 0; x < grid; x++) {
+        int unit, split;
+        kvq::dense_split_of((int)x, units, pl.page_splits, win_splits, &unit, &split);
+        if (unit < 0 || unit >= units || split < 0 || split >= pl.total_splits)
+            return pc.fail("workgroup outside the plan", x, unit, split);
+        if (seen[(size_t)unit * pl.total_splits + split]++)
+            return pc.fail("workgroup mapped twice", x, unit, split);
+    }
+    std::vector<uint8_t> sg, st;
+    const size_t cache_bytes = cache_bytes_of(G);
+    for (int u = 0; u < units; u++) {
+        int rc = check_unit(pc, G, u, n_pages, n_res, pl.page_splits, win_splits, gps, NW,
+                            pl.max_splits, 0, G.res_base, kvq::res_k_off(G, u), cache_bytes,
+                            ws_bytes, [&](int p) { return kvq::page_off(G, u, p); }, sg, st);
+        if (rc) return rc;
+    }
+    return KVQ_OK;
+}
+
+// The pool kernel's grid for plan `pl` of pool `p` (whose counters and block
+// lists are the ones the plan was made from).
+int check_pool(PlanCheck &pc, const kvq_pool *p, const kvq::PoolPlan &pl, size_t ws_bytes) {
+    const kvq::Geometry &G = p->G;
+    if (ws_bytes < kvq::decode_workspace_bytes(G, pl.max_splits))
+        return pc.fail("workspace smaller than the plan needs", (long)ws_bytes, 0, 0);
+    const uint32_t grid = pl.page_pref[pl.n_seq] + pl.win_pref[pl.n_seq];
+    std::vector<std::vector<uint8_t>> seen(G.B);
+    for (int b = 0; b < G.B; b++) {
+        const int S = (int)(pl.page_pref[b + 1] - pl.page_pref[b]) / G.Hkv;
+        const int W = (int)(pl.win_pref[b + 1] - pl.win_pref[b]) / G.Hkv;
+        if ((pl.page_pref[b + 1] - pl.page_pref[b]) % G.Hkv || (pl.win_pref[b + 1] - pl.win_pref[b]) % G.Hkv)
+            return pc.fail("split counts not a multiple of the KV heads", b, S, W);
+        if (S + W > kvq::kMaxCombineSplits) return pc.fail("more splits than the combine kernel merges", b, S, W);
+        seen[b].assign((size_t)G.Hkv * (S + W), 0);
+    }
+    for (uint32_t x = 0; x < grid; x++) {
+        int b, h, split, S;
+        kvq::pool_split_of(pl, G.Hkv, x, &b, &h, &split, &S);
+        const int W = (int)(pl.win_pref[b + 1] - pl.win_pref[b]) / G.Hkv;
+        if (b < 0 || b >= G.B || h < 0 || h >= G.Hkv || split < 0 || split >= S + W)
+            return pc.fail("workgroup outside the plan", x, b, split);
+        if (seen[b][(size_t)h * (S + W) + split]++) return pc.fail("workgroup mapped twice", x, b, split);
+    }
+    std::vector<uint8_t> sg, st;
+    for (int b = 0; b < G.B; b++) {
+        const int S = (int)(pl.page_pref[b + 1] - pl.page_pref[b]) / G.Hkv;
+        const int W = (int)(pl.win_pref[b + 1] - pl.win_pref[b]) / G.Hkv;
+        for (size_t i = 0; i < seen[b].size(); i++)
+            if (!seen[b][i]) return pc.fail("split without a workgroup", b, (long)i, 0);
+        if (!p->live[b]) {
+            if (S || W) return pc.fail("work for a released sequence", b, S, W);
+            continue;
+        }
+        const int np = pl.n_pages[b], nr = pl.n_res[b];
+        if (np > (int)p->blocks[b].size()) return pc.fail("pages beyond the block list", b, np, 0);
+        for (int h = 0; h < G.Hkv; h++) {
+            const int u = b * G.Hkv + h;
+            auto page_at = [&](int pg) {
+                const int32_t blk = pg < (int)p->blocks[b].size() ? p->blocks[b][pg] : -1;
+                return blk < 0 || blk >= p->n_blocks ? ~(size_t)0
+                                                     : ((size_t)blk * G.Hkv + h) * G.page_bytes;
+            };
+            int rc = check_unit(pc, G, u, np, nr, S, W, pl.gps, 1, pl.max_splits, 0, G.res_base,
+                                kvq::res_k_off(G, u), p->table_off, ws_bytes, page_at, sg, st);
+            if (rc) return rc;
+        }
+    }
+    return KVQ_OK;
+}
 
 // ---------------------------------------------------------------- pool ----
 constexpr int kPoolMaxPages = 65535;  // page counts travel as 16-bit values
@@ -158,7 +355,7 @@ int32_t *pool_table(kvq_pool *p) { return reinterpret_cast<int32_t *>(p->mem + p
 
 // Split plan of one decode launch over the live sequences (slot_of[b] >= 0:
 // the fused append's window slot of sequence b).
-kvq::PoolPlan pool_plan(const kvq_pool *p, const int *slot_of) {
+kvq::PoolPlan pool_plan(const kvq_pool *p, const int *slot_of, int slots = 0) {
     const kvq::Geometry &G = p->G;
     kvq::PoolPlan pl{};
     pl.n_seq = G.B;
@@ -177,7 +374,7 @@ kvq::PoolPlan pool_plan(const kvq_pool *p, const int *slot_of) {
     // a round.
     int gps = 1;
     if (units_with_pages > 0) {
-        const int target = kvq::pool_decode_slots(G);
+        const int target = slots > 0 ? slots : kvq::pool_decode_slots(G);
         if (target >= units_with_pages)
             gps = (int)std::max<int64_t>(1, (unit_groups + target - 1) / target);
         else
@@ -428,25 +625,7 @@ int kvq_append_decode_device(kvq_cache *c, const void *k, const void *v, const v
         return KVQ_EALIGN;
     if (ws_bytes < kvq::decode_workspace_bytes(c->G, max_splits_of(c->G)))
         return KVQ_EWORKSPACE;
-    // Page splits fixed for every replay: the override, or one round of
-    // resident waves sized for the host counters at this call (at least one,
-    // at most one wave per group of one more page than the cache holds now).
-    constexpr int NW = kvq::kDecodeWaves;
-    const int cap = std::min(kMaxSplits, (4 * std::min(c->G.max_pages, c->n_pages + 1) + NW - 1) / NW);
-    int S;
-    if (c->splits_override > 0) {
-        S = c->splits_override;
-    } else {
-        const int units = c->G.B * c->G.Hkv;
-        const int per_unit = kvq::decode_slots(c->G) / units;
-        S = per_unit >= NW ? per_unit / NW
-                           : (4 * (c->n_pages + 1) + kRoundGroups * NW - 1) / (kRoundGroups * NW);
-    }
-    kvq::DecodePlan pl{};
-    pl.page_splits = std::max(1, std::min(S, cap));
-    pl.groups_per_split = 1;  // derived on the device from the counters
-    pl.total_splits = pl.page_splits + (kvq::R + 32 * NW - 1) / (32 * NW);
-    pl.max_splits = max_splits_of(c->G);
+    kvq::DecodePlan pl = device_step_plan(c);
     pl.dstate = dev_state;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = kvq::launch_flush_window_device(c->G, c->mem, dev_state, c->rel, st);
@@ -455,6 +634,66 @@ int kvq_append_decode_device(kvq_cache *c, const void *k, const void *v, const v
                                          workspace, pl, static_cast<const uint16_t *>(k),
                                          static_cast<const uint16_t *>(v), 0, c->ev_before,
                                          c->ev_after, st));
+}
+
+int kvq_check_decode_plan(const kvq_cache *c, int32_t mode, int32_t slots, size_t ws_bytes,
+                          char *msg, size_t msg_len) {
+    if (!c || mode < 0 || mode > 2 || slots < 0) return KVQ_EINVAL;
+    PlanCheck pc{msg, msg_len};
+    if (msg && msg_len) msg[0] = 0;
+    if (mode == 0) {
+        if (c->n_pages == 0 && c->n_res == 0) return KVQ_OK;  // the call is refused before any launch
+        const kvq::DecodePlan pl = plan_of(c, c->n_res, slots);
+        return check_dense(pc, c, pl, c->n_pages, c->n_res, pl.groups_per_split, ws_bytes);
+    }
+    if (mode == 1) {  // kvq_append_decode: flush a full window first, then one more token
+        kvq_cache t = *c;
+        if (t.n_res == kvq::R) {
+            if (t.n_pages >= t.G.max_pages) return KVQ_OK;  // refused before any launch
+            t.n_pages += 1;
+            t.n_res = 0;
+        }
+        const kvq::DecodePlan pl = plan_of(&t, t.n_res + 1, slots);
+        return check_dense(pc, &t, pl, t.n_pages, t.n_res + 1, pl.groups_per_split, ws_bytes);
+    }
+    // mode 2: the graph-replayable step captured now, replayed until the
+    // cache is full: page split count fixed, groups per wave from the device
+    // counters of each replay
+    const kvq::DecodePlan pl = device_step_plan(c, slots);
+    const int lo = std::max(c->n_pages, 0), hi = c->G.max_pages;
+    const int pages[] = {lo, std::min(lo + 1, hi), (lo + hi) / 2, std::max(hi - 1, lo), hi};
+    const int wins[] = {1, 2, 31, 32, 33, 64, 97, 127, 128};
+    for (int np : pages)
+        for (int nr : wins) {
+            kvq::DecodePlan q = pl;
+            q.n_pages = np;
+            q.n_res = nr;
+            const int rc = check_dense(pc, c, q, np, nr, device_step_gps(pl, np), ws_bytes);
+            if (rc) return rc;
+        }
+    return KVQ_OK;
+}
+
+int kvq_pool_check_decode_plan(const kvq_pool *p, int32_t mode, int32_t slots, size_t ws_bytes,
+                               char *msg, size_t msg_len) {
+    if (!p || mode < 0 || mode > 1 || slots < 0) return KVQ_EINVAL;
+    PlanCheck pc{msg, msg_len};
+    if (msg && msg_len) msg[0] = 0;
+    if (mode == 0) return check_pool(pc, p, pool_plan(p, nullptr, slots), ws_bytes);
+    // kvq_pool_append_decode: full windows flushed into the next free blocks
+    // first, then one more token per live sequence
+    kvq_pool t = *p;
+    for (int b = 0; b < t.G.B; b++) {
+        if (!t.live[b] || t.n_res[b] != kvq::R) continue;
+        if (t.free_list.empty() || t.n_pages[b] >= t.G.max_pages) return KVQ_OK;  // refused first
+        t.blocks[b].push_back(t.free_list.back());
+        t.free_list.pop_back();
+        t.n_pages[b] += 1;
+        t.n_res[b] = 0;
+    }
+    int slot_of[kvq::kPoolMaxSeqs];
+    for (int b = 0; b < t.G.B; b++) slot_of[b] = t.live[b] ? t.n_res[b] : -1;
+    return check_pool(pc, &t, pool_plan(&t, slot_of, slots), ws_bytes);
 }
 
 int kvq_set_decode_splits(kvq_cache *c, int32_t splits) {

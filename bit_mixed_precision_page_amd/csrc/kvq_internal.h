@@ -87,6 +87,50 @@ hipError_t launch_quantize_groups(int dtype, int L, const uint16_t *x, int n_gro
                                   int group_len, uint16_t *s, uint16_t *z, uint8_t *codes,
                                   hipStream_t stream);
 
+// Splits (page + window) one combine workgroup merges per output row.
+constexpr int kMaxCombineSplits = 272;
+
+// Work of wave wv (of nw) of split `split` of one (sequence, KV head) unit
+// in a decode launch: a page split (split < page_splits) streams the unit's
+// Key groups [g0, g1) (four 32-token groups per page); a window split covers
+// window tokens [t0, t1) (t1 <= t0: none; its loads then read token
+// n_res - 1).  The decode kernels and the host-side extent check
+// (kvq_check_decode_plan) both take their indices from here.
+struct WaveWork {
+    bool window;
+    int g0, g1, t0, t1;
+};
+__host__ __device__ inline WaveWork wave_work(int split, int wv, int nw, int page_splits, int gps,
+                                              int n_pages, int n_res) {
+    WaveWork w{};
+    if (split >= page_splits) {
+        w.window = true;
+        w.t0 = 32 * ((split - page_splits) * nw + wv);
+        w.t1 = n_res < w.t0 + 32 ? n_res : w.t0 + 32;
+    } else {
+        w.g0 = (split * nw + wv) * gps;
+        w.g1 = 4 * n_pages < w.g0 + gps ? 4 * n_pages : w.g0 + gps;
+    }
+    return w;
+}
+// Workgroup x of the dense decode kernel's 1-D grid: every page split of
+// every unit first (unit-major), then the window splits.
+__host__ __device__ inline void dense_split_of(int x, int n_units, int page_splits, int win_splits,
+                                               int *unit, int *split) {
+    if (x < page_splits * n_units) {
+        *unit = x / page_splits;
+        *split = x % page_splits;
+    } else {
+        const int l = x - page_splits * n_units;
+        *unit = l / win_splits;
+        *split = page_splits + l % win_splits;
+    }
+}
+// Partial (m, l, acc) slot of query row bq = b Hq + hq, split `split`.
+__host__ __device__ inline size_t partial_index(size_t bq, int max_splits, int split) {
+    return bq * (size_t)max_splits + (size_t)split;
+}
+
 struct DecodePlan {
     int n_pages, n_res;
     int page_splits;      // splits over the 32-token page groups (0 when n_pages == 0)
@@ -183,6 +227,36 @@ struct PoolPlan {
     uint8_t n_res[kPoolMaxSeqs];
     uint8_t slot[kPoolMaxSeqs];  // fused append: window slot of the new token, or kPoolNoSlot
 };
+// Last index b in [0, n) with pref[b] <= x (pref ascending, pref[n] > x).
+template <typename T>
+__host__ __device__ inline int pool_seq_of(const T *pref, int n, uint32_t x) {
+    int lo = 0, hi = n;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((uint32_t)pref[mid] <= x) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+// Workgroup x of the pool decode kernel's grid -> (sequence b, KV head h,
+// split, page splits S of that sequence).
+__host__ __device__ inline void pool_split_of(const PoolPlan &pl, int Hkv, uint32_t x, int *b,
+                                              int *h, int *split, int *S) {
+    if (x < (uint32_t)pl.page_wgs) {
+        *b = pool_seq_of(pl.page_pref, pl.n_seq, x);
+        *S = (int)(pl.page_pref[*b + 1] - pl.page_pref[*b]) / Hkv;
+        const int l = (int)(x - pl.page_pref[*b]);
+        *h = l / *S;
+        *split = l % *S;
+    } else {
+        const uint32_t y = x - (uint32_t)pl.page_wgs;
+        *b = pool_seq_of(pl.win_pref, pl.n_seq, y);
+        *S = (int)(pl.page_pref[*b + 1] - pl.page_pref[*b]) / Hkv;
+        const int W = (int)(pl.win_pref[*b + 1] - pl.win_pref[*b]) / Hkv;
+        const int l = (int)(y - pl.win_pref[*b]);
+        *h = l / W;
+        *split = *S + l % W;
+    }
+}
 
 // G describes the pool: B = sequence slots, max_pages = pages per sequence,
 // res_base = byte offset of the windows ([B][Hkv][K | V][R][D]).

@@ -10,17 +10,6 @@
 namespace kvq {
 namespace {
 
-// Last index b in [0, n) with pref[b] <= x (pref ascending, pref[n] > x).
-template <typename T>
-__device__ __forceinline__ int seq_of(const T *pref, int n, uint32_t x) {
-    int lo = 0, hi = n;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if ((uint32_t)pref[mid] <= x) lo = mid; else hi = mid;
-    }
-    return lo;
-}
-
 // 1-D grid: the page splits of every sequence (sequence-major, then KV head,
 // then split), then the window splits in the same order.
 template <int DT, int G, int KH>
@@ -30,23 +19,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target
     const uint16_t *__restrict__ q, float *__restrict__ ws_ml, float *__restrict__ ws_acc,
     const int32_t *__restrict__ table, int Hkv, int max_pages, uint32_t page_bytes, int k,
     size_t res_base, float qscale, const PoolPlan pl) {
-    const uint32_t x = blockIdx.x;
     int b, h, split, S;
-    if (x < (uint32_t)pl.page_wgs) {
-        b = __builtin_amdgcn_readfirstlane(seq_of(pl.page_pref, pl.n_seq, x));
-        S = (int)(pl.page_pref[b + 1] - pl.page_pref[b]) / Hkv;
-        const int l = (int)(x - pl.page_pref[b]);
-        h = l / S;
-        split = l % S;
-    } else {
-        const uint32_t y = x - (uint32_t)pl.page_wgs;
-        b = __builtin_amdgcn_readfirstlane(seq_of(pl.win_pref, pl.n_seq, y));
-        S = (int)(pl.page_pref[b + 1] - pl.page_pref[b]) / Hkv;
-        const int W = (int)(pl.win_pref[b + 1] - pl.win_pref[b]) / Hkv;
-        const int l = (int)(y - pl.win_pref[b]);
-        h = l / W;
-        split = S + l % W;
-    }
+    pool_split_of(pl, Hkv, blockIdx.x, &b, &h, &split, &S);
+    b = __builtin_amdgcn_readfirstlane(b);
     const int slot = pl.slot[b] == kPoolNoSlot ? -1 : (int)pl.slot[b];
     split_body<DT, G, KH, true>(mem, window_w, knew, vnew, slot, q, ws_ml, ws_acc, Hkv, max_pages,
                                 page_bytes, k, res_base, (int)pl.n_pages[b], (int)pl.n_res[b], S,

@@ -33,7 +33,8 @@ EXPORTS = ["kvq_cache_bytes", "kvq_page_bytes", "kvq_cache_create", "kvq_cache_d
            "kvq_set_channel_relevance", "kvq_query_relevance", "kvq_pool_set_channel_relevance",
            "kvq_device_state_init", "kvq_append_decode_device",
            "kvq_prefill_workspace_bytes", "kvq_prefill_select", "kvq_prefill_set_kernel_events",
-           "kvq_prefill_set_max_key_splits"]
+           "kvq_prefill_set_max_key_splits", "kvq_check_decode_plan",
+           "kvq_pool_check_decode_plan"]
 
 
 class KvqError(RuntimeError):
@@ -102,6 +103,8 @@ _SIG = {
     "kvq_pool_set_kernel_events": [_vp, _vp, _vp],
     "kvq_prefill_set_kernel_events": [_vp, _vp],
     "kvq_prefill_set_max_key_splits": [_i32],
+    "kvq_check_decode_plan": [_vp, _i32, _i32, _sz, ctypes.c_char_p, _sz],
+    "kvq_pool_check_decode_plan": [_vp, _i32, _i32, _sz, ctypes.c_char_p, _sz],
     "kvq_set_channel_relevance": [_vp, _vp],
     "kvq_query_relevance": [_i32, _i32, _i32, _i32, _vp, _vp, _vp],
     "kvq_pool_set_channel_relevance": [_vp, _vp],
@@ -408,23 +411,48 @@ def kvq_prefill_set_kernel_events(before, after):
            "kvq_prefill_set_kernel_events")
 
 
+def kvq_check_decode_plan(handle, mode, slots, ws_bytes):
+    """Host-side extent check of a decode launch: (code, message)."""
+    buf = ctypes.create_string_buffer(256)
+    rc = _L.kvq_check_decode_plan(handle, mode, slots, ws_bytes, buf, len(buf))
+    return rc, buf.value.decode()
+
+
+def kvq_pool_check_decode_plan(handle, mode, slots, ws_bytes):
+    """Host-side extent check of a pool decode launch: (code, message)."""
+    buf = ctypes.create_string_buffer(256)
+    rc = _L.kvq_pool_check_decode_plan(handle, mode, slots, ws_bytes, buf, len(buf))
+    return rc, buf.value.decode()
+
+
 def kvq_prefill_set_max_key_splits(n):
     """Cap on the prefill's key chunks (1..4), 0 = automatic."""
     _check(_L.kvq_prefill_set_max_key_splits(n), "kvq_prefill_set_max_key_splits")
 
 
 # -- convenience owner of the device buffers -----------------------------------
+def _torch_alloc(nbytes, device):
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 class Cache:
     """Owns a cache's device memory and workspace (torch tensors) and its handle."""
 
-    def __init__(self, cfg, device="cuda"):
+    def __init__(self, cfg, device="cuda", alloc=None):
+        """alloc(nbytes, device) -> uint8 device tensor for the cache memory
+        and the workspace (default: torch.empty)."""
+        alloc = alloc or _torch_alloc
         self.cfg = cfg
         self.nbytes = kvq_cache_bytes(cfg)
-        self.mem = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        self.mem = alloc(self.nbytes, device)
         self.handle = kvq_cache_create(cfg, self.mem, self.nbytes)
         self.ws_bytes = kvq_decode_workspace_bytes(self.handle)
-        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.ws = alloc(max(self.ws_bytes, 16), device)
         self.page_bytes = kvq_page_bytes(cfg)
+
+    def check_plan(self, mode=0, slots=0):
+        """Host-side extent check of the next decode launch (kvq_check_decode_plan)."""
+        return kvq_check_decode_plan(self.handle, mode, slots, self.ws_bytes)
 
     def quantize_page(self, k, v, n_pages, stream=None):
         kvq_quantize_page(self.handle, k, v, n_pages, stream)
@@ -485,15 +513,20 @@ class Cache:
 class Pool:
     """Owns a block pool's device memory and workspace (torch tensors) and its handle."""
 
-    def __init__(self, cfg, n_blocks, device="cuda"):
+    def __init__(self, cfg, n_blocks, device="cuda", alloc=None):
+        alloc = alloc or _torch_alloc
         self.cfg = cfg
         self.n_blocks = n_blocks
         self.nbytes = kvq_pool_bytes(cfg, n_blocks)
-        self.mem = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        self.mem = alloc(self.nbytes, device)
         self.handle = kvq_pool_create(cfg, n_blocks, self.mem, self.nbytes)
         self.ws_bytes = kvq_pool_decode_workspace_bytes(self.handle)
-        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.ws = alloc(max(self.ws_bytes, 16), device)
         self.page_bytes = kvq_page_bytes(cfg)
+
+    def check_plan(self, mode=0, slots=0):
+        """Host-side extent check of the next decode launch (kvq_pool_check_decode_plan)."""
+        return kvq_pool_check_decode_plan(self.handle, mode, slots, self.ws_bytes)
 
     def prefill(self, seq, k, v, stream=None):
         """k, v: [Hkv][n_tokens][128] device tensors of one sequence."""

@@ -181,6 +181,24 @@ int kvq_append_decode_device(kvq_cache *cache, const void *k, const void *v, con
    it beyond rounding. */
 int kvq_set_decode_splits(kvq_cache *cache, int32_t splits);
 
+/* Host-side extent check of the decode launches a call would make now; no
+   GPU work and nothing is launched.  It walks every workgroup and wave of the
+   grid of kvq_decode_attention (mode 0), of kvq_append_decode (mode 1: a
+   full window flushed first, then one more window token) or of
+   kvq_append_decode_device as captured now and replayed until the cache is
+   full (mode 2), with the kernels' own index arithmetic, and checks that
+   every page, window token and split partial they address lies inside the
+   cache and inside a workspace of ws_bytes, that every 32-token Key group and
+   every window token of every (sequence, KV head) is read by exactly one
+   wave, and that the split count fits the combine kernel.  (The kernels load
+   pages through buffer descriptors, whose out-of-range reads return zeros
+   rather than faulting: this is where an offset mistake would show.)
+   slots > 0: the resident waves the split plan assumes (0: the device's,
+   from the occupancy API).  Returns KVQ_OK, or KVQ_EINVAL with the first
+   violation described in msg (msg_len bytes, may be NULL). */
+int kvq_check_decode_plan(const kvq_cache *cache, int32_t mode, int32_t slots, size_t ws_bytes,
+                          char *msg, size_t msg_len);
+
 /* The page split count the next kvq_decode_attention call will use. */
 int kvq_get_decode_splits(const kvq_cache *cache, int32_t *splits);
 
@@ -324,6 +342,13 @@ int kvq_pool_set_channel_relevance(kvq_pool *pool, const float *rel);
 
 /* Timing hooks of the pool's split kernel (as kvq_set_kernel_events). */
 int kvq_pool_set_kernel_events(kvq_pool *pool, void *before, void *after);
+
+/* The extent check of kvq_check_decode_plan for the pool's decode launch:
+   mode 0 = kvq_pool_decode_attention, mode 1 = kvq_pool_append_decode (full
+   windows flushed into the next free blocks first, then one more token per
+   live sequence); pages are reached through each sequence's block list. */
+int kvq_pool_check_decode_plan(const kvq_pool *pool, int32_t mode, int32_t slots,
+                               size_t ws_bytes, char *msg, size_t msg_len);
 
 /* ---- Prefill with cumulative attention scores and token selection ----
    MiniKV summary (f-binder), "proposed method": the prefill processes the

@@ -20,3 +20,13 @@ def pytest_configure(config):
 def ora():
     import oracle
     return oracle.lib()
+
+
+@pytest.fixture(autouse=True)
+def _guard_bands(request):
+    """GPU tests: every guarded device buffer (tests/gpu_util.py) keeps its
+    canary bands intact through the test."""
+    yield
+    if request.node.get_closest_marker("gpu") is not None:
+        import gpu_util
+        gpu_util.GUARDS.check()

@@ -7,6 +7,62 @@ import oracle
 from bit_mixed_precision_page_amd import inputs as gen
 
 P = 128
+GUARD = 1 << 16  # canary bytes before and after every guarded device buffer
+
+
+class Guards:
+    """Device buffers with canary bands: each allocation is the middle of a
+    larger tensor whose first and last GUARD bytes hold a seeded pattern.
+    `check()` asserts every band is unchanged (a kernel that writes past its
+    buffer, in either direction, changes one) and forgets the buffers."""
+
+    def __init__(self):
+        self.items = []
+        self.n = 0
+
+    def alloc(self, nbytes, device="cuda"):
+        buf = torch.empty(nbytes + 2 * GUARD, dtype=torch.uint8, device=device)
+        g = torch.Generator().manual_seed(1000 + self.n)
+        self.n += 1
+        pat = torch.randint(0, 256, (2, GUARD), dtype=torch.uint8, generator=g)
+        buf[:GUARD].copy_(pat[0])
+        buf[GUARD + nbytes:].copy_(pat[1])
+        self.items.append((buf, nbytes, pat))
+        return buf[GUARD:GUARD + nbytes]
+
+    def out(self, *shape, dtype=torch.float32):
+        """A guarded output tensor."""
+        n = int(np.prod(shape)) * torch.empty(0, dtype=dtype).element_size()
+        return self.alloc(n).view(dtype).view(*shape)
+
+    def check(self):
+        torch.cuda.synchronize()
+        items, self.items = self.items, []
+        for i, (buf, nbytes, pat) in enumerate(items):
+            lo = buf[:GUARD].cpu()
+            hi = buf[GUARD + nbytes:].cpu()
+            assert torch.equal(lo, pat[0]), f"guard band before buffer {i} ({nbytes} B) overwritten"
+            assert torch.equal(hi, pat[1]), f"guard band after buffer {i} ({nbytes} B) overwritten"
+        return len(items)
+
+
+GUARDS = Guards()
+
+
+def guarded_cache(cfg):
+    from bit_mixed_precision_page_amd import kvq
+    return kvq.Cache(cfg, alloc=GUARDS.alloc)
+
+
+def guarded_pool(cfg, n_blocks):
+    from bit_mixed_precision_page_amd import kvq
+    return kvq.Pool(cfg, n_blocks, alloc=GUARDS.alloc)
+
+
+def assert_plan_ok(obj, mode=0):
+    """The host-side extent check of the next decode launch passes."""
+    rc, msg = obj.check_plan(mode)
+    assert rc == 0, f"decode plan check: {msg}"
 
 
 def dev(bits):
@@ -44,7 +100,7 @@ class Pair:
         self.max_pages = max_pages or (self.bulk + self.window // P + 2)
         self.cfg = kvq.config(self.B, self.Hq, self.Hkv, self.k, self.max_pages, w.dtype,
                               softmax_scale=scale)
-        self.gpu = kvq.Cache(self.cfg)
+        self.gpu = guarded_cache(self.cfg)
         self.ora = (oracle.OracleCache(w.dtype, self.B, self.Hq, self.Hkv, self.k,
                                        self.max_pages, scale=scale)
                     if with_oracle else None)
@@ -62,6 +118,7 @@ class Pair:
             self.append(self.K[:, :, self.bulk * P + t], self.V[:, :, self.bulk * P + t])
 
     def append(self, k_t, v_t):
+        assert_plan_ok(self.gpu, mode=1)
         f = self.gpu.append_token(dev(k_t), dev(v_t))
         if self.ora is not None:
             fo = self.ora.append(k_t, v_t)
@@ -76,8 +133,9 @@ class Pair:
         return q
 
     def attention(self, q_bits, splits=0):
-        out = torch.empty(self.B, self.Hq, 128, dtype=torch.float32, device="cuda")
+        out = GUARDS.out(self.B, self.Hq, 128)
         self.kvq.kvq_set_decode_splits(self.gpu.handle, splits)
+        assert_plan_ok(self.gpu)
         self.gpu.decode_attention(dev(q_bits), out)
         torch.cuda.synchronize()
         return host(out)

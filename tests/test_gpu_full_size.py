@@ -19,7 +19,7 @@ import torch
 
 import oracle
 from bit_mixed_precision_page_amd import inputs as gen
-from gpu_util import dev, host
+from gpu_util import GUARDS, assert_plan_ok, dev, guarded_cache, host
 
 pytestmark = pytest.mark.gpu
 P = 128
@@ -35,7 +35,7 @@ def say(*a):
 def build_gpu(w, K, V, bulk, window):
     from bit_mixed_precision_page_amd import kvq
     cfg = kvq.config(w.B, w.Hq, w.Hkv, w.boost, w.max_pages, w.dtype)
-    c = kvq.Cache(cfg)
+    c = guarded_cache(cfg)
     if bulk:
         c.quantize_page(dev(K[:, :, :bulk * P]), dev(V[:, :, :bulk * P]), bulk)
     for t in range(window):
@@ -78,7 +78,8 @@ def oracle_attention(w, pages, kres, vres, q, n_pages, n_res, units):
 
 
 def gpu_attention(gpu, q, w):
-    out = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    out = GUARDS.out(w.B, w.Hq, 128)
+    assert_plan_ok(gpu)
     gpu.decode_attention(dev(q), out)
     torch.cuda.synchronize()
     return host(out)

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from bit_mixed_precision_page_amd import inputs as gen
-from gpu_util import Pair, dev, host
+from gpu_util import GUARDS, Pair, assert_plan_ok, dev, host
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -55,7 +55,8 @@ def test_graph_replay_equals_eager_steps():
     kt, vt = gen.step_kv(w, 700)
     kt, vt = kt[:B], vt[:B]
     q = ref.query(0)
-    out = torch.empty(B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    out = GUARDS.out(B, w.Hq, 128)
+    assert_plan_ok(graph.gpu, mode=2)
     graph.gpu.append_decode_device(dev(kt), dev(vt), dev(q), out, st)
     torch.cuda.synchronize()
     want = ref_step(0, kt, vt, q)
@@ -66,7 +67,7 @@ def test_graph_replay_equals_eager_steps():
     ks = torch.empty(B, w.Hkv, 128, dtype=torch.int16, device="cuda")
     vs = torch.empty_like(ks)
     qs = torch.empty(B, w.Hq, 128, dtype=torch.int16, device="cuda")
-    os_ = torch.empty(B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    os_ = GUARDS.out(B, w.Hq, 128)
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     with torch.cuda.graph(g, stream=side):

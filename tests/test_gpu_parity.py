@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from bit_mixed_precision_page_amd import inputs as gen
-from gpu_util import Pair, dev, first_page_mismatch, host
+from gpu_util import GUARDS, Pair, dev, first_page_mismatch, guarded_cache, host
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -152,10 +152,10 @@ def test_snapshot_restore():
     pair = Pair(W["tiny"], bulk_pages=3, window=40, with_oracle=False)
     q = pair.query()
     a = pair.attention(q)
-    c2 = kvq.Cache(pair.cfg)
+    c2 = guarded_cache(pair.cfg)
     c2.mem.copy_(pair.gpu.mem)
     kvq.kvq_set_state(c2.handle, *pair.gpu.state)
-    out = torch.empty(pair.B, pair.Hq, 128, dtype=torch.float32, device="cuda")
+    out = GUARDS.out(pair.B, pair.Hq, 128)
     c2.decode_attention(dev(q), out)
     torch.cuda.synchronize()
     assert (host(out) == a).all()
@@ -172,7 +172,7 @@ def test_fused_append_decode_equals_two_calls():
         kt, vt = gen.step_kv(w, 500 + step)
         kt, vt = kt[:2], vt[:2]
         q = ref.query(step)
-        out = torch.empty(2, w.Hq, 128, dtype=torch.float32, device="cuda")
+        out = GUARDS.out(2, w.Hq, 128)
         f1 = fused.gpu.append_decode(dev(kt), dev(vt), dev(q), out)
         torch.cuda.synchronize()
         f2 = ref.append(kt, vt)

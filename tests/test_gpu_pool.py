@@ -18,7 +18,7 @@ import torch
 
 import oracle
 from bit_mixed_precision_page_amd import inputs as gen
-from gpu_util import dev, host
+from gpu_util import GUARDS, assert_plan_ok, dev, guarded_cache, guarded_pool, host
 
 pytestmark = pytest.mark.gpu
 P = 128
@@ -39,7 +39,7 @@ class PoolPair:
         self.kvq, self.w = kvq, w
         self.max_pages = max_pages
         self.cfg = kvq.config(w.B, w.Hq, w.Hkv, w.boost, max_pages, w.dtype, softmax_scale=scale)
-        self.gpu = kvq.Pool(self.cfg, n_blocks)
+        self.gpu = guarded_pool(self.cfg, n_blocks)
         self.scale = scale
         self.ora = {}      # seq -> OracleCache (B = 1)
         self.tokens = {}   # seq -> tokens so far
@@ -144,7 +144,8 @@ def test_pool_varlen_streaming(dtype, Hq, Hkv, boost):
     pair.check_state()
     say("    prefill: pages, table and windows bit-exact")
     k, v, q = pair.step_inputs(0)
-    out = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    out = GUARDS.out(w.B, w.Hq, 128)
+    assert_plan_ok(pair.gpu)
     pair.gpu.decode_attention(dev(q), out)
     torch.cuda.synchronize()
     say(f"    decode after prefill: max |gpu - oracle| = {pair.check_attention(host(out), q):.3e}")
@@ -154,6 +155,7 @@ def test_pool_varlen_streaming(dtype, Hq, Hkv, boost):
         assert nf == pair.oracle_append(k, v), step
         if step in (1, 25, 26, 85, 129, 140):
             pair.check_state()
+            assert_plan_ok(pair.gpu)
             pair.gpu.decode_attention(dev(q), out)
             torch.cuda.synchronize()
             err = pair.check_attention(host(out), q)
@@ -170,11 +172,12 @@ def test_pool_fused_equals_two_calls():
         pr.prefill(0, 300, oracle_side=False)
         pr.prefill(3, 127, oracle_side=False)
         pr.prefill(4, 1000, oracle_side=False)
-    oa = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device="cuda")
-    ob = torch.empty_like(oa)
+    oa = GUARDS.out(w.B, w.Hq, 128)
+    ob = GUARDS.out(w.B, w.Hq, 128)
     for step in range(1, 30):
         k, v, q = a.step_inputs(step)
         kd, vd, qd = dev(k), dev(v), dev(q)
+        assert_plan_ok(a.gpu, mode=1)
         na = a.gpu.append_decode(kd, vd, qd, oa)
         nb = b.gpu.append(kd, vd)
         b.gpu.decode_attention(qd, ob)
@@ -203,7 +206,7 @@ def test_pool_matches_dense_cache():
         for h in range(w.Hkv):
             K[s, h], V[s, h] = gen.unit_kv(w, s, h, n_tok)
         pair.gpu.prefill(s, dev(K[s]), dev(V[s]))
-    dense = kvq.Cache(kvq.config(w.B, w.Hq, w.Hkv, w.boost, 10, w.dtype))
+    dense = guarded_cache(kvq.config(w.B, w.Hq, w.Hkv, w.boost, 10, w.dtype))
     dense.quantize_page(dev(np.ascontiguousarray(K[:, :, :full * P])),
                         dev(np.ascontiguousarray(V[:, :, :full * P])), full)
     for t in range(full * P, n_tok):
@@ -217,8 +220,9 @@ def test_pool_matches_dense_cache():
                 assert np.array_equal(host(pair.gpu.page_view(blk, h)), dp[s, h, p]), (s, p, h)
     q = gen.to_bits(np.random.default_rng(3).standard_normal((w.B, w.Hq, 128), dtype=np.float32),
                     w.dtype)
-    o1 = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device="cuda")
-    o2 = torch.empty_like(o1)
+    o1 = GUARDS.out(w.B, w.Hq, 128)
+    o2 = GUARDS.out(w.B, w.Hq, 128)
+    assert_plan_ok(pair.gpu)
     pair.gpu.decode_attention(dev(q), o1)
     dense.decode_attention(dev(q), o2)
     torch.cuda.synchronize()
@@ -289,7 +293,8 @@ def test_pool_full_size_varlen():
     pair.check_state()
     say(f"    all {sum(n // P for n in lengths) * w.Hkv} pages and every window bit-exact")
     q = gen.query(w)
-    out = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    out = GUARDS.out(w.B, w.Hq, 128)
+    assert_plan_ok(pair.gpu)
     pair.gpu.decode_attention(dev(q), out)
     torch.cuda.synchronize()
     got = host(out)

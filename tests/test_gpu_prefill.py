@@ -15,7 +15,7 @@ import pytest
 import torch
 
 from bit_mixed_precision_page_amd import inputs as gen
-from gpu_util import dev, host
+from gpu_util import dev, guarded_cache, host
 
 import oracle
 
@@ -144,7 +144,7 @@ def test_prefill_selected_rows_quantize_like_the_oracle():
     out, score, keep, k_sel, v_sel = kvq.prefill_select(w.dtype, dev(q), dev(k), dev(v), heavy,
                                                         recent)
     cfg = kvq.config(1, w.Hq, w.Hkv, w.boost, 2, w.dtype)
-    cache = kvq.Cache(cfg)
+    cache = guarded_cache(cfg)
     cache.quantize_page(k_sel.contiguous()[None], v_sel.contiguous()[None], 2)
     torch.cuda.synchronize()
     ks = host(k_sel).view(np.uint16)[None]

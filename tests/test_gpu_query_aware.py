@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from bit_mixed_precision_page_amd import inputs as gen
-from gpu_util import Pair, dev, first_page_mismatch, host
+from gpu_util import Pair, dev, first_page_mismatch, guarded_pool, host
 
 pytestmark = pytest.mark.gpu
 P = 128
@@ -83,7 +83,7 @@ def test_query_aware_pool_pages(ora):
     from bit_mixed_precision_page_amd import kvq
     w = dataclasses.replace(gen.WORKLOADS["tiny"], B=4, Hq=8, Hkv=2, dtype=gen.BF16)
     cfg = kvq.config(w.B, w.Hq, w.Hkv, 16, 8, w.dtype)
-    pool = kvq.Pool(cfg, 24)
+    pool = guarded_pool(cfg, 24)
     r = np.random.default_rng(77)
     rel = np.abs(r.standard_normal((w.B, w.Hkv, 128))).astype(np.float32)
     rel[1] = 0.0
