@@ -1,10 +1,21 @@
 // kvq_decode.hip -- split-K GQA decode attention over the dense cache: the
 // kernels that map a 1-D grid onto (unit, split), the combine kernel and the
 // launchers.  The work itself is in kvq_decode_core.h.
+#include <mutex>
+
 #include "kvq_decode_core.h"
+
+// Partials of kvq_decode_attention_noalloc: device memory that no call
+// allocates.  Each GPU the library runs on holds its own copy until the
+// process ends; every no-allocation call on that GPU shares it.
+static __device__ __align__(256) uint8_t scratch[kvq::kStaticScratchBytes];
 
 namespace kvq {
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
 
 // 1-D grid of kDecodeWaves-wave workgroups: every page split of every
 // (sequence, KV head) first, then the window splits, so the hardware places
@@ -212,6 +223,25 @@ int slots1(int g, int k) {
 }
 
 }  // namespace
+
+// Device address of the current device's `scratch`, looked up once per device
+// (with that device current) and kept; the host-side name of the array is
+// only a stand-in and is never passed to a kernel.
+hipError_t static_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_dev[dev] = p;
+    }
+    *ptr = g_scratch_dev[dev];
+    return hipSuccess;
+}
 
 int decode_slots(const Geometry &G) {
     return G.dtype == F16 ? slots1<F16>(G.g, G.k) : slots1<BF16>(G.g, G.k);

@@ -578,6 +578,21 @@ int kvq_decode_attention(kvq_cache *c, const void *q, float *out, void *workspac
                                          c->ev_after, static_cast<hipStream_t>(stream)));
 }
 
+int kvq_decode_attention_noalloc(kvq_cache *c, const void *q, float *out, void *stream) {
+    if (!c || !q || !out) return KVQ_EINVAL;
+    if (!aligned16(q) || !aligned16(out)) return KVQ_EALIGN;
+    if (c->n_pages == 0 && c->n_res == 0) return KVQ_EEMPTY;
+    kvq::DecodePlan pl = plan_of(c);
+    pl.max_splits = pl.total_splits;  // partial stride: only the splits this launch writes
+    if (kvq::decode_workspace_bytes(c->G, pl.max_splits) > kvq::kStaticScratchBytes)
+        return KVQ_EWORKSPACE;
+    void *ws = nullptr;
+    if (kvq::static_scratch(&ws) != hipSuccess) return KVQ_EHIP;
+    return hip_status(kvq::launch_decode(c->G, c->mem, static_cast<const uint16_t *>(q), out, ws,
+                                         pl, nullptr, nullptr, -1, c->ev_before, c->ev_after,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int kvq_append_decode(kvq_cache *c, const void *k, const void *v, const void *q, float *out,
                       void *workspace, size_t ws_bytes, void *stream, int32_t *flushed) {
     if (!c || !k || !v || !q || !out || !workspace) return KVQ_EINVAL;

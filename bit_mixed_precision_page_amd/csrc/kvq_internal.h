@@ -189,6 +189,10 @@ int decode_slots(const Geometry &G);
 // knew, vnew ([B][Hkv][D]) and slot >= 0: the newest window token (slot) is
 // read from knew / vnew and written into the window by the kernel itself (a
 // fused append); slot = -1: the window is read as it is.
+// Bytes of the static partials buffer of the no-allocation decode call, and
+// its device address on the current device.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(void **ptr);
 hipError_t launch_decode(const Geometry &G, uint8_t *cache, const uint16_t *q,
                          float *out, void *workspace, const DecodePlan &plan,
                          const uint16_t *knew, const uint16_t *vnew, int slot,

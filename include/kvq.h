@@ -138,6 +138,21 @@ int kvq_decode_workspace_bytes(const kvq_cache *cache, size_t *bytes);
 int kvq_decode_attention(kvq_cache *cache, const void *q, float *out, void *workspace,
                          size_t ws_bytes, void *stream);
 
+/* kvq_decode_attention for callers that cannot allocate device memory (code
+   under HIP graph capture, tight serving loops, harnesses that forbid
+   allocation): the same kernels and the same output, bit for bit, with the
+   split partials in a static device buffer of KVQ_NOALLOC_SCRATCH_BYTES that
+   the library holds per GPU until the process ends, instead of a caller's
+   workspace.  No allocation of any kind happens in the call.  It needs
+   B * Hq * (splits of this call) * 520 bytes (splits = page splits + window
+   splits, kvq_get_decode_splits + ceil(n_res / 128)); a call that would need
+   more returns KVQ_EWORKSPACE before any launch.  Every no-allocation call on
+   one GPU shares that buffer: calls that overlap on one GPU (several streams
+   or threads) race and must be ordered by the caller.  Errors: KVQ_EINVAL,
+   KVQ_EALIGN, KVQ_EEMPTY, KVQ_EWORKSPACE, KVQ_EHIP. */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int kvq_decode_attention_noalloc(kvq_cache *cache, const void *q, float *out, void *stream);
+
 /* One decode step in fewer launches (NEXT-2 of the design: fused append and
    decode): exactly kvq_append_token(k, v, &flushed) followed by
    kvq_decode_attention(q, out, ...), with the same arguments, results (cache
