@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the graph-replayed step (kvq_append_decode_device captured once "
                          "per layer replica)")
+    ap.add_argument("--lean", action="store_true",
+                    help="headline phase only (no per-step timestamps, graph step, bandwidth "
+                         "probes or CPU baseline): the run a profiler wraps")
     ap.add_argument("--query-aware", action="store_true",
                     help="rank Key channels by group range x query relevance (relevance of "
                          "the first decode query) instead of magnitude")
@@ -190,6 +193,8 @@ def dtype_name(gen, w):
 
 def main():
     a = parse()
+    if a.lean:
+        a.graph, a.no_cpu_baseline = False, True
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
               "(the path would shard by (sequence, KV head), with no exchange between GPUs)",
@@ -269,7 +274,7 @@ def main():
     timed = [i for i in range(a.steps) if a.event_every > 0 and i % a.event_every == 0]
     hev = HipEvents(len(timed), a.event_fence)
     ev_of = {i: hev.pair(j) for j, i in enumerate(timed)}
-    hall = HipEvents(a.steps, a.event_fence)  # every step's split kernel (distribution phase)
+    hall = None if a.lean else HipEvents(a.steps, a.event_fence)  # every step's split kernel
     torch.cuda.synchronize()
     print(f"[bench] setup {time.time() - t0:.1f}s; {layers} layer replicas of "
           f"{base.nbytes / 1e6:.1f} MB (replica bytes {base.nbytes}); state {n_pages0} pages + "
@@ -333,26 +338,28 @@ def main():
     # -- phase 2 (distribution): the next K steps with every split kernel's
     # dispatch timestamps; a step = from one split kernel's start to the
     # next's (its combine, and the next step's flush when there is one)
-    flush_at = []
-    for i in range(a.steps):
-        s = a.steps + i
-        f, _, _ = step(s, hall.pair(i))
-        flush_at.append(bool(f))
-    torch.cuda.synchronize()
-    kern_all = np.array([hall.elapsed_ms(j) for j in range(a.steps)]) * 1e3
-    gaps = []
-    for i in range(a.steps - 1):
-        ms_i = hall.ct.c_float()
-        hall.hip.hipEventElapsedTime(hall.ct.byref(ms_i), hall.ev[2 * i], hall.ev[2 * (i + 1)])
-        gaps.append(ms_i.value * 1e3)
-    gaps = np.array(gaps)
-    fl = np.array(flush_at[1:])  # interval i holds the flush of step i + 1
-    # (the timestamps themselves widen each step a little: "mean" beside
-    # ms_per_step shows by how much)
-    step_dist = {"from": "split kernel start to the next step's start, per-step dispatch "
-                         "timestamps", "mean": round(float(gaps.mean()), 2),
-                 "non_flush": pctl(gaps[~fl]), "flush": pctl(gaps[fl]),
-                 "split_kernel": pctl(kern_all[~np.array(flush_at)])}
+    step_dist = None
+    if not a.lean:
+        flush_at = []
+        for i in range(a.steps):
+            s = a.steps + i
+            f, _, _ = step(s, hall.pair(i))
+            flush_at.append(bool(f))
+        torch.cuda.synchronize()
+        kern_all = np.array([hall.elapsed_ms(j) for j in range(a.steps)]) * 1e3
+        gaps = []
+        for i in range(a.steps - 1):
+            ms_i = hall.ct.c_float()
+            hall.hip.hipEventElapsedTime(hall.ct.byref(ms_i), hall.ev[2 * i], hall.ev[2 * (i + 1)])
+            gaps.append(ms_i.value * 1e3)
+        gaps = np.array(gaps)
+        fl = np.array(flush_at[1:])  # interval i holds the flush of step i + 1
+        # (the timestamps themselves widen each step a little: "mean" beside
+        # ms_per_step shows by how much)
+        step_dist = {"from": "split kernel start to the next step's start, per-step dispatch "
+                             "timestamps", "mean": round(float(gaps.mean()), 2),
+                     "non_flush": pctl(gaps[~fl]), "flush": pctl(gaps[fl]),
+                     "split_kernel": pctl(kern_all[~np.array(flush_at)])}
 
     # -- graph-replayed step (kvq_append_decode_device captured once per
     # layer replica): the launch-floor comparison
@@ -383,8 +390,10 @@ def main():
         assert not any(err_flags), "a graph-replayed step found its cache full"
         print(f"[bench] graph-replayed steps: {graph_us:.1f} us/step", file=sys.stderr, flush=True)
 
-    copy_gbs = copy_bandwidth(torch, dev, 1 << 30)
-    read_gbs = read_bandwidth(torch, dev, 1 << 30)
+    copy_gbs = read_gbs = None
+    if not a.lean:
+        copy_gbs = copy_bandwidth(torch, dev, 1 << 30)
+        read_gbs = read_bandwidth(torch, dev, 1 << 30)
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -427,10 +436,10 @@ def main():
         "flushes": n_flush,
         "step_us": step_dist,
         "graph_step_us": round(graph_us, 2) if graph_us else None,
-        "copy_gbs": round(copy_gbs, 1),
-        "pct_copy_bw": round(100.0 * achieved / copy_gbs, 2),
-        "read_gbs": round(read_gbs, 1),
-        "pct_read_bw": round(100.0 * achieved / read_gbs, 2),
+        "copy_gbs": round(copy_gbs, 1) if copy_gbs else None,
+        "pct_copy_bw": round(100.0 * achieved / copy_gbs, 2) if copy_gbs else None,
+        "read_gbs": round(read_gbs, 1) if read_gbs else None,
+        "pct_read_bw": round(100.0 * achieved / read_gbs, 2) if read_gbs else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "kernel_us": round(kern_avg_s * 1e6, 2), "traffic": traffic},
@@ -480,6 +489,8 @@ def stream_main(a, w, torch, gen, kvq):
     q_out = units * bulk * pb
     del scratch, Kd, Vd
     layers = max(2, math.ceil(a.rotate_bytes / base.nbytes))
+    print(f"[bench] {layers} layer replicas (replica bytes {base.nbytes})", file=sys.stderr,
+          flush=True)
     caches = [base]
     for _ in range(layers - 1):
         c = kvq.Cache(cfg, device=dev)
