@@ -15,7 +15,8 @@ Counter scaling: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are divided by
 what they read for the runtime's device-to-device copy kernel
 (__amd_rocclr_copyBuffer) on the benchmark's cache replicas, whose size is
 known exactly (one replica per copy, read once and written once; the
-benchmark prints it as "replica bytes").
+benchmark prints it as "replica bytes"); copies of small host transfers,
+which the runtime also stages through that kernel, are left out.
 """
 import csv
 import glob
@@ -65,8 +66,12 @@ def trace(d, workload, command):
     return out
 
 
-def counter_means(d, counter, split):
-    """Mean counter value per dispatch of the split kernel and of the copy kernel."""
+def counter_means(d, counter, split, copy_kib):
+    """Mean counter value per dispatch of the split kernel and of the copy
+    kernel's replica copies.  Only copies whose counter reads at least a
+    quarter of the replica size count: the runtime also runs its copy kernel
+    for small host-to-device transfers through staging memory, which read
+    host memory and would dilute the calibration."""
     vals = {split: [], COPY: []}
     for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(path)):
@@ -74,7 +79,10 @@ def counter_means(d, counter, split):
                 continue
             for key in vals:
                 if key in r["Kernel_Name"]:
-                    vals[key].append(float(r["Counter_Value"]))
+                    v = float(r["Counter_Value"])
+                    if key == COPY and v < 0.25 * copy_kib:
+                        continue
+                    vals[key].append(v)
     for key, v in vals.items():
         if not v:
             raise SystemExit(f"no {counter} samples for {key} under {d}")
@@ -83,9 +91,9 @@ def counter_means(d, counter, split):
 
 def pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, copy_bytes,
         split="decode_split_kernel"):
-    f, nf = counter_means(fetch_dir, "FETCH_SIZE", split)
-    w, nw = counter_means(write_dir, "WRITE_SIZE", split)
     copy_kib = copy_bytes / 1024.0
+    f, nf = counter_means(fetch_dir, "FETCH_SIZE", split, copy_kib)
+    w, nw = counter_means(write_dir, "WRITE_SIZE", split, copy_kib)
     f_scale = copy_kib / f[COPY]
     w_scale = copy_kib / w[COPY]
     fetch_b = f[split] * f_scale * 1024.0
