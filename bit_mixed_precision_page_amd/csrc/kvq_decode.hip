@@ -22,16 +22,27 @@ void *g_scratch_dev[kMaxDevices] = {};
 // the long page workgroups evenly and the short window workgroups run as
 // they drain.
 //
+// Counters of a graph-replayed step after its token: a full window was
+// flushed into page n_pages by the step's flush launch (when a page was
+// free), and the new token takes the next window slot; without a free page
+// the step leaves the cache as it is (room = false).
+__device__ __forceinline__ void step_state(int np, int nr, int max_pages, int *n_pages, int *n_res,
+                                           bool *room) {
+    const bool full = nr == R;
+    *room = !full || np < max_pages;
+    *n_pages = full && *room ? np + 1 : np;
+    *n_res = full ? (*room ? 1 : R) : nr + 1;
+}
+
 // dstate != null: a step whose counters live in device memory (dstate =
-// {pages, window tokens, finished-workgroup count, error}), so that its
+// {pages, window tokens, unused (0), error}), so that its
 // launches have the same arguments at every step and can be replayed from a
 // captured graph.  The kernel derives the step's state (a full window was
 // flushed by the preceding quantize launch; the new token takes the next
-// window slot), covers the pages with page_splits splits of
+// window slot) and covers the pages with page_splits splits of
 // ceil(4 pages / (page_splits kDecodeWaves)) groups per wave (empty runs and
-// window waves past the
-// last token write empty partials) and the last workgroup to finish stores
-// the new counters.
+// window waves past the last token write empty partials); the step's combine
+// launch stores the new counters.
 template <int DT, int G, int KH>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(waves_target(G, KH)))) void decode_split_kernel(
     const uint8_t *__restrict__ cache, uint8_t *__restrict__ window_w,
@@ -40,13 +51,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     float *__restrict__ ws_acc, int Hkv, int max_pages, uint32_t page_bytes, int k,
     size_t res_base, int n_pages, int n_res, int page_splits, int gps, int win_splits, int max_splits,
     float qscale, int32_t *__restrict__ dstate) {
-    bool room = true;
     if (dstate) {
-        const int np = dstate[0], nr = dstate[1];
-        const bool full = nr == R;
-        room = !full || np < max_pages;
-        n_pages = full && room ? np + 1 : np;
-        n_res = full ? (room ? 1 : R) : nr + 1;
+        bool room;
+        step_state(dstate[0], dstate[1], max_pages, &n_pages, &n_res, &room);
         slot = room ? n_res - 1 : -1;
         gps = max(1, (4 * n_pages + page_splits * kDecodeWaves - 1) / (page_splits * kDecodeWaves));
     }
@@ -56,16 +63,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     split_body<DT, G, KH, false, kDecodeWaves>(cache, window_w, knew, vnew, slot, q, ws_ml, ws_acc, Hkv,
                                  max_pages, page_bytes, k, res_base, n_pages, n_res, page_splits,
                                  gps, max_splits, qscale, unit, split, nullptr);
-    if (dstate && threadIdx.x == 0) {
-        // every other workgroup has finished (and read dstate at its start)
-        // when the count reaches the grid size
-        if (atomicAdd(reinterpret_cast<unsigned *>(dstate + 2), 1u) == gridDim.x - 1) {
-            dstate[0] = n_pages;
-            dstate[1] = n_res;
-            dstate[2] = 0;
-            if (!room) dstate[3] = 1;
-        }
-    }
+}
+
+// The combine launch of a graph-replayed step advances the device counters
+// (the split kernel, which read them, has finished; the next step's flush
+// launch reads the new ones).
+__device__ __forceinline__ void advance_state(int32_t *dstate, int max_pages) {
+    int n_pages, n_res;
+    bool room;
+    step_state(dstate[0], dstate[1], max_pages, &n_pages, &n_res, &room);
+    dstate[0] = n_pages;
+    dstate[1] = n_res;
+    if (!room) dstate[3] = 1;
 }
 
 // Device counters for graph-replayed steps.
@@ -81,8 +90,10 @@ template <int PER, int CPL>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *__restrict__ ws_ml,
                                                                   const float *__restrict__ ws_acc,
                                                                   float *__restrict__ out, int n,
-                                                                  int max_splits) {
+                                                                  int max_splits, int32_t *dstate,
+                                                                  int max_pages) {
     constexpr int kSlices = D / (32 * CPL);
+    if (dstate && blockIdx.x == 0 && threadIdx.x == 0) advance_state(dstate, max_pages);
     combine_body<PER, CPL>(ws_ml, ws_acc, out, n, max_splits, blockIdx.x / kSlices,
                            blockIdx.x % kSlices);
 }
@@ -96,7 +107,9 @@ template <int NMAX>
 __global__ __launch_bounds__(256) void combine_wave_kernel(const float *__restrict__ ws_ml,
                                                            const float *__restrict__ ws_acc,
                                                            float *__restrict__ out, int rows, int n,
-                                                           int max_splits) {
+                                                           int max_splits, int32_t *dstate,
+                                                           int max_pages) {
+    if (dstate && blockIdx.x == 0 && threadIdx.x == 0) advance_state(dstate, max_pages);
     const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
@@ -125,17 +138,17 @@ __global__ __launch_bounds__(256) void combine_wave_kernel(const float *__restri
 
 template <int NMAX>
 hipError_t launch_combine_wave(int rows, const float *ml, const float *acc, float *out, int n,
-                               int max_splits, hipStream_t st) {
+                               int max_splits, int32_t *dstate, int max_pages, hipStream_t st) {
     hipLaunchKernelGGL((combine_wave_kernel<NMAX>), dim3((rows + 3) / 4), dim3(256), 0, st, ml, acc,
-                       out, rows, n, max_splits);
+                       out, rows, n, max_splits, dstate, max_pages);
     return hipGetLastError();
 }
 
 template <int PER, int CPL>
 hipError_t launch_combine(int rows, const float *ml, const float *acc, float *out, int n,
-                          int max_splits, hipStream_t st) {
+                          int max_splits, int32_t *dstate, int max_pages, hipStream_t st) {
     hipLaunchKernelGGL((combine_kernel<PER, CPL>), dim3(rows * (D / (32 * CPL))),
-                       dim3(kCombineThreads), 0, st, ml, acc, out, n, max_splits);
+                       dim3(kCombineThreads), 0, st, ml, acc, out, n, max_splits, dstate, max_pages);
     return hipGetLastError();
 }
 
@@ -270,16 +283,16 @@ hipError_t launch_decode(const Geometry &G, uint8_t *cache, const uint16_t *q,
                        : launch1<BF16>(G, cache, kn, vn, slot, q, ml, acc, pl, ev_before, ev_after, st);
     if (e != hipSuccess) return e;
     const int rows = G.B * G.Hq;
-    if (pl.total_splits <= 16)
-        return launch_combine_wave<16>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st);
-    if (pl.total_splits <= 32)
-        return launch_combine_wave<32>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st);
-    const CombineShape cs = combine_shape(rows, pl.total_splits);
+    const int n = pl.total_splits, ms = pl.max_splits, mp = G.max_pages;
+    int32_t *ds = pl.dstate;
+    if (n <= 16) return launch_combine_wave<16>(rows, ml, acc, out, n, ms, ds, mp, st);
+    if (n <= 32) return launch_combine_wave<32>(rows, ml, acc, out, n, ms, ds, mp, st);
+    const CombineShape cs = combine_shape(rows, n);
     if (cs.cpl == 4)
-        return cs.per == 8 ? launch_combine<8, 4>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st)
-                           : launch_combine<kCombinePerMax, 4>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st);
-    return cs.per == 8 ? launch_combine<8, 1>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st)
-                       : launch_combine<kCombinePerMax, 1>(rows, ml, acc, out, pl.total_splits, pl.max_splits, st);
+        return cs.per == 8 ? launch_combine<8, 4>(rows, ml, acc, out, n, ms, ds, mp, st)
+                           : launch_combine<kCombinePerMax, 4>(rows, ml, acc, out, n, ms, ds, mp, st);
+    return cs.per == 8 ? launch_combine<8, 1>(rows, ml, acc, out, n, ms, ds, mp, st)
+                       : launch_combine<kCombinePerMax, 1>(rows, ml, acc, out, n, ms, ds, mp, st);
 }
 
 }  // namespace kvq

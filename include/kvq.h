@@ -164,14 +164,14 @@ int kvq_append_decode(kvq_cache *cache, const void *k, const void *v, const void
                       void *workspace, size_t ws_bytes, void *stream, int32_t *flushed);
 
 /* Graph-replayable decode step (same launches, same arguments, every step).
-   dev_state: device int32[4] = {pages, window tokens, internal counter (0),
-   error flag}, 16-byte aligned, owned by the caller.
+   dev_state: device int32[4] = {pages, window tokens, unused (0), error flag},
+   16-byte aligned, owned by the caller.
    kvq_device_state_init writes the handle's host counters into dev_state (a
    kernel launch, so it may itself be captured).
    kvq_append_decode_device is kvq_append_decode with the counters read from
    and advanced in dev_state by the kernels themselves: a window flush launch
-   that acts only when the window is full, then the attention launches, whose
-   last finishing workgroup stores the new counters.  Its page split count is
+   that acts only when the window is full, then the attention launches, the
+   last of which (the split merge) stores the new counters.  Its page split count is
    fixed at the call (kvq_set_decode_splits, else one round of resident waves
    for the host counters at that moment), so the launches it records into a
    HIP graph stay valid for any later state.  The host counters of the handle
