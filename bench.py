@@ -17,8 +17,9 @@ elapsed time (GB/s); step_us = per-step percentiles (from the split kernel's
 own dispatch timestamps on a second run of as many steps), flush steps apart;
 graph_step_us = the same step replayed from a captured HIP graph; roofline =
 the split decode kernel's algorithmic bytes per launch / its average launch
-time; copy_gbs = a measured 1 GiB device copy; cpu_baseline = the CPU oracle
-on the same cache.
+time; copy_gbs and read_gbs = the library's bandwidth probe copying and
+reading 1 GiB (the measured reference beside the 8 TB/s specification);
+cpu_baseline = the CPU oracle on the same cache.
 """
 import argparse
 import json
@@ -143,40 +144,27 @@ def staggered_windows(L):
     return [max(1, 128 - (128 * i + 64) // L) for i in range(L)]
 
 
-def copy_bandwidth(torch, dev, nbytes, reps=5):
-    """Device-to-device copy of nbytes: read + written bytes / time (GB/s),
-    the best of `reps` copies."""
-    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+def probe_bandwidth(torch, kvq, dev, nbytes, reps=5):
+    """The library's bandwidth probe over nbytes of HBM (kvq_probe_bandwidth):
+    (copy GB/s counting bytes read + written, read-only GB/s), best of
+    `reps` each."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    best = float("inf")
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        best = min(best, e0.elapsed_time(e1))
+    sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+    out = []
+    for mode, moved in ((1, 2 * nbytes), (0, nbytes)):
+        kvq.kvq_probe_bandwidth(mode, src, dst if mode == 1 else sink, nbytes)
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            kvq.kvq_probe_bandwidth(mode, src, dst if mode == 1 else sink, nbytes)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        out.append(moved / (best / 1e3) / 1e9)
     del src, dst
-    return 2 * nbytes / (best / 1e3) / 1e9
-
-
-def read_bandwidth(torch, dev, nbytes, reps=5):
-    """Read-only stream of nbytes (a float32 sum of a 1 GiB tensor): bytes /
-    time (GB/s), the best of `reps` -- the bandwidth a kernel that only reads
-    can reach, beside the copy's read + write."""
-    x = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
-    x.sum()
-    best = float("inf")
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        x.sum()
-        e1.record()
-        torch.cuda.synchronize()
-        best = min(best, e0.elapsed_time(e1))
-    del x
-    return nbytes / (best / 1e3) / 1e9
+    return out[0], out[1]
 
 
 def pctl(x):
@@ -392,8 +380,7 @@ def main():
 
     copy_gbs = read_gbs = None
     if not a.lean:
-        copy_gbs = copy_bandwidth(torch, dev, 1 << 30)
-        read_gbs = read_bandwidth(torch, dev, 1 << 30)
+        copy_gbs, read_gbs = probe_bandwidth(torch, kvq, dev, 1 << 30)
 
     cpu = None
     if not a.no_cpu_baseline:

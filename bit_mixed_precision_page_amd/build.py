@@ -16,7 +16,7 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["kvq_host.cpp", "kvq_quantize.hip", "kvq_decode.hip", "kvq_pool.hip",
-           "kvq_prefill.hip"]
+           "kvq_prefill.hip", "kvq_probe.hip"]
 # The decode kernels never produce or test NaNs; without NaN semantics
 # fmaxf needs no quieting of its operands and fuses with cross-lane DPP moves.
 PER_FILE = {"kvq_decode.hip": ["-fno-honor-nans"], "kvq_pool.hip": ["-fno-honor-nans"],

@@ -1108,6 +1108,12 @@ int kvq_pool_set_kernel_events(kvq_pool *p, void *before, void *after) {
     return KVQ_OK;
 }
 
+int kvq_probe_bandwidth(int32_t mode, const void *src, void *dst, size_t bytes, void *stream) {
+    if ((mode != 0 && mode != 1) || !src || !dst || bytes == 0 || bytes % 16) return KVQ_EINVAL;
+    if (!aligned16(src) || !aligned16(dst)) return KVQ_EALIGN;
+    return hip_status(kvq::launch_probe(mode, src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
 const char *kvq_strerror(int code) {
     switch (code) {
         case KVQ_OK: return "ok";

@@ -189,6 +189,9 @@ int decode_slots(const Geometry &G);
 // knew, vnew ([B][Hkv][D]) and slot >= 0: the newest window token (slot) is
 // read from knew / vnew and written into the window by the kernel itself (a
 // fused append); slot = -1: the window is read as it is.
+// Bandwidth probe: mode 0 streams `bytes` of src (a 4-byte sink in dst),
+// mode 1 copies them to dst.
+hipError_t launch_probe(int mode, const void *src, void *dst, size_t bytes, hipStream_t stream);
 // Bytes of the static partials buffer of the no-allocation decode call, and
 // its device address on the current device.
 constexpr size_t kStaticScratchBytes = (size_t)32 << 20;

@@ -34,7 +34,7 @@ EXPORTS = ["kvq_cache_bytes", "kvq_page_bytes", "kvq_cache_create", "kvq_cache_d
            "kvq_device_state_init", "kvq_append_decode_device",
            "kvq_prefill_workspace_bytes", "kvq_prefill_select", "kvq_prefill_set_kernel_events",
            "kvq_prefill_set_max_key_splits", "kvq_check_decode_plan",
-           "kvq_pool_check_decode_plan", "kvq_decode_attention_noalloc"]
+           "kvq_pool_check_decode_plan", "kvq_decode_attention_noalloc", "kvq_probe_bandwidth"]
 
 
 class KvqError(RuntimeError):
@@ -104,6 +104,7 @@ _SIG = {
     "kvq_prefill_set_kernel_events": [_vp, _vp],
     "kvq_prefill_set_max_key_splits": [_i32],
     "kvq_decode_attention_noalloc": [_vp, _vp, _vp, _vp],
+    "kvq_probe_bandwidth": [_i32, _vp, _vp, _sz, _vp],
     "kvq_check_decode_plan": [_vp, _i32, _i32, _sz, ctypes.c_char_p, _sz],
     "kvq_pool_check_decode_plan": [_vp, _i32, _i32, _sz, ctypes.c_char_p, _sz],
     "kvq_set_channel_relevance": [_vp, _vp],
@@ -415,6 +416,12 @@ def kvq_prefill_set_kernel_events(before, after):
 def kvq_decode_attention_noalloc(handle, q, out, stream=None):
     _check(_L.kvq_decode_attention_noalloc(handle, _ptr(q), _ptr(out), _stream(stream)),
            "kvq_decode_attention_noalloc")
+
+
+def kvq_probe_bandwidth(mode, src, dst, nbytes, stream=None):
+    """Bandwidth probe: mode 0 reads src, mode 1 copies src to dst."""
+    _check(_L.kvq_probe_bandwidth(mode, _ptr(src), _ptr(dst), nbytes, _stream(stream)),
+           "kvq_probe_bandwidth")
 
 
 def kvq_check_decode_plan(handle, mode, slots, ws_bytes):

@@ -265,6 +265,14 @@ int kvq_set_kernel_events(kvq_cache *cache, void *before, void *after);
 /* Static description of an error code. */
 const char *kvq_strerror(int code);
 
+/* Bandwidth probe, the measured reference for the decode kernels' HBM rates:
+   mode 0 reads `bytes` of src once with 16-byte loads (dst: a device word
+   that is almost never written), mode 1 copies src to dst (both `bytes`
+   long).  bytes must be a positive multiple of 16; 16-byte aligned device
+   pointers; asynchronous on the stream.  Errors: KVQ_EINVAL, KVQ_EALIGN,
+   KVQ_EHIP. */
+int kvq_probe_bandwidth(int32_t mode, const void *src, void *dst, size_t bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * Block pool: variable-length batches (a page pool with a block table, as
  * in paged attention; Kitty abstract: page-centric layout).
