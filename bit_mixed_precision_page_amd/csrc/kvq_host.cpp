@@ -473,6 +473,54 @@ int prefill_shape_ok(int32_t T, int32_t Hq, int32_t Hkv) {
     return T >= 1 && T <= kPrefillMaxT && Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 &&
            Hq / Hkv <= 16 && (int64_t)Hq * T * kvq::D <= (int64_t)1 << 31;
 }
+// Runtime debugging switches, read once from the environment:
+//   KVQ_CHECK=1  every decode call first walks its launch with the extent
+//                check (check_dense / check_pool) and is refused with
+//                KVQ_EINVAL, before anything is launched, on a violation;
+//   KVQ_TRACE=1  one line per call on stderr (entry point, shape, counters,
+//                split plan).
+struct DebugFlags {
+    bool check, trace;
+};
+bool env_on(const char *name) {
+    const char *v = std::getenv(name);
+    return v && *v && *v != '0';
+}
+const DebugFlags &debug_flags() {
+    static const DebugFlags f{env_on("KVQ_CHECK"), env_on("KVQ_TRACE")};
+    return f;
+}
+int debug_dense(const char *who, const kvq_cache *c, const kvq::DecodePlan &pl, int np, int nr,
+                int gps, size_t ws_bytes) {
+    const DebugFlags &f = debug_flags();
+    if (f.trace)
+        std::fprintf(stderr, "[kvq] %s: B=%d Hq=%d Hkv=%d k=%d pages=%d window=%d splits=%d+%d "
+                     "groups/wave=%d\n", who, c->G.B, c->G.Hq, c->G.Hkv, c->G.k, np, nr,
+                     pl.page_splits, pl.total_splits - pl.page_splits, gps);
+    if (!f.check) return KVQ_OK;
+    char msg[256];
+    PlanCheck pc{msg, sizeof msg};
+    const int rc = check_dense(pc, c, pl, np, nr, gps, ws_bytes);
+    if (rc) std::fprintf(stderr, "[kvq] %s: launch refused (KVQ_CHECK): %s\n", who, msg);
+    return rc;
+}
+int debug_pool(const char *who, const kvq_pool *p, const kvq::PoolPlan &pl, size_t ws_bytes) {
+    const DebugFlags &f = debug_flags();
+    if (f.trace)
+        std::fprintf(stderr, "[kvq] %s: slots=%d Hq=%d Hkv=%d k=%d workgroups=%u+%u groups/split=%d\n",
+                     who, p->G.B, p->G.Hq, p->G.Hkv, p->G.k, pl.page_pref[pl.n_seq],
+                     (unsigned)pl.win_pref[pl.n_seq], pl.gps);
+    if (!f.check) return KVQ_OK;
+    char msg[256];
+    PlanCheck pc{msg, sizeof msg};
+    const int rc = check_pool(pc, p, pl, ws_bytes);
+    if (rc) std::fprintf(stderr, "[kvq] %s: launch refused (KVQ_CHECK): %s\n", who, msg);
+    return rc;
+}
+void debug_trace(const char *who, int a, int b, int c2) {
+    if (debug_flags().trace) std::fprintf(stderr, "[kvq] %s: %d %d %d\n", who, a, b, c2);
+}
+
 }  // namespace
 
 extern "C" {
@@ -535,6 +583,7 @@ int kvq_quantize_page(kvq_cache *c, const void *k, const void *v, int32_t n_page
         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return KVQ_EHIP;
     c->n_pages += n_pages;
+    debug_trace("kvq_quantize_page: new pages, pages, window", n_pages, c->n_pages, c->n_res);
     return KVQ_OK;
 }
 
@@ -556,6 +605,7 @@ int kvq_append_token(kvq_cache *c, const void *k, const void *v, void *stream,
     if (e != hipSuccess) return KVQ_EHIP;
     c->n_res += 1;
     if (flushed) *flushed = flush ? 1 : 0;
+    debug_trace("kvq_append_token: flushed, pages, window", flush ? 1 : 0, c->n_pages, c->n_res);
     return KVQ_OK;
 }
 
@@ -573,6 +623,8 @@ int kvq_decode_attention(kvq_cache *c, const void *q, float *out, void *workspac
         return KVQ_EWORKSPACE;
     if (c->n_pages == 0 && c->n_res == 0) return KVQ_EEMPTY;
     kvq::DecodePlan pl = plan_of(c);
+    if (debug_dense("kvq_decode_attention", c, pl, c->n_pages, c->n_res, pl.groups_per_split, ws_bytes))
+        return KVQ_EINVAL;
     return hip_status(kvq::launch_decode(c->G, c->mem, static_cast<const uint16_t *>(q), out,
                                          workspace, pl, nullptr, nullptr, -1, c->ev_before,
                                          c->ev_after, static_cast<hipStream_t>(stream)));
@@ -586,6 +638,9 @@ int kvq_decode_attention_noalloc(kvq_cache *c, const void *q, float *out, void *
     pl.max_splits = pl.total_splits;  // partial stride: only the splits this launch writes
     if (kvq::decode_workspace_bytes(c->G, pl.max_splits) > kvq::kStaticScratchBytes)
         return KVQ_EWORKSPACE;
+    if (debug_dense("kvq_decode_attention_noalloc", c, pl, c->n_pages, c->n_res,
+                    pl.groups_per_split, kvq::kStaticScratchBytes))
+        return KVQ_EINVAL;
     void *ws = nullptr;
     if (kvq::static_scratch(&ws) != hipSuccess) return KVQ_EHIP;
     return hip_status(kvq::launch_decode(c->G, c->mem, static_cast<const uint16_t *>(q), out, ws,
@@ -604,16 +659,25 @@ int kvq_append_decode(kvq_cache *c, const void *k, const void *v, const void *q,
     bool flush = c->n_res == kvq::R;
     if (flush && c->n_pages >= c->G.max_pages) return KVQ_ECAPACITY;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // the plan and the kernel see the window (flushed first when full) with
+    // the new token in it; the counters move only once the launches that
+    // flush and write the token succeeded
+    kvq_cache next = *c;
+    if (flush) {
+        next.n_pages += 1;
+        next.n_res = 0;
+    }
+    const int slot = next.n_res;
+    kvq::DecodePlan pl = plan_of(&next, slot + 1);
+    if (debug_dense("kvq_append_decode", &next, pl, next.n_pages, slot + 1, pl.groups_per_split,
+                    ws_bytes))
+        return KVQ_EINVAL;
     if (flush) {
         hipError_t e = kvq::launch_flush_window(c->G, c->mem, c->n_pages, c->rel, st);
         if (e != hipSuccess) return KVQ_EHIP;
         c->n_pages += 1;
         c->n_res = 0;
     }
-    // the plan and the kernel see the window with the new token in it; the
-    // counter moves only once the launch that writes the token succeeded
-    const int slot = c->n_res;
-    kvq::DecodePlan pl = plan_of(c, c->n_res + 1);
     hipError_t e = kvq::launch_decode(c->G, c->mem, static_cast<const uint16_t *>(q), out,
                                       workspace, pl, static_cast<const uint16_t *>(k),
                                       static_cast<const uint16_t *>(v), slot, c->ev_before,
@@ -642,6 +706,15 @@ int kvq_append_decode_device(kvq_cache *c, const void *k, const void *v, const v
         return KVQ_EWORKSPACE;
     kvq::DecodePlan pl = device_step_plan(c);
     pl.dstate = dev_state;
+    {
+        // the step the host counters describe (the device counters may have
+        // moved on; KVQ_CHECK walks the state they would have next)
+        const bool full = c->n_res == kvq::R && c->n_pages < c->G.max_pages;
+        const int np = full ? c->n_pages + 1 : c->n_pages;
+        const int nr = full ? 1 : std::min(c->n_res + 1, (int)kvq::R);
+        if (debug_dense("kvq_append_decode_device", c, pl, np, nr, device_step_gps(pl, np), ws_bytes))
+            return KVQ_EINVAL;
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = kvq::launch_flush_window_device(c->G, c->mem, dev_state, c->rel, st);
     if (e != hipSuccess) return KVQ_EHIP;
@@ -837,6 +910,7 @@ int kvq_prefill_select(int32_t dtype, int32_t T, int32_t num_q_heads, int32_t nu
     a.ev_before = g_prefill_ev_before;
     a.ev_after = g_prefill_ev_after;
     *n_keep = nk;
+    debug_trace("kvq_prefill_select: tokens, key chunks, kept", T, a.nsplit, nk);
     return hip_status(kvq::launch_prefill(dtype, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -1000,6 +1074,7 @@ int kvq_pool_decode_attention(kvq_pool *p, const void *q, float *out, void *work
     if (ws_bytes < kvq::decode_workspace_bytes(p->G, max_splits_of(p->G)))
         return KVQ_EWORKSPACE;
     const kvq::PoolPlan pl = pool_plan(p, nullptr);
+    if (debug_pool("kvq_pool_decode_attention", p, pl, ws_bytes)) return KVQ_EINVAL;
     return hip_status(kvq::launch_pool_decode(p->G, p->mem, pool_table(p),
                                               static_cast<const uint16_t *>(q), out, workspace,
                                               pl, nullptr, nullptr, p->ev_before, p->ev_after,
@@ -1015,6 +1090,13 @@ int kvq_pool_append_decode(kvq_pool *p, const void *k, const void *v, const void
     if (ws_bytes < kvq::decode_workspace_bytes(p->G, max_splits_of(p->G)))
         return KVQ_EWORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_flags().check) {  // the launch this call makes, walked before the flushes
+        char msg[256];
+        if (kvq_pool_check_decode_plan(p, 1, 0, ws_bytes, msg, sizeof msg)) {
+            std::fprintf(stderr, "[kvq] kvq_pool_append_decode: launch refused (KVQ_CHECK): %s\n", msg);
+            return KVQ_EINVAL;
+        }
+    }
     int32_t nf = 0;
     int rc = pool_flush_full(p, st, &nf);
     if (rc) return rc;
@@ -1024,6 +1106,7 @@ int kvq_pool_append_decode(kvq_pool *p, const void *k, const void *v, const void
     int slot_of[kvq::kPoolMaxSeqs];
     for (int b = 0; b < p->G.B; b++) slot_of[b] = p->live[b] ? p->n_res[b] : -1;
     const kvq::PoolPlan pl = pool_plan(p, slot_of);
+    if (debug_flags().trace) debug_pool("kvq_pool_append_decode", p, pl, ws_bytes);
     hipError_t e = kvq::launch_pool_decode(p->G, p->mem, pool_table(p),
                                            static_cast<const uint16_t *>(q), out, workspace, pl,
                                            static_cast<const uint16_t *>(k),

@@ -56,6 +56,12 @@
  * check happens before any launch, so a failed call changes no state.
  * Preconditions the library does not check: inputs are finite, and a group's
  * range (max - min) is finite in fp32.
+ *
+ * Debugging switches (environment, read once per process): KVQ_CHECK=1 makes
+ * every decode call walk its launch with the extent check of
+ * kvq_check_decode_plan first and refuse it with KVQ_EINVAL, before anything
+ * is launched, on a violation (the reason on stderr); KVQ_TRACE=1 prints one
+ * line per call on stderr (entry point, shape, counters, split plan).
  */
 #ifndef KVQ_H
 #define KVQ_H
