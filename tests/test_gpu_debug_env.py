@@ -1,7 +1,7 @@
 """The library's environment switches, in a child process of their own (they
 are read once per process): KVQ_TRACE=1 prints one line per call, and
-KVQ_CHECK=1 walks every decode launch before it runs without changing what
-the calls compute."""
+KVQ_CHECK=1 walks every decode launch (dense cache and block pool) before it
+runs without changing what the calls compute."""
 import os
 import subprocess
 import sys
@@ -28,8 +28,18 @@ for t in range(130):
     vt = torch.randn(B, Hkv, 128, device="cuda").bfloat16()
     c.append_decode(kt, vt, q, out)
 c.decode_attention(q, out)
+pool = kvq.Pool(kvq.config(B, Hq, Hkv, 16, 4, kvq.KVQ_BF16), 16)
+for s, n in ((0, 300), (1, 140)):
+    pool.prefill(s, torch.randn(Hkv, n, 128, device="cuda").bfloat16(),
+                 torch.randn(Hkv, n, 128, device="cuda").bfloat16())
+pout = torch.zeros(B, Hq, 128, device="cuda")
+for t in range(20):
+    pool.append_decode(torch.randn(B, Hkv, 128, device="cuda").bfloat16(),
+                       torch.randn(B, Hkv, 128, device="cuda").bfloat16(), q, pout)
+pool.decode_attention(q, pout)
 torch.cuda.synchronize()
-print("STATE", *c.state, float(out.double().abs().sum()), flush=True)
+print("STATE", *c.state, *pool.seq(0), *pool.seq(1), float(out.double().abs().sum()),
+      float(pout.double().abs().sum()), flush=True)
 """
 
 
@@ -55,9 +65,13 @@ def test_check_and_trace_switches():
     # the same counters and the same outputs, bit for bit (one process each,
     # the same seeded inputs and the same launches)
     assert checked == plain
-    assert plain.split()[1:3] == ["3", "2"]  # two pages quantized, one flush, 2 in the window
+    # dense cache: two pages quantized, one flush, 2 in the window; pool: 300 + 20 tokens
+    # (2 pages, 64 in the window) and 140 + 20 (1 page, 32)
+    assert plain.split()[1:9] == ["3", "2", "True", "2", "64", "True", "1", "32"]
     lines = [ln for ln in err1.splitlines() if ln.startswith("[kvq]")]
     assert not any("refused" in ln for ln in lines), lines
     assert sum("kvq_quantize_page" in ln for ln in lines) == 1
     assert sum("kvq_append_decode" in ln for ln in lines) == 130
     assert sum("kvq_decode_attention" in ln for ln in lines) == 1
+    assert sum("kvq_pool_append_decode" in ln for ln in lines) == 20
+    assert sum("kvq_pool_decode_attention" in ln for ln in lines) == 1
