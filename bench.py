@@ -525,20 +525,32 @@ def stream_main(a, w, torch, gen, kvq):
     torch.cuda.synchronize()
     flush_step = None
     bytes_steps, split_bytes = [], []
+    # launch arguments as plain integers, resolved once (the host then issues
+    # a layer step in little more than the C call itself)
+    sp = torch.cuda.current_stream().cuda_stream
+    kp = [t.data_ptr() for t in kts]
+    vp = [t.data_ptr() for t in vts]
+    qp = [t.data_ptr() for t in qs]
+    op = out.data_ptr()
+    hw = [(c.handle, c.ws.data_ptr(), c.ws_bytes) for c in caches]
+    # one untimed attention call (it changes no state) loads the kernels the
+    # steps launch, so the first timed step pays no one-time set-up
+    kvq.kvq_decode_attention(hw[0][0], qp[0], op, hw[0][1], hw[0][2], sp)
+    torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(w.decode_steps):
         evs[i][0].record()
-        for li, c in enumerate(caches):
+        for li, (h, wsp, wsb) in enumerate(hw):
             if li == 0:
-                kvq.kvq_set_kernel_events(c.handle, *hev.pair(i))
+                kvq.kvq_set_kernel_events(h, *hev.pair(i))
             if a.unfused:
-                flushed = c.append_token(kts[i], vts[i])
-                c.decode_attention(qs[i], out)
+                flushed = kvq.kvq_append_token(h, kp[i], vp[i], sp)
+                kvq.kvq_decode_attention(h, qp[i], op, wsp, wsb, sp)
             else:
-                flushed = c.append_decode(kts[i], vts[i], qs[i], out)
+                flushed = kvq.kvq_append_decode(h, kp[i], vp[i], qp[i], op, wsp, wsb, sp)
             if li == 0:
-                kvq.kvq_set_kernel_events(c.handle, None, None)
+                kvq.kvq_set_kernel_events(h, None, None)
         evs[i][1].record()
         if flushed:
             flush_step = i + 1
@@ -573,6 +585,8 @@ def stream_main(a, w, torch, gen, kvq):
         "step_us": {"p10": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
                     "median": round(float(np.median(step_ms)) * 1e3, 2),
                     "p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
+                    "first": round(float(step_ms[0]) * 1e3, 2),
+                    "max": round(float(step_ms.max()) * 1e3, 2),
                     "flush_step": flush_step,
                     "flush_step_us": round(float(step_ms[flush_step - 1]) * 1e3, 2)
                     if flush_step else None},
@@ -838,25 +852,48 @@ def pool_main(a, w, torch, gen, kvq):
     for s in range(a.warmup):
         pools[s % layers].append_decode(kts[s], vts[s], qs[s], out)
     torch.cuda.synchronize()
+    # launch arguments as plain integers, resolved once; the slots' counters
+    # tracked here (a full window is flushed before its token goes in) and
+    # checked against the library's after the timed steps
+    sp = torch.cuda.current_stream().cuda_stream
+    kp = [t.data_ptr() for t in kts]
+    vp = [t.data_ptr() for t in vts]
+    qp = [t.data_ptr() for t in qs]
+    op = out.data_ptr()
+    hw = [(p.handle, p.ws.data_ptr(), p.ws_bytes) for p in pools]
+    tracked = [[list(x) for x in seq_states(p)] for p in pools]
+
+    def track(states):
+        nf = 0
+        for e in states:
+            if e[0]:
+                if e[2] == PAGE:
+                    e[1], e[2], nf = e[1] + 1, 0, nf + 1
+                e[2] += 1
+        return nf
+
     total_bytes, split_bytes, n_flush = 0, [], 0
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(a.steps):
         s = a.warmup + i
-        p = pools[s % layers]
+        h, wsp, wsb = hw[s % layers]
         ev = ev_of.get(i)
         if ev is not None:
-            kvq.kvq_pool_set_kernel_events(p.handle, ev[0], ev[1])
-        nf = p.append_decode(kts[s], vts[s], qs[s], out)
+            kvq.kvq_pool_set_kernel_events(h, ev[0], ev[1])
+        nf = kvq.kvq_pool_append_decode(h, kp[s], vp[s], qp[s], op, wsp, wsb, sp)
         if ev is not None:
-            kvq.kvq_pool_set_kernel_events(p.handle, None, None)
-        att, app = step_bytes(seq_states(p), nf)
+            kvq.kvq_pool_set_kernel_events(h, None, None)
+        st = tracked[s % layers]
+        assert track(st) == nf
+        att, app = step_bytes(st, nf)
         total_bytes += att + app
         n_flush += nf
         if ev is not None:
             split_bytes.append(att - w.B * w.Hq * 128 * 4)
     end.record()
     torch.cuda.synchronize()
+    assert all([tuple(e) for e in tracked[li]] == seq_states(p) for li, p in enumerate(pools))
     ms = start.elapsed_time(end)
     ms_step = ms / a.steps
     kern_ms = np.array([hev.elapsed_ms(j) for j in range(len(timed))])

@@ -4,6 +4,7 @@
 #include <mutex>
 
 #include "kvq_decode_core.h"
+#include "kvq_quantize_core.h"
 
 // Partials of kvq_decode_attention_noalloc: device memory that no call
 // allocates.  Each GPU the library runs on holds its own copy until the
@@ -22,27 +23,29 @@ void *g_scratch_dev[kMaxDevices] = {};
 // the long page workgroups evenly and the short window workgroups run as
 // they drain.
 //
-// Counters of a graph-replayed step after its token: a full window was
-// flushed into page n_pages by the step's flush launch (when a page was
-// free), and the new token takes the next window slot; without a free page
-// the step leaves the cache as it is (room = false).
-__device__ __forceinline__ void step_state(int np, int nr, int max_pages, int *n_pages, int *n_res,
-                                           bool *room) {
-    const bool full = nr == R;
-    *room = !full || np < max_pages;
-    *n_pages = full && *room ? np + 1 : np;
-    *n_res = full ? (*room ? 1 : R) : nr + 1;
+// Counters of a graph-replayed step, in device memory:
+//   dstate[0], dstate[1]  pages and window tokens at the start of the step;
+//   dstate[3]             error flag (a token that found the cache full);
+//   dstate[4], dstate[5]  pages and window tokens after the step's append,
+//                         written by the split launch for the merge launch.
+// A step starts with room in its window unless the cache is full: a window
+// that a step fills is flushed into a page by that step's merge launch (the
+// flush the next step would otherwise start with).  The new token takes
+// window slot dstate[1]; with a full window (no free page was left) the step
+// skips it and raises the flag.
+__device__ __forceinline__ void step_state(int nr, int *slot, int *n_res, bool *room) {
+    *room = nr < R;
+    *slot = *room ? nr : -1;
+    *n_res = *room ? nr + 1 : R;
 }
 
-// dstate != null: a step whose counters live in device memory (dstate =
-// {pages, window tokens, unused (0), error}), so that its
+// dstate != null: a step whose counters live in device memory, so that its
 // launches have the same arguments at every step and can be replayed from a
-// captured graph.  The kernel derives the step's state (a full window was
-// flushed by the preceding quantize launch; the new token takes the next
-// window slot) and covers the pages with page_splits splits of
-// ceil(4 pages / (page_splits kDecodeWaves)) groups per wave (empty runs and
-// window waves past the last token write empty partials); the step's combine
-// launch stores the new counters.
+// captured graph.  The kernel derives the step's state and covers the pages
+// with page_splits splits of ceil(4 pages / (page_splits kDecodeWaves))
+// groups per wave (empty runs and window waves past the last token write
+// empty partials); its first thread records the counters after the append,
+// which no other workgroup of this launch reads.
 template <int DT, int G, int KH>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(waves_target(G, KH)))) void decode_split_kernel(
     const uint8_t *__restrict__ cache, uint8_t *__restrict__ window_w,
@@ -53,9 +56,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     float qscale, int32_t *__restrict__ dstate) {
     if (dstate) {
         bool room;
-        step_state(dstate[0], dstate[1], max_pages, &n_pages, &n_res, &room);
-        slot = room ? n_res - 1 : -1;
+        n_pages = dstate[0];
+        step_state(dstate[1], &slot, &n_res, &room);
         gps = max(1, (4 * n_pages + page_splits * kDecodeWaves - 1) / (page_splits * kDecodeWaves));
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            dstate[4] = n_pages;
+            dstate[5] = n_res;
+            if (!room) dstate[3] = 1;
+        }
     }
     const int n_units = gridDim.x / (page_splits + win_splits);
     int unit, split;
@@ -65,24 +73,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
                                  gps, max_splits, qscale, unit, split, nullptr);
 }
 
-// The combine launch of a graph-replayed step advances the device counters
-// (the split kernel, which read them, has finished; the next step's flush
-// launch reads the new ones).
-__device__ __forceinline__ void advance_state(int32_t *dstate, int max_pages) {
-    int n_pages, n_res;
-    bool room;
-    step_state(dstate[0], dstate[1], max_pages, &n_pages, &n_res, &room);
-    dstate[0] = n_pages;
-    dstate[1] = n_res;
-    if (!room) dstate[3] = 1;
-}
-
 // Device counters for graph-replayed steps.
 __global__ void state_init_kernel(int32_t *dstate, int n_pages, int n_res) {
+    for (int i = 0; i < kDeviceStateWords; i++) dstate[i] = 0;
     dstate[0] = n_pages;
     dstate[1] = n_res;
-    dstate[2] = 0;
-    dstate[3] = 0;
 }
 
 // D / (32 CPL) workgroups per output row.
@@ -90,10 +85,8 @@ template <int PER, int CPL>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *__restrict__ ws_ml,
                                                                   const float *__restrict__ ws_acc,
                                                                   float *__restrict__ out, int n,
-                                                                  int max_splits, int32_t *dstate,
-                                                                  int max_pages) {
+                                                                  int max_splits) {
     constexpr int kSlices = D / (32 * CPL);
-    if (dstate && blockIdx.x == 0 && threadIdx.x == 0) advance_state(dstate, max_pages);
     combine_body<PER, CPL>(ws_ml, ws_acc, out, n, max_splits, blockIdx.x / kSlices,
                            blockIdx.x % kSlices);
 }
@@ -104,13 +97,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *_
 // channels of each partial -- so a row costs one memory round trip, with no
 // LDS and no barrier.
 template <int NMAX>
-__global__ __launch_bounds__(256) void combine_wave_kernel(const float *__restrict__ ws_ml,
-                                                           const float *__restrict__ ws_acc,
-                                                           float *__restrict__ out, int rows, int n,
-                                                           int max_splits, int32_t *dstate,
-                                                           int max_pages) {
-    if (dstate && blockIdx.x == 0 && threadIdx.x == 0) advance_state(dstate, max_pages);
-    const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+__device__ __forceinline__ void combine_wave_body(const float *__restrict__ ws_ml,
+                                                  const float *__restrict__ ws_acc,
+                                                  float *__restrict__ out, int rows, int n,
+                                                  int max_splits, int wg) {
+    const int row = wg * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
     const float2 *ml = reinterpret_cast<const float2 *>(ws_ml + (size_t)row * max_splits * 2);
@@ -135,20 +126,106 @@ __global__ __launch_bounds__(256) void combine_wave_kernel(const float *__restri
     *reinterpret_cast<float2 *>(out + (size_t)row * D + 2 * lane) =
         den > 0.0f ? make_float2(ax / den, ay / den) : make_float2(0.0f, 0.0f);
 }
-
 template <int NMAX>
-hipError_t launch_combine_wave(int rows, const float *ml, const float *acc, float *out, int n,
-                               int max_splits, int32_t *dstate, int max_pages, hipStream_t st) {
-    hipLaunchKernelGGL((combine_wave_kernel<NMAX>), dim3((rows + 3) / 4), dim3(256), 0, st, ml, acc,
-                       out, rows, n, max_splits, dstate, max_pages);
+__global__ __launch_bounds__(256) void combine_wave_kernel(const float *__restrict__ ws_ml,
+                                                           const float *__restrict__ ws_acc,
+                                                           float *__restrict__ out, int rows, int n,
+                                                           int max_splits) {
+    combine_wave_body<NMAX>(ws_ml, ws_acc, out, rows, n, max_splits, blockIdx.x);
+}
+
+// Merge launch of a graph-replayed step: workgroups [0, n_merge) merge the
+// split partials exactly as the combine kernels do; workgroup n_merge + u
+// flushes unit u's window into page dstate[4] when the step filled it and a
+// page is free (the quantizer of the page launches).  Its first thread
+// stores the counters the next step starts from; the other workgroups read
+// only dstate[4], dstate[5], which the split launch wrote.
+struct StepFlush {
+    uint8_t *cache;
+    size_t res_base;
+    int max_pages, k;
+    uint32_t page_bytes;
+    const float *rel;  // [B][Hkv][D] or null
+};
+template <int DT>
+__device__ __forceinline__ void step_flush(const int32_t *dstate, const StepFlush &f, int unit) {
+    const int np = dstate[4], nr = dstate[5];
+    if (nr != R || np >= f.max_pages) return;  // workgroup-uniform
+    const uint16_t *kw = reinterpret_cast<const uint16_t *>(f.cache + f.res_base) +
+                         (size_t)unit * 2 * R * D;
+    uint8_t *pg = f.cache + ((size_t)unit * f.max_pages + np) * f.page_bytes;
+    qz::quantize_page_body<DT>(pg, kw, kw + (size_t)R * D, f.k,
+                               f.rel ? f.rel + (size_t)unit * D : nullptr);
+}
+__device__ __forceinline__ void step_advance(int32_t *dstate, int max_pages) {
+    const int np = dstate[4], nr = dstate[5];
+    const bool flush = nr == R && np < max_pages;
+    dstate[0] = flush ? np + 1 : np;
+    dstate[1] = flush ? 0 : nr;
+}
+static_assert(qz::kThreads == 256 && kCombineThreads == 256, "one workgroup shape for both roles");
+template <int DT, int NMAX>
+__global__ __launch_bounds__(256) void step_merge_wave_kernel(const float *__restrict__ ws_ml,
+                                                              const float *__restrict__ ws_acc,
+                                                              float *__restrict__ out, int rows,
+                                                              int n, int max_splits, int n_merge,
+                                                              int32_t *dstate, StepFlush f) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) step_advance(dstate, f.max_pages);
+    if ((int)blockIdx.x >= n_merge) return step_flush<DT>(dstate, f, blockIdx.x - n_merge);
+    combine_wave_body<NMAX>(ws_ml, ws_acc, out, rows, n, max_splits, blockIdx.x);
+}
+template <int DT, int PER, int CPL>
+__global__ __launch_bounds__(kCombineThreads) void step_merge_kernel(const float *__restrict__ ws_ml,
+                                                                     const float *__restrict__ ws_acc,
+                                                                     float *__restrict__ out, int n,
+                                                                     int max_splits, int n_merge,
+                                                                     int32_t *dstate, StepFlush f) {
+    constexpr int kSlices = D / (32 * CPL);
+    if (blockIdx.x == 0 && threadIdx.x == 0) step_advance(dstate, f.max_pages);
+    if ((int)blockIdx.x >= n_merge) return step_flush<DT>(dstate, f, blockIdx.x - n_merge);
+    combine_body<PER, CPL>(ws_ml, ws_acc, out, n, max_splits, blockIdx.x / kSlices,
+                           blockIdx.x % kSlices);
+}
+
+// Merge of the split partials; with a graph-replayed step (dstate) the
+// merge launch also flushes a window the step filled and advances the
+// counters (n_units more workgroups).
+struct MergeArgs {
+    int rows, n, max_splits, n_units;
+    int32_t *dstate;
+    StepFlush flush;
+};
+template <int NMAX>
+hipError_t launch_combine_wave(int dtype, const MergeArgs &m, const float *ml, const float *acc,
+                               float *out, hipStream_t st) {
+    const int wgs = (m.rows + 3) / 4;
+    if (!m.dstate)
+        hipLaunchKernelGGL((combine_wave_kernel<NMAX>), dim3(wgs), dim3(256), 0, st, ml, acc, out,
+                           m.rows, m.n, m.max_splits);
+    else if (dtype == F16)
+        hipLaunchKernelGGL((step_merge_wave_kernel<F16, NMAX>), dim3(wgs + m.n_units), dim3(256), 0,
+                           st, ml, acc, out, m.rows, m.n, m.max_splits, wgs, m.dstate, m.flush);
+    else
+        hipLaunchKernelGGL((step_merge_wave_kernel<BF16, NMAX>), dim3(wgs + m.n_units), dim3(256), 0,
+                           st, ml, acc, out, m.rows, m.n, m.max_splits, wgs, m.dstate, m.flush);
     return hipGetLastError();
 }
 
 template <int PER, int CPL>
-hipError_t launch_combine(int rows, const float *ml, const float *acc, float *out, int n,
-                          int max_splits, int32_t *dstate, int max_pages, hipStream_t st) {
-    hipLaunchKernelGGL((combine_kernel<PER, CPL>), dim3(rows * (D / (32 * CPL))),
-                       dim3(kCombineThreads), 0, st, ml, acc, out, n, max_splits, dstate, max_pages);
+hipError_t launch_combine(int dtype, const MergeArgs &m, const float *ml, const float *acc,
+                          float *out, hipStream_t st) {
+    const int wgs = m.rows * (D / (32 * CPL));
+    if (!m.dstate)
+        hipLaunchKernelGGL((combine_kernel<PER, CPL>), dim3(wgs), dim3(kCombineThreads), 0, st, ml,
+                           acc, out, m.n, m.max_splits);
+    else if (dtype == F16)
+        hipLaunchKernelGGL((step_merge_kernel<F16, PER, CPL>), dim3(wgs + m.n_units),
+                           dim3(kCombineThreads), 0, st, ml, acc, out, m.n, m.max_splits, wgs,
+                           m.dstate, m.flush);
+    else
+        hipLaunchKernelGGL((step_merge_kernel<BF16, PER, CPL>), dim3(wgs + m.n_units),
+                           dim3(kCombineThreads), 0, st, ml, acc, out, m.n, m.max_splits, wgs,
+                           m.dstate, m.flush);
     return hipGetLastError();
 }
 
@@ -282,17 +359,22 @@ hipError_t launch_decode(const Geometry &G, uint8_t *cache, const uint16_t *q,
         G.dtype == F16 ? launch1<F16>(G, cache, kn, vn, slot, q, ml, acc, pl, ev_before, ev_after, st)
                        : launch1<BF16>(G, cache, kn, vn, slot, q, ml, acc, pl, ev_before, ev_after, st);
     if (e != hipSuccess) return e;
-    const int rows = G.B * G.Hq;
-    const int n = pl.total_splits, ms = pl.max_splits, mp = G.max_pages;
-    int32_t *ds = pl.dstate;
-    if (n <= 16) return launch_combine_wave<16>(rows, ml, acc, out, n, ms, ds, mp, st);
-    if (n <= 32) return launch_combine_wave<32>(rows, ml, acc, out, n, ms, ds, mp, st);
-    const CombineShape cs = combine_shape(rows, n);
+    MergeArgs m{};
+    m.rows = G.B * G.Hq;
+    m.n = pl.total_splits;
+    m.max_splits = pl.max_splits;
+    m.n_units = G.B * G.Hkv;
+    m.dstate = pl.dstate;
+    m.flush = StepFlush{cache, G.res_base, G.max_pages, G.k, G.page_bytes, pl.rel};
+    const int dt = G.dtype;
+    if (m.n <= 16) return launch_combine_wave<16>(dt, m, ml, acc, out, st);
+    if (m.n <= 32) return launch_combine_wave<32>(dt, m, ml, acc, out, st);
+    const CombineShape cs = combine_shape(m.rows, m.n);
     if (cs.cpl == 4)
-        return cs.per == 8 ? launch_combine<8, 4>(rows, ml, acc, out, n, ms, ds, mp, st)
-                           : launch_combine<kCombinePerMax, 4>(rows, ml, acc, out, n, ms, ds, mp, st);
-    return cs.per == 8 ? launch_combine<8, 1>(rows, ml, acc, out, n, ms, ds, mp, st)
-                       : launch_combine<kCombinePerMax, 1>(rows, ml, acc, out, n, ms, ds, mp, st);
+        return cs.per == 8 ? launch_combine<8, 4>(dt, m, ml, acc, out, st)
+                           : launch_combine<kCombinePerMax, 4>(dt, m, ml, acc, out, st);
+    return cs.per == 8 ? launch_combine<8, 1>(dt, m, ml, acc, out, st)
+                       : launch_combine<kCombinePerMax, 1>(dt, m, ml, acc, out, st);
 }
 
 }  // namespace kvq

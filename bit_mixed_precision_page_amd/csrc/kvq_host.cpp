@@ -41,6 +41,7 @@ struct kvq_pool {
 
 namespace {
 
+static_assert(kvq::kDeviceStateWords == KVQ_DEVICE_STATE_WORDS, "device state size");
 constexpr int kMaxSplits = 256;  // page splits per (sequence, KV head)
 constexpr int kRoundGroups = 32;  // groups per split when one round of waves cannot hold every unit
 
@@ -691,8 +692,17 @@ int kvq_append_decode(kvq_cache *c, const void *k, const void *v, const void *q,
 int kvq_device_state_init(kvq_cache *c, int32_t *dev_state, void *stream) {
     if (!c || !dev_state) return KVQ_EINVAL;
     if (!aligned16(dev_state)) return KVQ_EALIGN;
-    return hip_status(kvq::launch_state_init(dev_state, c->n_pages, c->n_res,
-                                             static_cast<hipStream_t>(stream)));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // a replayed step starts with room in its window: a full one is flushed
+    // here, as the next step would start by doing (the host counters follow)
+    if (c->n_res == kvq::R && c->n_pages < c->G.max_pages) {
+        const hipError_t e = kvq::launch_flush_window(c->G, c->mem, c->n_pages, c->rel, st);
+        if (e != hipSuccess) return KVQ_EHIP;
+        c->n_pages += 1;
+        c->n_res = 0;
+    }
+    debug_trace("kvq_device_state_init: pages, window, -", c->n_pages, c->n_res, 0);
+    return hip_status(kvq::launch_state_init(dev_state, c->n_pages, c->n_res, st));
 }
 
 int kvq_append_decode_device(kvq_cache *c, const void *k, const void *v, const void *q,
@@ -706,6 +716,7 @@ int kvq_append_decode_device(kvq_cache *c, const void *k, const void *v, const v
         return KVQ_EWORKSPACE;
     kvq::DecodePlan pl = device_step_plan(c);
     pl.dstate = dev_state;
+    pl.rel = c->rel;
     {
         // the step the host counters describe (the device counters may have
         // moved on; KVQ_CHECK walks the state they would have next)
@@ -716,8 +727,6 @@ int kvq_append_decode_device(kvq_cache *c, const void *k, const void *v, const v
             return KVQ_EINVAL;
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = kvq::launch_flush_window_device(c->G, c->mem, dev_state, c->rel, st);
-    if (e != hipSuccess) return KVQ_EHIP;
     return hip_status(kvq::launch_decode(c->G, c->mem, static_cast<const uint16_t *>(q), out,
                                          workspace, pl, static_cast<const uint16_t *>(k),
                                          static_cast<const uint16_t *>(v), 0, c->ev_before,

@@ -70,11 +70,9 @@ hipError_t launch_quantize_pages(const Geometry &G, uint8_t *cache, const uint16
 // Same, with each unit's window as the source (one page per unit).
 hipError_t launch_flush_window(const Geometry &G, uint8_t *cache, int page, const float *rel,
                                hipStream_t stream);
-// Same, reading the counters from device memory ({pages, window tokens, ..}):
-// does nothing unless the window is full and a page is free.
-hipError_t launch_flush_window_device(const Geometry &G, uint8_t *cache, const int32_t *dstate,
-                                      const float *rel, hipStream_t stream);
-// dstate <- {n_pages, n_res, 0, 0}
+// Words of a graph-replayed step's device counters, and their initial
+// values: dstate <- {n_pages, n_res, 0, ...}.
+constexpr int kDeviceStateWords = 8;
 hipError_t launch_state_init(int32_t *dstate, int n_pages, int n_res, hipStream_t stream);
 // rel [B][Hkv][D] = sum over each KV head's query heads of |q| (q [B][Hq][D]).
 hipError_t launch_query_relevance(int dtype, const uint16_t *q, float *rel, int B, int Hq,
@@ -139,6 +137,8 @@ struct DecodePlan {
     int max_splits;       // workspace stride (splits per (b, hq))
     int32_t *dstate;      // non-null: counters in device memory (graph-replayable step);
                           // then total_splits = page_splits + R / 32
+    const float *rel;     // with dstate: channel relevance of the window flush of the
+                          // merge launch ([B][Hkv][D]), or null
 };
 size_t decode_workspace_bytes(const Geometry &G, int max_splits);
 

@@ -17,6 +17,7 @@ if not os.path.exists(LIB_PATH):
 _L = ctypes.CDLL(LIB_PATH)
 
 KVQ_F16, KVQ_BF16 = 0, 1
+KVQ_DEVICE_STATE_WORDS = 8
 ERRORS = {-1: "KVQ_EINVAL", -2: "KVQ_ECAPACITY", -3: "KVQ_ESTATE", -4: "KVQ_EEMPTY",
           -5: "KVQ_EWORKSPACE", -6: "KVQ_EALIGN", -7: "KVQ_EHIP"}
 EXPORTS = ["kvq_cache_bytes", "kvq_page_bytes", "kvq_cache_create", "kvq_cache_destroy",
@@ -485,8 +486,9 @@ class Cache:
         kvq_set_channel_relevance(self.handle, rel)
 
     def device_state(self, stream=None):
-        """A new int32[4] device state holding the current counters."""
-        st = torch.zeros(4, dtype=torch.int32, device=self.mem.device)
+        """A new int32[KVQ_DEVICE_STATE_WORDS] device state holding the current
+        counters (a full window with a free page is flushed first)."""
+        st = torch.zeros(KVQ_DEVICE_STATE_WORDS, dtype=torch.int32, device=self.mem.device)
         kvq_device_state_init(self.handle, st, stream)
         return st
 

@@ -170,23 +170,31 @@ int kvq_append_decode(kvq_cache *cache, const void *k, const void *v, const void
                       void *workspace, size_t ws_bytes, void *stream, int32_t *flushed);
 
 /* Graph-replayable decode step (same launches, same arguments, every step).
-   dev_state: device int32[4] = {pages, window tokens, unused (0), error flag},
+   dev_state: device int32[KVQ_DEVICE_STATE_WORDS] = {pages, window tokens,
+   unused (0), error flag, and four words the step's own launches use},
    16-byte aligned, owned by the caller.
    kvq_device_state_init writes the handle's host counters into dev_state (a
-   kernel launch, so it may itself be captured).
+   kernel launch, so it may itself be captured); when the window is full and
+   a page is free it first flushes the window into that page, the flush the
+   next step would start with (the host counters follow).
    kvq_append_decode_device is kvq_append_decode with the counters read from
-   and advanced in dev_state by the kernels themselves: a window flush launch
-   that acts only when the window is full, then the attention launches, the
-   last of which (the split merge) stores the new counters.  Its page split count is
-   fixed at the call (kvq_set_decode_splits, else one round of resident waves
-   for the host counters at that moment), so the launches it records into a
-   HIP graph stay valid for any later state.  The host counters of the handle
-   are NOT advanced: read dev_state back and call kvq_set_state before using
-   the other entry points again.  When a flush would need a page beyond
-   max_pages the kernels leave the cache unchanged, the step skips the new
-   token, and dev_state[3] becomes 1.  Results equal kvq_append_decode's up to
-   the rounding of a different split count.
-   Errors: KVQ_EINVAL, KVQ_EALIGN, KVQ_EWORKSPACE (argument checks only). */
+   and advanced in dev_state by the kernels themselves, in two launches: the
+   split attention (which stores the new token into its window slot) and the
+   split merge, which also flushes a window the step has just filled into the
+   next page (the flush that kvq_append_decode makes at the start of the
+   following step; the results are the same) and stores the new counters.
+   Its page split count is fixed at the call (kvq_set_decode_splits, else one
+   round of resident waves for the host counters at that moment), so the
+   launches it records into a HIP graph stay valid for any later state.  The
+   host counters of the handle are NOT advanced: read dev_state back and call
+   kvq_set_state before using the other entry points again.  When the window
+   is full and no page is free the kernels leave the cache unchanged, the
+   step skips the new token (attending the cache as it is), and dev_state[3]
+   becomes 1.  Results equal kvq_append_decode's up to the rounding of a
+   different split count.
+   Errors: KVQ_EINVAL, KVQ_EALIGN, KVQ_EWORKSPACE (argument checks only);
+   KVQ_EHIP from the initial flush. */
+#define KVQ_DEVICE_STATE_WORDS 8
 int kvq_device_state_init(kvq_cache *cache, int32_t *dev_state, void *stream);
 int kvq_append_decode_device(kvq_cache *cache, const void *k, const void *v, const void *q,
                              float *out, void *workspace, size_t ws_bytes, int32_t *dev_state,
