@@ -125,3 +125,33 @@ def test_query_aware_pool_pages(ora):
                     idx = got[lay["kidx"]:lay["kidx"] + 16]
                     assert idx.tolist() == list(range(5, 21))
     say(f"    pool pages with relevance bit-exact ({sum(pool.seq(s)[1] for s in ref)} per head)")
+
+
+def test_query_aware_graph_step_flush(ora):
+    """The merge launch of a graph-replayable step flushes the window its step
+    filled with the cache's relevance vector: that page bit-exact with the
+    oracle's, and attention after the flush within tolerance."""
+    w = dataclasses.replace(gen.WORKLOADS["llama3_8b_decode"], B=2)
+    graph = Pair(w, B=2, bulk_pages=1, window=126, max_pages=4, with_oracle=False)
+    ref = Pair(w, B=2, bulk_pages=1, window=126, max_pages=4)
+    rel = ora.query_relevance(w.dtype, ref.query(step=0), ref.Hkv)
+    rel_d = torch.from_numpy(rel).cuda()
+    graph.gpu.set_relevance(rel_d)
+    ref.gpu.set_relevance(rel_d)
+    ref.ora.rel = rel
+    st = graph.gpu.device_state()
+    out = torch.empty(2, w.Hq, 128, dtype=torch.float32, device="cuda")
+    for step in range(3):  # window 127, 128 (flushed by that step's merge launch), then 1
+        kt, vt = gen.step_kv(w, 300 + step)
+        kt, vt = kt[:2], vt[:2]
+        q = ref.query(step)
+        graph.gpu.append_decode_device(dev(kt), dev(vt), dev(q), out, st)
+        ref.append(kt, vt)
+    torch.cuda.synchronize()
+    assert tuple(host(st)[:4]) == (2, 1, 0, 0)
+    assert ref.ora.n_pages == 2 and ref.ora.n_res == 1 and ref.flushes[-1]
+    msg = first_page_mismatch(graph.pages()[:, :, :2], ref.ora.pages[:, :, :2])
+    assert msg is None, msg
+    err = np.abs(host(out) - ref.ora.attention(q)).max()
+    say(f"    graph step with relevance: flushed page bit-exact, max |gpu - oracle| = {err:.3e}")
+    assert err <= TOL
