@@ -285,6 +285,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
                 for (int n = 0; n < 8; n++) acc[u][n] *= alpha[u];
             }
+        // the P.V products at a raised issue priority (s_setprio) against the
+        // other waves of the SIMD: 2 % less time for this kernel, measured
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int n = 0; n < 8; n++) {
             const u4_t va = *reinterpret_cast<const u4_t *>(L + kKTile + (16 * n + r) * kVRow + 8 * kb);
@@ -294,6 +297,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 acc[u][n] = mfma_dt<DT>(va, blo[u], acc[u][n]);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     }
     if (nsplit > 1) {
         // unnormalized partials of this key chunk; a wave whose rows end
