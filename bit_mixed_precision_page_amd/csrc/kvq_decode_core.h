@@ -28,11 +28,13 @@
 //      eight channels for its row's head and takes four packed two-element
 //      dot products with the raw Key zeros (exact products, fp32 sums); a row
 //      sum over 16 lanes finishes it.
-//  PV  (16 rows = 4 heads x 4 Value groups) x (32 tokens x 16 channels): the
-//      A operand is p * s_v (softmax weight times the token's Value scale for
-//      the group), split hi/lo; p reaches that layout through a 512-byte LDS
-//      transpose.  The B operand is the Value code read the same way as the
-//      Key codes.  Only the row whose group matches the channel is kept; the
+//  PV  (16 rows = 4 heads x 2 Value groups x fp16 hi/lo) x (32 tokens x 16
+//      channels): the A operand is p * s_v (softmax weight times the token's
+//      Value scale for the group), its hi and lo parts in separate rows, one
+//      operand for groups 0-1 and one for groups 2-3; p reaches that layout
+//      through a 512-byte LDS transpose.  The B operand is the Value code read
+//      the same way as the Key codes.  One product per 16-channel tile; the
+//      two rows of the tile's group (hi, lo) are kept and added; the
 //      zero-point term p . z_v accumulates on the VALU.
 //
 // The softmax runs in the log2 domain with a per-head running maximum; the
@@ -279,9 +281,11 @@ __device__ __forceinline__ void load_group(GroupRegs<KHE> &Gr, __amdgpu_buffer_r
 }
 
 // Waves per SIMD the register allocation aims at (more registers per wave
-// beyond that would spill).
+// beyond that would spill; at eight heads and up to 32 boosted channels the
+// compiler keeps a few values that only the partials need in scratch,
+// stored before the group loop and read after it).
 constexpr int waves_target(int G, int KH) {
-    return G <= 4 ? (KH == 0 || (KH == 1 && G > 1) ? 4 : KH <= 3 ? 3 : 2) : G == 8 ? (KH <= 1 ? 3 : KH <= 3 ? 2 : 1) : 1;
+    return G <= 4 ? (KH == 0 || (KH == 1 && G > 1) ? 4 : KH <= 3 ? 3 : 2) : G == 8 ? (KH <= 1 ? 4 : KH <= 3 ? 3 : 1) : 1;
 }
 
 
@@ -295,7 +299,8 @@ template <int G, int KH>
 constexpr int split_lds_bytes() {
     constexpr int HQ = (G + 3) / 4, KHE = KH > 0 ? KH : 1, D_ = 128;
     constexpr int page = G * D_ * 2 + HQ * 4 * 32 * 16 + HQ * KHE * 2 * 16 * 16 + 416 * 4 + D_ * 2 +
-                         HQ * 4 * 48 * 4 + (KH > 0 && G <= 4 ? G * D_ * 4 : 0);
+                         HQ * 4 * (G >= 8 ? 44 : 48) * 4 - (G >= 8 ? D_ * 2 : 0) +
+                         (KH > 0 && G <= 4 ? G * D_ * 4 : 0);
     constexpr int win = G * D_ * 4 + 32 * G * 4;
     return page > win ? page : win;
 }
@@ -328,9 +333,13 @@ __device__ __forceinline__ void split_body(
     // f32 [416] K scale 2^E [128] | V scale [4 groups][36] | V zero [4][36]
     // (rows padded to 36: the PV-side reads of four groups hit four banks)
     constexpr int O_ST = O_WH + HQ * KHE * 2 * 16 * 16;
+    constexpr int PXR = G >= 8 ? 44 : 48;
+    // (with eight or more heads the softmax weights reuse the K zero row,
+    // which a group reads before it writes them, and their rows are padded
+    // less: the region of four waves then fits four workgroups per CU)
     constexpr int O_KZ = O_ST + 416 * 4;                  // u16 [D] K zero of the group
-    constexpr int O_PX = O_KZ + D * 2;                    // f32 [HQ][4][48] softmax weights (rows padded)
-    constexpr int O_QF = O_PX + HQ * 4 * 48 * 4;          // f32 [G][D] q' (boosted-channel gathers)
+    constexpr int O_PX = G >= 8 ? O_KZ : O_KZ + D * 2;    // f32 [HQ][4][PXR] softmax weights (rows padded)
+    constexpr int O_QF = O_PX + HQ * 4 * PXR * 4;         // f32 [G][D] q' (boosted-channel gathers)
     constexpr int LDSB = split_lds_bytes<G, KH>();
     // fp32 q' table for the boosted-channel gathers: only where the LDS it
     // takes does not cost occupancy (G <= 4); larger groups decode raw q
@@ -617,12 +626,17 @@ __device__ __forceinline__ void split_body(
         }
     // raw q pairs of channels 8 r + [0, 8) for the head of row kb: the
     // zero-point term
-    uint32_t qz[HQ][4];
+    // (held in registers for up to four heads; larger groups read them from
+    // LDS at each group)
+    constexpr bool QZR = G <= 4;
+    uint32_t qz[QZR ? HQ : 1][4];
+    if constexpr (QZR) {
 #pragma unroll
-    for (int s = 0; s < HQ; s++) {
-        const u4_t v = *reinterpret_cast<const u4_t *>(qr + head_of<G>(kb, s) * D + 8 * r);
+        for (int s = 0; s < HQ; s++) {
+            const u4_t v = *reinterpret_cast<const u4_t *>(qr + head_of<G>(kb, s) * D + 8 * r);
 #pragma unroll
-        for (int i = 0; i < 4; i++) qz[s][i] = v[i];
+            for (int i = 0; i < 4; i++) qz[s][i] = v[i];
+        }
     }
 
     // Hi-plane producer role (hkb, hR, hq, defined above): its boosted slots
@@ -638,8 +652,11 @@ __device__ __forceinline__ void split_body(
             fhs[ms][t] = 32 * ms + 16 * (hkb >> 1) + 4 * (hkb & 1) + hq + 8 * t < k ? fh : 0.0f;
 
     // staging destinations of this lane's metadata chunk
-    const int st_o = lane < 16 ? 8 * lane
-                               : 128 + 144 * ((lane - 32) >> 4) + 36 * ((lane >> 2) & 3) + 8 * (lane & 3);
+    // (lanes 16..31 hold raw K zeros: their chunk goes to the K zero row,
+    // which follows the fp32 tables)
+    const int st_o = lane < 16   ? 8 * lane
+                     : lane < 32 ? 416 + 4 * (lane - 16)
+                                 : 128 + 144 * ((lane - 32) >> 4) + 36 * ((lane >> 2) & 3) + 8 * (lane & 3);
     const bool st_f32 = lane < 16 || lane >= 32;
 
     float acc[HQ][8];  // lane (r, R): head head_of(R, s), channel 16 n + r
@@ -717,7 +734,7 @@ __device__ __forceinline__ void split_body(
                 *reinterpret_cast<float4 *>(st + st_o) = make_float4(f[0], f[1], f[2], f[3]);
                 *reinterpret_cast<float4 *>(st + st_o + 4) = make_float4(f[4], f[5], f[6], f[7]);
             } else {
-                *reinterpret_cast<u4_t *>(kz + 8 * (lane - 16)) = M;
+                *reinterpret_cast<u4_t *>(st + st_o) = M;
             }
             wave_sync();
             // sback = 2^(24 - E) undoes 2^E and the 2^-24 of the code operand
@@ -761,9 +778,14 @@ __device__ __forceinline__ void split_body(
                 const u4_t zr = *reinterpret_cast<const u4_t *>(kz + 8 * r);
 #pragma unroll
                 for (int s = 0; s < HQ; s++) {
+                    u4_t qs;
+                    if constexpr (QZR)
+                        qs = u4_t{qz[s][0], qz[s][1], qz[s][2], qz[s][3]};
+                    else
+                        qs = *reinterpret_cast<const u4_t *>(qr + head_of<G>(kb, s) * D + 8 * r);
                     float t = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < 4; i++) t = dot2<DT>(qz[s][i], zr[i], t);
+                    for (int i = 0; i < 4; i++) t = dot2<DT>(qs[i], zr[i], t);
                     bias[s] = row_sum(t) * qscale;
                 }
             }
@@ -825,8 +847,8 @@ __device__ __forceinline__ void split_body(
                     const float p0 = __builtin_amdgcn_exp2f(sc0 - mo);
                     const float p1 = __builtin_amdgcn_exp2f(sc1 - mo);
                     l_part[s] += p0 + p1;
-                    px[(s * 4 + kb) * 48 + r] = p0;
-                    px[(s * 4 + kb) * 48 + 16 + r] = p1;
+                    px[(s * 4 + kb) * PXR + r] = p0;
+                    px[(s * 4 + kb) * PXR + 16 + r] = p1;
                 }
             }
             wave_sync();
@@ -834,20 +856,25 @@ __device__ __forceinline__ void split_body(
 
         __builtin_amdgcn_s_setprio(1);
         // ---- PV on the matrix cores (32 tokens x 16-channel tiles) ----
-        u4_t ahi[HQ], alo[HQ];
+        // Rows r = 4 R' + 2 g' + hl of A operand (s, gp) hold part hl (fp16
+        // hi or lo) of p' s_v for head slot s of row R' and Value group
+        // 2 gp + g'; a tile of group g takes operand g / 2 and keeps its
+        // rows g' = g % 2.  Lane pairs (hl = 0, 1) compute one group each
+        // (2 hl + g') and swap the parts the other needs.
+        u4_t a0[HQ], a1[HQ];
         {
-            const int cg = r & 3;
-            const float4 va = *reinterpret_cast<const float4 *>(st + 128 + 36 * cg + 4 * kb);
-            const float4 vb = *reinterpret_cast<const float4 *>(st + 128 + 36 * cg + 16 + 4 * kb);
-            const float4 za = *reinterpret_cast<const float4 *>(st + 272 + 36 * cg + 4 * kb);
-            const float4 zb = *reinterpret_cast<const float4 *>(st + 272 + 36 * cg + 16 + 4 * kb);
+            const int hl = r & 1, gsel = 2 * hl + ((r >> 1) & 1);
+            const float4 va = *reinterpret_cast<const float4 *>(st + 128 + 36 * gsel + 4 * kb);
+            const float4 vb = *reinterpret_cast<const float4 *>(st + 128 + 36 * gsel + 16 + 4 * kb);
+            const float4 za = *reinterpret_cast<const float4 *>(st + 272 + 36 * gsel + 4 * kb);
+            const float4 zb = *reinterpret_cast<const float4 *>(st + 272 + 36 * gsel + 16 + 4 * kb);
             const float v8[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
             const float z8[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
 #pragma unroll
             for (int s = 0; s < HQ; s++) {
-                const float4 pa = *reinterpret_cast<const float4 *>(px + (s * 4 + (r >> 2)) * 48 + 4 * kb);
+                const float4 pa = *reinterpret_cast<const float4 *>(px + (s * 4 + (r >> 2)) * PXR + 4 * kb);
                 const float4 pb =
-                    *reinterpret_cast<const float4 *>(px + (s * 4 + (r >> 2)) * 48 + 16 + 4 * kb);
+                    *reinterpret_cast<const float4 *>(px + (s * 4 + (r >> 2)) * PXR + 16 + 4 * kb);
                 const float p8[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
                 uint32_t hi[4], lo[4];
 #pragma unroll
@@ -855,20 +882,29 @@ __device__ __forceinline__ void split_body(
                     split2(p8[2 * e2] * v8[2 * e2], p8[2 * e2 + 1] * v8[2 * e2 + 1], hi[e2], lo[e2]);
                     zt[s] = fmaf(p8[2 * e2], z8[2 * e2], fmaf(p8[2 * e2 + 1], z8[2 * e2 + 1], zt[s]));
                 }
-                ahi[s] = u4_t{hi[0], hi[1], hi[2], hi[3]};
-                alo[s] = u4_t{lo[0], lo[1], lo[2], lo[3]};
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++) {
+                    const uint32_t recv = dppu<0xB1>(hl ? hi[e2] : lo[e2]);  // from lane r ^ 1
+                    a0[s][e2] = hl ? recv : hi[e2];
+                    a1[s][e2] = hl ? lo[e2] : recv;
+                }
             }
         }
         const Codes8 v0(Gr.vc[0]), v1(Gr.vc[1]), v2(Gr.vc[2]), v3(Gr.vc[3]);
         __builtin_amdgcn_s_setprio(1);
+        // two tiles in flight: a product's result is read after the next
+        // product has issued
 #pragma unroll
-        for (int n = 0; n < 8; n++) {
-            const u4_t bv = {v0[n], v1[n], v2[n], v3[n]};
+        for (int n = 0; n < 8; n += 2) {
+            const u4_t bv0 = {v0[n], v1[n], v2[n], v3[n]};
+            const u4_t bv1 = {v0[n + 1], v1[n + 1], v2[n + 1], v3[n + 1]};
+            const int i = 2 * ((n >> 1) & 1);
 #pragma unroll
             for (int s = 0; s < HQ; s++) {
-                f4_t cs = mfma_f16(ahi[s], bv, f4_t{0, 0, 0, 0});
-                cs = mfma_f16(alo[s], bv, cs);
-                acc[s][n] += cs[n >> 1];
+                const f4_t c0 = mfma_f16(n < 4 ? a0[s] : a1[s], bv0, f4_t{0, 0, 0, 0});
+                const f4_t c1 = mfma_f16(n < 4 ? a0[s] : a1[s], bv1, f4_t{0, 0, 0, 0});
+                acc[s][n] += c0[i] + c0[i + 1];
+                acc[s][n + 1] += c1[i] + c1[i + 1];
             }
         }
         __builtin_amdgcn_s_setprio(1);
@@ -892,13 +928,15 @@ __device__ __forceinline__ void split_body(
 #pragma unroll
     for (int s = 0; s < HQ; s++) {
         const float l = row_sum(l_part[s]);
-        // zt: lanes (4 R' + cg, kb) hold head row R', Value group cg: sum over kb
+        // zt: lanes (4 R' + 2 (cg & 1) + (cg >> 1), kb) hold head row R', Value
+        // group cg: sum over kb
         float z = zt[s];
         z += shfl_xor(z, 16);
         z += shfl_xor(z, 32);
         float zg[4];
 #pragma unroll
-        for (int cg = 0; cg < 4; cg++) zg[cg] = shfl(z, 4 * kb + cg);
+        for (int cg = 0; cg < 4; cg++)
+            zg[cg] = shfl(z, 4 * kb + 2 * (cg & 1) + (cg >> 1));
         const int hh = head_of<G>(kb, s);
         if (s == 0 && NW > 1) wave_sync();  // this wave's reads of its LDS region are done
         if (G >= 4 || kb < G) {

@@ -10,10 +10,15 @@
 namespace kvq {
 namespace {
 
+// Waves per SIMD of the pool kernel: as the dense kernel's, except eight
+// heads with up to 32 boosted channels, where the block-table addressing
+// would push values the group loop reads into scratch at four waves.
+constexpr int pool_waves_target(int G, int KH) { return G == 8 && KH <= 1 ? 3 : waves_target(G, KH); }
+
 // 1-D grid: the page splits of every sequence (sequence-major, then KV head,
 // then split), then the window splits in the same order.
 template <int DT, int G, int KH>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_target(G, KH)))) void pool_split_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(pool_waves_target(G, KH)))) void pool_split_kernel(
     const uint8_t *__restrict__ mem, uint8_t *__restrict__ window_w,
     const uint16_t *__restrict__ knew, const uint16_t *__restrict__ vnew,
     const uint16_t *__restrict__ q, float *__restrict__ ws_ml, float *__restrict__ ws_acc,
