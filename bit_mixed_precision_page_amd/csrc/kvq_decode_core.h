@@ -675,12 +675,13 @@ __device__ __forceinline__ void split_body(
 
     // Issue priority by phase of the group (s_setprio; among the waves of a
     // SIMD the higher priority issues first, the older wave on a tie): the
-    // metadata -> exponent -> weight chain that starts a group highest, the
-    // QK matrix-core products lowest, the softmax and the PV products between.
-    // Measured against one flat priority: 1.3-8 % less time for the split
-    // kernel on every workload, 14 % with eight query heads per KV head.  The
-    // repeated settings before the PV operands, the PV products and at the
-    // end are part of what was measured: each also bounds the compiler's
+    // metadata -> exponent -> weight chain that starts a group and the
+    // softmax highest, the QK matrix-core products lowest, the PV operands
+    // and products between.  Measured against one flat priority: 1.3-8 %
+    // less time for the split kernel on every workload, 14 % with eight query
+    // heads per KV head (the softmax at the top came later: a further 0-1 %).
+    // The repeated settings before the PV operands, the PV products and at
+    // the end are part of what was measured: each also bounds the compiler's
     // instruction schedule, and without them the eight-head case is slower.
     auto process = [&](const GroupRegs<KHE> &Gr) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(2);
@@ -825,7 +826,7 @@ __device__ __forceinline__ void split_body(
                         else c1 = mfma_f16(w, bh, c1);
                     }
                 }
-                __builtin_amdgcn_s_setprio(1);
+                __builtin_amdgcn_s_setprio(2);
                 // ---- online softmax: lane (token r, row kb) owns its head's scores ----
 #pragma unroll
                 for (int a = 0; a < 2; a++) {
