@@ -15,7 +15,8 @@ before the timed region.
 Prints one JSON line: value = algorithmic bytes moved by the timed steps /
 elapsed time (GB/s); step_us = per-step percentiles (from the split kernel's
 own dispatch timestamps on a second run of as many steps), flush steps apart;
-graph_step_us = the same step replayed from a captured HIP graph; roofline =
+graph_step_us = the same step replayed from a captured HIP graph per layer;
+graph_all_layers_step_us = per layer step, every layer's step in one graph; roofline =
 the split decode kernel's algorithmic bytes per launch / its average launch
 time; copy_gbs and read_gbs = the library's bandwidth probe copying and
 reading 1 GiB (the measured reference beside the 8 TB/s specification);
@@ -373,7 +374,7 @@ def main():
 
     # -- graph-replayed step (kvq_append_decode_device captured once per
     # layer replica): the launch-floor comparison
-    graph_us = None
+    graph_us = graph_model_us = None
     if not a.unfused and a.graph:
         restore()
         sts = [c.device_state() for c in caches]
@@ -399,6 +400,31 @@ def main():
         err_flags = [int(x.cpu()[3]) for x in sts]
         assert not any(err_flags), "a graph-replayed step found its cache full"
         print(f"[bench] graph-replayed steps: {graph_us:.1f} us/step", file=sys.stderr, flush=True)
+
+        # every layer replica's step in one graph, as a model's decode step
+        # would capture its layers' attention calls together: no host launch
+        # between layers
+        restore()
+        sts = [c.device_state() for c in caches]
+        gm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gm, stream=side):
+            for li, c in enumerate(caches):
+                c.append_decode_device(kts[li % steps_total], vts[li % steps_total],
+                                       qs[li % steps_total], out, sts[li])
+        torch.cuda.synchronize()
+        gm.replay()  # untimed
+        torch.cuda.synchronize()
+        reps = max(1, a.steps // layers)
+        g0.record()
+        for _ in range(reps):
+            gm.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_model_us = g0.elapsed_time(g1) / (reps * layers) * 1e3
+        err_flags = [int(x.cpu()[3]) for x in sts]
+        assert not any(err_flags), "a graph-replayed step found its cache full"
+        print(f"[bench] all {layers} layer steps in one graph: {graph_model_us:.1f} us per layer step "
+              f"({reps} replays)", file=sys.stderr, flush=True)
 
     copy_gbs = read_gbs = None
     if not a.lean:
@@ -445,6 +471,7 @@ def main():
         "flushes": n_flush,
         "step_us": step_dist,
         "graph_step_us": round(graph_us, 2) if graph_us else None,
+        "graph_all_layers_step_us": round(graph_model_us, 2) if graph_model_us else None,
         "copy_gbs": round(copy_gbs, 1) if copy_gbs else None,
         "pct_copy_bw": round(100.0 * achieved / copy_gbs, 2) if copy_gbs else None,
         "read_gbs": round(read_gbs, 1) if read_gbs else None,
