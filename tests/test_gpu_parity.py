@@ -125,6 +125,22 @@ def test_query_group_sizes(g):
     check_attention(pair, pair.query())
 
 
+@pytest.mark.parametrize("wl,g,boost", [
+    ("llama3_8b_decode", 8, 0), ("llama3_8b_decode", 8, 48), ("llama3_8b_decode", 8, 96),
+    ("llama3_8b_decode", 8, 128), ("llama3_8b_decode", 16, 0), ("llama3_8b_decode", 16, 48),
+    ("tiny", 8, 16), ("tiny", 16, 32), ("tiny", 2, 80)])
+def test_group_size_with_boost_count(wl, g, boost):
+    """Each (query group, boosted-channel blocks, dtype) instantiation has its
+    own register budget and LDS layout (eight and sixteen heads share the
+    K-zero row with the softmax weights): the shapes the workloads do not
+    reach, against the oracle."""
+    tiny = wl == "tiny"
+    pair = Pair(W[wl], B=2, bulk_pages=2, window=33, Hq=(2 if tiny else 8) * g,
+                Hkv=2 if tiny else None, boost=boost)
+    check_pages(pair)
+    check_attention(pair, pair.query())
+
+
 def test_softmax_scale_argument():
     pair = Pair(W["tiny"], bulk_pages=2, window=3, scale=0.3)
     check_attention(pair, pair.query())
