@@ -158,3 +158,53 @@ def test_device_state_init_flushes_a_full_window():
     say(f"    flushed at set-up: |graph - eager| = {d_ref:.2e}, |graph - oracle| = {d_ora:.2e}")
     assert d_ref <= SPLIT_TOL
     assert d_ora <= TOL
+
+
+def test_several_caches_in_one_graph():
+    """Three caches' steps captured in one graph, as a model's decode step
+    holds every layer's attention call: each replay equals eager steps on twin
+    caches (pages and windows bit-exact) and the oracle, across flushes that
+    fall at different replays for the three caches."""
+    w = W["llama3_8b_decode"]
+    B = 2
+    wins = (124, 127, 60)
+    graphs = [Pair(w, B=B, bulk_pages=2, window=n, max_pages=5, with_oracle=False) for n in wins]
+    refs = [Pair(w, B=B, bulk_pages=2, window=n, max_pages=5) for n in wins]
+    sts = [gp.gpu.device_state() for gp in graphs]
+    ins = [(torch.empty(B, w.Hkv, 128, dtype=torch.int16, device="cuda"),
+            torch.empty(B, w.Hkv, 128, dtype=torch.int16, device="cuda"),
+            torch.empty(B, w.Hq, 128, dtype=torch.int16, device="cuda"),
+            GUARDS.out(B, w.Hq, 128)) for _ in wins]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        for gp, st, (ks, vs, qs, os_) in zip(graphs, sts, ins):
+            gp.gpu.append_decode_device(ks, vs, qs, os_, st)
+    torch.cuda.synchronize()
+    for step in range(1, 7):
+        wants = []
+        for i, (ref, (ks, vs, qs, os_)) in enumerate(zip(refs, ins)):
+            kt, vt = gen.step_kv(w, 900 + 10 * i + step)
+            kt, vt = kt[:B], vt[:B]
+            q = ref.query(100 * i + step)
+            ks.copy_(dev(kt))
+            vs.copy_(dev(vt))
+            qs.copy_(dev(q))
+            ref.append(kt, vt)
+            wants.append((ref.attention(q), ref.ora.attention(q)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (gp, ref, st, (_, _, _, os_)) in enumerate(zip(graphs, refs, sts, ins)):
+            got = host(os_)
+            _compare(gp, ref, os_, st, step)
+            d_ref = np.abs(got - wants[i][0]).max()
+            d_ora = np.abs(got - wants[i][1]).max()
+            say(f"    replay {step}, cache {i}: state {tuple(int(x) for x in host(st)[:2])}, "
+                f"|graph - eager| = {d_ref:.2e}, |graph - oracle| = {d_ora:.2e}")
+            assert np.isfinite(got).all()
+            assert d_ref <= SPLIT_TOL
+            assert d_ora <= TOL
+    # the 127-token cache flushed at the end of replay 1, the 124-token one at the end of replay 4
+    assert refs[1].flushes[-6:].count(True) == 1 and refs[0].flushes[-6:].count(True) == 1
+    assert refs[2].flushes[-6:].count(True) == 0
