@@ -11,6 +11,14 @@ summaries kept under profiles/.
       bytes per launch and the SHA-256 of the sources it was built from
       (KERNEL: decode_split_kernel, the default, or pool_split_kernel).
 
+  python -m bit_mixed_precision_page_amd.profsum sq WORKLOAD KERNEL SIMDS DIR "CMD" [DIR "CMD" ...]
+      each DIR holds run_counter_collection.csv of one --pmc pass over SQ
+      counters; writes profiles/KERNEL__WORKLOAD__sq.txt (JSON): every
+      counter's mean per dispatch of KERNEL, the instruction counts per wave
+      and per SIMD (SIMDS = SIMDs of the device), the share of the matrix
+      core's busy cycles with a VALU instruction issued beside it, and the
+      share of wave time spent waiting to issue.
+
 Counter scaling: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are divided by
 what they read for the runtime's device-to-device copy kernel
 (__amd_rocclr_copyBuffer) on the benchmark's cache replicas, whose size is
@@ -118,7 +126,54 @@ def pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, copy_bytes,
     return out
 
 
+def sq(workload, kernel, simds, passes):
+    """passes: [(dir, command)] of --pmc runs over SQ counters."""
+    means, counts = {}, {}
+    for d, _ in passes:
+        per = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                if kernel not in r["Kernel_Name"]:
+                    continue
+                per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        if not per:
+            raise SystemExit(f"no {kernel} samples under {d}")
+        for c, v in per.items():
+            if c in means:
+                continue
+            means[c] = sum(v) / len(v)
+            counts[c] = len(v)
+    rec = {"kernel": kernel, "workload": workload, "simds": simds,
+           "mean_per_dispatch": {c: round(v, 1) for c, v in sorted(means.items())},
+           "dispatches": counts}
+    der = {}
+    waves = means.get("SQ_WAVES")
+    for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_INSTS_LDS"):
+        if c in means:
+            der[c + "_per_simd"] = round(means[c] / simds, 1)
+            if waves:
+                der[c + "_per_wave"] = round(means[c] / waves, 1)
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in means:
+        der["mfma_busy_cycles_per_simd"] = round(means["SQ_VALU_MFMA_BUSY_CYCLES"] / simds, 1)
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in means:
+            der["valu_issued_while_mfma_busy"] = round(
+                means["SQ_VALU_MFMA_COEXEC_CYCLES"] / means["SQ_VALU_MFMA_BUSY_CYCLES"], 3)
+    if "SQ_WAIT_INST_ANY" in means and "SQ_WAVE_CYCLES" in means:
+        der["wave_time_waiting_to_issue"] = round(means["SQ_WAIT_INST_ANY"] / means["SQ_WAVE_CYCLES"], 3)
+    rec["derived"] = der
+    rec["commands"] = [cmd for _, cmd in passes]
+    rec["source_sha256"] = source_sha256(kernel)
+    out = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__sq.txt")
+    open(out, "w").write(json.dumps(rec, indent=1) + "\n")
+    print(json.dumps(rec, indent=1))
+    return out
+
+
 def main(argv):
+    if argv[:1] == ["sq"]:
+        rest = argv[4:]
+        sq(argv[1], argv[2], int(argv[3]), list(zip(rest[0::2], rest[1::2])))
+        return
     if argv[:1] == ["trace"]:
         trace(argv[1], argv[2], argv[3])
     elif argv[:1] == ["pmc"]:
